@@ -1,0 +1,195 @@
+"""ctypes front-end of the plain C oracle (``dsa_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()``
+and the CPU-baseline leg of ``bench.py``, never by the product package.  The
+functions take host numpy arrays (or CPU torch tensors) holding the same bytes
+the GPU path consumes and return float64 results.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "dsa_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+F32, BF16, E4M3 = 0, 1, 2
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (fp64, OpenMP over rows)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall",
+               "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        build()
+        L = ctypes.CDLL(_LIB)
+        vp, i32, i64, dp = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
+        L.orc_e4m3_value.argtypes = [i32]
+        L.orc_e4m3_value.restype = dp
+        L.orc_e4m3_table.argtypes = [vp]
+        L.orc_e4m3_table.restype = None
+        L.orc_indexer.argtypes = [vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, vp]
+        L.orc_indexer.restype = i32
+        L.orc_topk.argtypes = [vp, i64, vp, i32, i32, vp]
+        L.orc_topk.restype = i32
+        L.orc_sparse_attn.argtypes = [vp, vp, i32, vp, i32, i32, i32, i32, i32, i32, dp, vp, vp]
+        L.orc_sparse_attn.restype = i32
+        L.orc_num_threads.argtypes = []
+        L.orc_num_threads.restype = i32
+        _lib = L
+    return _lib
+
+
+def _np(x, dtype=None) -> np.ndarray:
+    """Host, C-contiguous numpy view of a numpy array or CPU torch tensor."""
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            x = x.detach().cpu()
+            if x.dtype == torch.bfloat16 or x.dtype == torch.float8_e4m3fn:
+                x = x.view(torch.uint16 if x.dtype == torch.bfloat16 else torch.uint8)
+            x = x.contiguous().numpy()
+    except ImportError:
+        pass
+    a = np.ascontiguousarray(x)
+    if dtype is not None:
+        a = np.ascontiguousarray(a, dtype=dtype)
+    return a
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def num_threads() -> int:
+    return int(lib().orc_num_threads())
+
+
+def e4m3_value(code: int) -> float:
+    return float(lib().orc_e4m3_value(int(code)))
+
+
+def e4m3_table() -> np.ndarray:
+    out = np.empty(256, dtype=np.float32)
+    lib().orc_e4m3_table(_ptr(out))
+    return out
+
+
+def indexer(q_idx, q_scale, k_idx, k_scale, w, t_pos, dtype: int) -> np.ndarray:
+    """Scores [n_rows, Lk] (float64, -inf where s > t_pos) for one batch entry.
+
+    q_idx [n_rows,H,D], q_scale [n_rows,H] or None, k_idx [Lk,D],
+    k_scale [Lk] or None, w [n_rows,H], t_pos [n_rows] int64.
+    """
+    q = _np(q_idx)
+    k = _np(k_idx)
+    n_rows, H, D = q.shape
+    Lk = k.shape[0]
+    assert k.shape[1] == D
+    if dtype == E4M3:
+        q = q.view(np.uint8)
+        k = k.view(np.uint8)
+    else:
+        q = _np(q, np.float32)
+        k = _np(k, np.float32)
+    qs = None if q_scale is None else _np(q_scale, np.float32)
+    ks = None if k_scale is None else _np(k_scale, np.float32)
+    ww = _np(w, np.float32)
+    tp = _np(t_pos, np.int64)
+    assert ww.shape == (n_rows, H) and tp.shape == (n_rows,)
+    out = np.empty((n_rows, Lk), dtype=np.float64)
+    rc = lib().orc_indexer(_ptr(q), _ptr(qs), _ptr(k), _ptr(ks), _ptr(ww), dtype,
+                           _ptr(tp), n_rows, Lk, H, D, _ptr(out))
+    if rc != 0:
+        raise ValueError("orc_indexer: bad arguments")
+    return out
+
+
+def topk(scores, t_pos, k: int) -> np.ndarray:
+    """Top-k index sets [n_rows, k] int32 (ascending s, -1 padded)."""
+    sc = _np(scores, np.float64)
+    n_rows, ld = sc.shape
+    tp = _np(t_pos, np.int64)
+    out = np.empty((n_rows, k), dtype=np.int32)
+    rc = lib().orc_topk(_ptr(sc), ld, _ptr(tp), n_rows, int(k), _ptr(out))
+    if rc != 0:
+        raise ValueError("orc_topk: bad arguments")
+    return out
+
+
+def sparse_attn(q, kv, idx, d_v: int, scale: float, dtype: int) -> Tuple[np.ndarray, np.ndarray]:
+    """(out [n_rows,H,d_v], lse [n_rows,H]) float64 over the selected rows.
+
+    q [n_rows,H,d_qk] and kv [Lk,d_qk] as fp32 or as bf16 bit patterns.
+    """
+    qq = _np(q)
+    kk = _np(kv)
+    if dtype == BF16:
+        qq = qq.view(np.uint16)
+        kk = kk.view(np.uint16)
+    else:
+        qq = _np(qq, np.float32)
+        kk = _np(kk, np.float32)
+    ii = _np(idx, np.int32)
+    n_rows, H, d_qk = qq.shape
+    Lk = kk.shape[0]
+    k = ii.shape[1]
+    out = np.empty((n_rows, H, d_v), dtype=np.float64)
+    lse = np.empty((n_rows, H), dtype=np.float64)
+    rc = lib().orc_sparse_attn(_ptr(qq), _ptr(kk), dtype, _ptr(ii), n_rows, k, Lk, H,
+                               d_qk, int(d_v), float(scale), _ptr(out), _ptr(lse))
+    if rc != 0:
+        raise ValueError("orc_sparse_attn: bad arguments")
+    return out, lse
+
+
+def forward_rows(inp: dict, cfg, rows, with_scores: bool = False):
+    """End-to-end oracle (scores -> top-k -> attention) for flattened rows.
+
+    ``inp`` is a dict of host tensors as drawn by ``dsa_inputs.make_inputs``
+    (or row-subsets of the query-side tensors when ``rows`` is given as the
+    explicit list they were taken from).  Returns dict with idx, out, lse and
+    optionally scores, all for the listed rows in order.
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    dt = E4M3 if cfg.idx_dtype == "fp8" else F32
+    io = BF16 if cfg.io_dtype == "bf16" else F32
+    res = {"idx": [], "out": [], "lse": [], "scores": []}
+    for b in np.unique(rows // cfg.Lq):
+        sel = rows[rows // cfg.Lq == b]
+        t = sel % cfg.Lq
+        t_pos = cfg.q_pos0 + t
+        qi = inp["q_idx"][b][t]
+        qs = inp["q_scale"][b][t] if dt == E4M3 else None
+        ks = inp["k_scale"][b] if dt == E4M3 else None
+        sc = indexer(qi, qs, inp["k_idx"][b], ks, inp["w"][b][t], t_pos, dt)
+        ix = topk(sc, t_pos, cfg.k)
+        o, l = sparse_attn(inp["q"][b][t], inp["kv"][b], ix, cfg.d_v, cfg.softmax_scale, io)
+        res["idx"].append(ix)
+        res["out"].append(o)
+        res["lse"].append(l)
+        if with_scores:
+            res["scores"].append(sc)
+    # restore the caller's row order
+    order = np.concatenate([np.nonzero(rows // cfg.Lq == b)[0] for b in np.unique(rows // cfg.Lq)])
+    inv = np.empty_like(order)
+    inv[order] = np.arange(order.size)
+    outd = {k: np.concatenate(v)[inv] for k, v in res.items() if v}
+    return outd

@@ -1,0 +1,294 @@
+/*
+ * Plain CPU oracle for the DeepSeek Sparse Attention (DSA) forward path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library calls, links or
+ * includes this file; only the tests, the smoke check and the benchmark's CPU
+ * baseline leg load it.  It shares no code, header or table with the HIP path.
+ *
+ * It evaluates the definitions literally, by brute force, in double precision:
+ *
+ *  - indexer score ("DeepseekV3.2 拆解", section 核心组件, lightning indexer
+ *    equation):  I[t,s] = sum_j w[t,j] * ReLU(q[t,j] . k[s]) over the preceding
+ *    tokens s <= t (self included);
+ *  - fine-grained token selection (same section, the u_t equation): the k
+ *    largest I[t,s]; ties go to the lower s; the set is emitted in ascending s
+ *    and padded with -1 when fewer than k tokens precede t;
+ *  - attention of the query over the selected latent rows only, with the row's
+ *    first d_qk columns as key and first d_v columns as value ("DeepSeek模型架构
+ *    创新解析" section 1.1: the up-projection is absorbed so attention runs on the
+ *    latent row) and a softmax scale supplied by the caller.
+ *
+ * Inputs are the same bytes the GPU consumes.  FP8 e4m3fn codes are decoded
+ * with a table built here from the OCP E4M3 definition (1 sign bit, 4 exponent
+ * bits with bias 7, 3 mantissa bits, subnormals at exponent 0, S.1111.111 = NaN,
+ * no infinities, largest finite 448), then multiplied by their fp32 scale in
+ * fp32.  bf16 is decoded by placing its 16 bits at the top of an fp32 word.
+ *
+ * Rows are independent; OpenMP parallelises over rows only, so the arithmetic
+ * order within a row is exactly the order written below.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_E4M3 = 2 };
+
+/* ---- decoding ----------------------------------------------------------- */
+
+double orc_e4m3_value(int code)
+{
+    int sign = (code >> 7) & 1;
+    int e = (code >> 3) & 0xF;
+    int m = code & 0x7;
+    double v;
+    if (e == 0xF && m == 0x7)
+        return NAN;
+    if (e == 0)
+        v = ldexp((double)m / 8.0, 1 - 7);           /* subnormal: 2^(1-bias) * 0.m */
+    else
+        v = ldexp(1.0 + (double)m / 8.0, e - 7);     /* normal: 2^(e-bias) * 1.m */
+    return sign ? -v : v;
+}
+
+static float g_e4m3[256];
+static int g_e4m3_ready = 0;
+
+static void e4m3_table_init(void)
+{
+    if (g_e4m3_ready)
+        return;
+    for (int c = 0; c < 256; ++c)
+        g_e4m3[c] = (float)orc_e4m3_value(c);
+    g_e4m3_ready = 1;
+}
+
+void orc_e4m3_table(float* out256)
+{
+    e4m3_table_init();
+    memcpy(out256, g_e4m3, sizeof(g_e4m3));
+}
+
+static float bf16_to_float(uint16_t h)
+{
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* Element i of a row stored as dtype, optionally multiplied by an fp32 scale
+ * in fp32 arithmetic (dequantisation). */
+static float load_elem(const void* base, int dtype, int64_t i)
+{
+    switch (dtype) {
+    case ORC_F32: return ((const float*)base)[i];
+    case ORC_BF16: return bf16_to_float(((const uint16_t*)base)[i]);
+    default: return g_e4m3[((const uint8_t*)base)[i]];
+    }
+}
+
+/* ---- indexer scores ------------------------------------------------------ */
+
+/*
+ * scores[r][s] for r < n_rows, s < Lk:
+ *   I = sum_j w[r][j] * max(0, sum_d qhat[r][j][d] * khat[s][d])   for s <= t_pos[r]
+ *   -INFINITY                                                     for s >  t_pos[r]
+ * q_idx: [n_rows][H][D], q_scale: [n_rows][H] (NULL when dtype is F32),
+ * k_idx: [Lk][D], k_scale: [Lk] (NULL when F32), w: [n_rows][H].
+ * qhat = fp32(decode(q) * q_scale), khat = fp32(decode(k) * k_scale).
+ * Returns 0, or -1 on bad arguments.
+ */
+int orc_indexer(const void* q_idx, const float* q_scale, const void* k_idx,
+                const float* k_scale, const float* w, int dtype,
+                const int64_t* t_pos, int n_rows, int Lk, int H, int D,
+                double* scores)
+{
+    if (dtype != ORC_F32 && dtype != ORC_E4M3)
+        return -1;
+    if (dtype == ORC_E4M3 && (!q_scale || !k_scale))
+        return -1;
+    e4m3_table_init();
+
+    float* khat = (float*)malloc(sizeof(float) * (size_t)Lk * (size_t)D);
+    if (!khat)
+        return -1;
+    for (int64_t s = 0; s < Lk; ++s)
+        for (int d = 0; d < D; ++d) {
+            float v = load_elem(k_idx, dtype, s * D + d);
+            khat[s * D + d] = (dtype == ORC_E4M3) ? v * k_scale[s] : v;
+        }
+
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(|: bad)
+    for (int r = 0; r < n_rows; ++r) {
+        if (t_pos[r] < 0 || t_pos[r] >= Lk) {
+            bad = 1;
+            continue;
+        }
+        float* qhat = (float*)malloc(sizeof(float) * (size_t)H * (size_t)D);
+        for (int j = 0; j < H; ++j)
+            for (int d = 0; d < D; ++d) {
+                int64_t i = ((int64_t)r * H + j) * D + d;
+                float v = load_elem(q_idx, dtype, i);
+                qhat[j * D + d] = (dtype == ORC_E4M3) ? v * q_scale[(int64_t)r * H + j] : v;
+            }
+        double* row = scores + (int64_t)r * Lk;
+        for (int64_t s = 0; s < Lk; ++s) {
+            if (s > t_pos[r]) {
+                row[s] = -INFINITY;
+                continue;
+            }
+            double I = 0.0;
+            for (int j = 0; j < H; ++j) {
+                double dot = 0.0;
+                for (int d = 0; d < D; ++d)
+                    dot += (double)qhat[j * D + d] * (double)khat[s * D + d];
+                double relu = dot > 0.0 ? dot : 0.0;
+                I += (double)w[(int64_t)r * H + j] * relu;
+            }
+            row[s] = I;
+        }
+        free(qhat);
+    }
+    free(khat);
+    return bad ? -1 : 0;
+}
+
+/* ---- top-k selection ---------------------------------------------------- */
+
+typedef struct { double v; int32_t s; } scored_t;
+
+/* Order: larger score first; equal scores (−0 == +0) by smaller index. */
+static int by_score_then_index(const void* a, const void* b)
+{
+    const scored_t* x = (const scored_t*)a;
+    const scored_t* y = (const scored_t*)b;
+    if (x->v > y->v) return -1;
+    if (x->v < y->v) return 1;
+    return (x->s > y->s) - (x->s < y->s);
+}
+
+static int by_index(const void* a, const void* b)
+{
+    int32_t x = *(const int32_t*)a, y = *(const int32_t*)b;
+    return (x > y) - (x < y);
+}
+
+/*
+ * idx[r][0..k): the min(k, t_pos[r]+1) indices s <= t_pos[r] of the largest
+ * scores[r][s] (ties to the smaller s), in ascending s, then -1 padding.
+ * scores: [n_rows][ld]; only s <= t_pos[r] is read.
+ */
+int orc_topk(const double* scores, int64_t ld, const int64_t* t_pos, int n_rows,
+             int k, int32_t* idx)
+{
+    if (k < 1)
+        return -1;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(|: bad)
+    for (int r = 0; r < n_rows; ++r) {
+        int64_t n = t_pos[r] + 1;
+        int32_t* out = idx + (int64_t)r * k;
+        if (n < 1 || n > ld) {
+            bad = 1;
+            continue;
+        }
+        int m = n < k ? (int)n : k;
+        scored_t* all = (scored_t*)malloc(sizeof(scored_t) * (size_t)n);
+        for (int64_t s = 0; s < n; ++s) {
+            double v = scores[(int64_t)r * ld + s];
+            all[s].v = (v == 0.0) ? 0.0 : v;   /* −0 and +0 are one value */
+            all[s].s = (int32_t)s;
+        }
+        qsort(all, (size_t)n, sizeof(scored_t), by_score_then_index);
+        for (int i = 0; i < m; ++i)
+            out[i] = all[i].s;
+        qsort(out, (size_t)m, sizeof(int32_t), by_index);
+        for (int i = m; i < k; ++i)
+            out[i] = -1;
+        free(all);
+    }
+    return bad ? -1 : 0;
+}
+
+/* ---- sparse attention over the selected rows ---------------------------- */
+
+/*
+ * For each row r and head h, over the selected set S = {idx[r][i] : idx >= 0}:
+ *   z_s  = scale * sum_d q[r][h][d] * kv[s][d]            (d < d_qk)
+ *   o[d] = sum_s exp(z_s - max z) * kv[s][d] / sum_s exp(z_s - max z)   (d < d_v)
+ *   lse  = max z + log(sum_s exp(z_s - max z))
+ * q: [n_rows][H][d_qk], kv: [Lk][d_qk] (both F32 or BF16), idx: [n_rows][k].
+ * out: [n_rows][H][d_v], lse: [n_rows][H] (may be NULL).  An empty set gives
+ * o = 0 and lse = -inf.
+ */
+int orc_sparse_attn(const void* q, const void* kv, int dtype, const int32_t* idx,
+                    int n_rows, int k, int Lk, int H, int d_qk, int d_v,
+                    double scale, double* out, double* lse)
+{
+    if (dtype != ORC_F32 && dtype != ORC_BF16)
+        return -1;
+    if (d_v > d_qk)
+        return -1;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(|: bad)
+    for (int r = 0; r < n_rows; ++r) {
+        const int32_t* sel = idx + (int64_t)r * k;
+        int n = 0;
+        for (int i = 0; i < k; ++i) {
+            if (sel[i] >= Lk) bad = 1;
+            if (sel[i] >= 0 && sel[i] < Lk) ++n;
+        }
+        double* z = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+        int32_t* rows = (int32_t*)malloc(sizeof(int32_t) * (size_t)(n > 0 ? n : 1));
+        n = 0;
+        for (int i = 0; i < k; ++i)
+            if (sel[i] >= 0 && sel[i] < Lk)
+                rows[n++] = sel[i];
+        for (int h = 0; h < H; ++h) {
+            double* o = out + ((int64_t)r * H + h) * d_v;
+            const int64_t qoff = ((int64_t)r * H + h) * d_qk;
+            if (n == 0) {
+                for (int d = 0; d < d_v; ++d) o[d] = 0.0;
+                if (lse) lse[(int64_t)r * H + h] = -INFINITY;
+                continue;
+            }
+            double zmax = -INFINITY;
+            for (int i = 0; i < n; ++i) {
+                double dot = 0.0;
+                for (int d = 0; d < d_qk; ++d)
+                    dot += (double)load_elem(q, dtype, qoff + d) *
+                           (double)load_elem(kv, dtype, (int64_t)rows[i] * d_qk + d);
+                z[i] = scale * dot;
+                if (z[i] > zmax) zmax = z[i];
+            }
+            double denom = 0.0;
+            for (int i = 0; i < n; ++i) {
+                z[i] = exp(z[i] - zmax);          /* z now holds the weight p_s */
+                denom += z[i];
+            }
+            for (int d = 0; d < d_v; ++d) {
+                double acc = 0.0;
+                for (int i = 0; i < n; ++i)
+                    acc += z[i] * (double)load_elem(kv, dtype, (int64_t)rows[i] * d_qk + d);
+                o[d] = acc / denom;
+            }
+            if (lse) lse[(int64_t)r * H + h] = zmax + log(denom);
+        }
+        free(z);
+        free(rows);
+    }
+    return bad ? -1 : 0;
+}
+
+/* Number of threads OpenMP would use for the loops above. */
+int orc_num_threads(void)
+{
+#ifdef _OPENMP
+    extern int omp_get_max_threads(void);
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

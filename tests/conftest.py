@@ -1,0 +1,35 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+
+
+def _has_gpu() -> bool:
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+@pytest.fixture(scope="session")
+def gpu():
+    if not _has_gpu():
+        pytest.skip("no GPU visible")
+    import torch
+    return torch.device("cuda:0")
+
+
+def pytest_runtest_setup(item):
+    # Name the case before any GPU work so a fault that ends the box still
+    # leaves the test id in the log.
+    if item.get_closest_marker("gpu") is not None:
+        print(f"\n[gpu-case] {item.nodeid}", flush=True)
