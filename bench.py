@@ -1,0 +1,188 @@
+#!/usr/bin/env python3
+"""Benchmark of the DSA forward hot path on one MI355X.
+
+One step = one fused forward (lightning-indexer scores -> top-k -> sparse
+attention) over one batch of synthetic inputs already resident in HBM.  The
+default workload is MLA-style prefill at L = 32768, k = 2048 (64 indexer heads
+x 128 in FP8 e4m3; 128 query heads over 576-wide bf16 latent rows, value width
+512, softmax scale 1/sqrt(192)).
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "DSA prefill tokens/s at L=32K,k=2048 (1 GPU); indexer % FP8 MFMA peak"
+PEAK_FP8 = 5.0e15        # dense FP8 MFMA, MI355X
+PEAK_BF16 = 2.5e15       # dense BF16 MFMA, MI355X
+PEAK_HBM = 8.0e12        # HBM3E bytes/s
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic(cfg):
+    """Algorithmic work of one forward (causal, no credit for masked work)."""
+    t_pos = [cfg.q_pos0 + t for t in range(cfg.Lq)]
+    n_all = cfg.B * sum(tp + 1 for tp in t_pos)
+    n_sel = cfg.B * sum(min(cfg.k, tp + 1) for tp in t_pos)
+    n_topk_read = cfg.B * sum(tp + 1 for tp in t_pos if tp + 1 > cfg.k)
+    return {
+        "indexer_flop": 2.0 * cfg.n_idx_heads * cfg.idx_dim * n_all,
+        "attn_flop": 2.0 * cfg.n_heads * (cfg.d_qk + cfg.d_v) * n_sel,
+        "topk_bytes": 4.0 * n_topk_read + 4.0 * cfg.B * cfg.Lq * cfg.k,
+        "attn_gather_bytes": 2.0 * cfg.d_qk * n_sel,
+    }
+
+
+def time_loop(fn, steps, stream):
+    import torch
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def cpu_baseline(cfg, inp, n_rows):
+    """The oracle, as it stands, on a uniform sample of query rows."""
+    import numpy as np
+    import torch
+    import oracle
+    rows = np.unique(np.linspace(0, cfg.Lq - 1, n_rows).astype(np.int64))
+    rt = torch.as_tensor(rows, device=inp["q"].device)
+    b = 0
+    qi = inp["q_idx"][b].index_select(0, rt).cpu()
+    qs = inp["q_scale"][b].index_select(0, rt).cpu()
+    w = inp["w"][b].index_select(0, rt).cpu()
+    q = inp["q"][b].index_select(0, rt).cpu()
+    ki, ks, kv = inp["k_idx"][b].cpu(), inp["k_scale"][b].cpu(), inp["kv"][b].cpu()
+    t_pos = cfg.q_pos0 + rows
+    t0 = time.perf_counter()
+    sc = oracle.indexer(qi, qs, ki, ks, w, t_pos, oracle.E4M3)
+    ix = oracle.topk(sc, t_pos, cfg.k)
+    oracle.sparse_attn(q, kv, ix, cfg.d_v, cfg.softmax_scale, oracle.BF16)
+    dt = time.perf_counter() - t0
+    return {"value": len(rows) / dt, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{len(rows)} query rows evenly spaced over t=0..{cfg.Lq - 1} of the same inputs "
+                      f"(indexer + top-k + attention per row, fp64), {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="mla_prefill_L32768")
+    ap.add_argument("--cpu-rows", type=int, default=48, help="oracle sample size (0 = skip)")
+    ap.add_argument("--no-stages", action="store_true", help="skip the per-stage timing loops")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
+              f"the path shards by query rows but no multi-GPU run is part of this build", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import sparse_attention_04_amd as dsa
+    from dsa_inputs import CONFIGS, make_inputs
+
+    cfg = CONFIGS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    log(f"[bench] {cfg.name}: drawing inputs on {torch.cuda.get_device_name(dev)}")
+    inp = make_inputs(cfg, seed=0, device=dev)
+    torch.cuda.synchronize()
+    work = algorithmic(cfg)
+
+    fwd = dsa.Forward(cfg.B, cfg.Lq, cfg.Lk, cfg.k, cfg.n_heads, cfg.d_v, inp["q"].dtype, dev,
+                      q_tile_rows=cfg.q_tile_rows)
+    run = lambda: fwd(inp["q_idx"], inp["q_scale"], inp["k_idx"], inp["k_scale"], inp["w"], inp["q"],
+                      inp["kv"], cfg.softmax_scale, q_pos0=cfg.q_pos0, stream=stream)
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps")
+    ms = time_loop(run, args.steps, stream)
+    tokens = cfg.B * cfg.Lq
+    log(f"[bench] forward {ms:.3f} ms/step -> {tokens / (ms * 1e-3):.4g} tokens/s")
+
+    stages = {}
+    if not args.no_stages:
+        # each stage alone, on the same stream, same inputs; the attention uses
+        # the forward's own selected sets
+        scores = torch.empty((cfg.B, cfg.Lq, cfg.Lk), dtype=torch.float32, device=dev)
+        idx = torch.empty((cfg.B, cfg.Lq, cfg.k), dtype=torch.int32, device=dev)
+        out = torch.empty_like(fwd.out)
+        lse = torch.empty_like(fwd.lse)
+        f_idx = lambda: dsa.dsa_indexer_scores(inp["q_idx"], inp["q_scale"], inp["k_idx"], inp["k_scale"],
+                                               inp["w"], q_pos0=cfg.q_pos0, scores=scores, stream=stream)
+        f_topk = lambda: dsa.dsa_topk(scores, cfg.k, q_pos0=cfg.q_pos0, idx=idx, stream=stream)
+        f_attn = lambda: dsa.dsa_sparse_attn(inp["q"], inp["kv"], fwd.idx, cfg.d_v, cfg.softmax_scale,
+                                             q_pos0=cfg.q_pos0, out=out, lse=lse, stream=stream)
+        for name, f in (("indexer", f_idx), ("topk", f_topk), ("attention", f_attn)):
+            f()
+            stages[name] = time_loop(f, max(1, args.steps), stream)
+            log(f"[bench] stage {name}: {stages[name]:.3f} ms")
+        del scores, idx, out, lse
+
+    res = {
+        "metric": METRIC,
+        "value": tokens / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3+bf16 (fp32 accumulate)",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "B": cfg.B, "L": cfg.Lk, "k": cfg.k,
+                   "n_idx_heads": cfg.n_idx_heads, "idx_dim": cfg.idx_dim, "n_heads": cfg.n_heads,
+                   "d_qk": cfg.d_qk, "d_v": cfg.d_v, "q_tile_rows": cfg.q_tile_rows},
+    }
+    if stages:
+        t_att = stages["attention"] * 1e-3
+        t_idx = stages["indexer"] * 1e-3
+        t_tk = stages["topk"] * 1e-3
+        att = work["attn_flop"] / t_att
+        res["roofline"] = {"bound": "mfma", "kernel": "sparse_attn_bf16", "achieved": att / 1e12,
+                           "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s", "frac": att / PEAK_BF16,
+                           "traffic": None}
+        res["indexer_frac_fp8_peak"] = work["indexer_flop"] / t_idx / PEAK_FP8
+        res["stages_ms"] = stages
+        res["stage_roofline"] = {
+            "indexer": {"bound": "mfma", "achieved_tflops": work["indexer_flop"] / t_idx / 1e12,
+                        "peak_tflops": PEAK_FP8 / 1e12, "frac": work["indexer_flop"] / t_idx / PEAK_FP8},
+            "topk": {"bound": "hbm", "achieved_gbs": work["topk_bytes"] / t_tk / 1e9,
+                     "peak_gbs": PEAK_HBM / 1e9, "frac": work["topk_bytes"] / t_tk / PEAK_HBM},
+            "attention": {"bound": "mfma", "achieved_tflops": att / 1e12, "peak_tflops": PEAK_BF16 / 1e12,
+                          "frac": att / PEAK_BF16,
+                          "gather_tbs": work["attn_gather_bytes"] / t_att / 1e12},
+        }
+        floor = max(work["indexer_flop"] / PEAK_FP8, 0) + work["topk_bytes"] / PEAK_HBM + work["attn_flop"] / PEAK_BF16
+        res["e2e_frac_of_floor"] = floor / (ms * 1e-3)
+    if args.cpu_rows > 0:
+        log(f"[bench] oracle on {args.cpu_rows} sampled rows")
+        res["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_rows)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

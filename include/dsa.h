@@ -1,0 +1,179 @@
+/*
+ * dsa.h — C ABI of the MI355X (gfx950) DeepSeek Sparse Attention forward path.
+ *
+ * The method ("DeepseekV3.2 拆解", section 核心组件):
+ *   1. lightning-indexer score  I[t,s] = sum_j w[t,j] * ReLU(q_I[t,j] . k_I[s])
+ *      over the tokens s that precede query t (s <= t), computed in FP8;
+ *   2. fine-grained token selection: per query, the k (= 2048) tokens with the
+ *      largest I[t,:];
+ *   3. attention of the query over the latent rows c_s of the selected tokens
+ *      only.  All query heads share one selected set and one latent row per
+ *      token (MQA over the MLA latent cache, "DeepSeek模型架构创新解析" section
+ *      1.1): the key is the row's first d_qk columns, the value its first d_v.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every tensor is a dense row-major array; the last dimension is unit-stride.
+ *    Device pointers must be 16-byte aligned.  The caller owns every buffer; the
+ *    library never allocates device memory except where a function says so.
+ *  - Positions: query row t of a batch entry sits at absolute position
+ *    t_pos = q_pos0 + t and may attend to keys 0..t_pos; q_pos0 + Lq <= Lk.
+ *    Prefill is q_pos0 = 0, Lq = Lk; decode of one new token is q_pos0 = Lk-1,
+ *    Lq = 1.
+ *  - Outputs are fully overwritten (callers need not clear them).
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream).  No
+ *    entry point synchronises or copies between host and device.
+ *  - Argument errors are detected before any launch and returned as a status;
+ *    dsa_last_error() then holds a message (per thread).  A failed launch
+ *    returns DSA_ERR_HIP.  Device faults surface at the caller's next
+ *    synchronisation.  No C++ exception crosses this interface.
+ *  - Entry points keep no state between calls; concurrent calls on different
+ *    streams are safe.
+ *  - B == 0 or Lq == 0 is a valid empty call: nothing is launched, DSA_OK.
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum dsa_status {
+    DSA_OK = 0,
+    DSA_ERR_NULL = 1,         /* a required pointer is NULL                      */
+    DSA_ERR_SHAPE = 2,        /* sizes inconsistent (e.g. q_pos0 + Lq > Lk)      */
+    DSA_ERR_DTYPE = 3,        /* dtype not valid for this argument               */
+    DSA_ERR_UNSUPPORTED = 4,  /* valid, but outside what the kernels implement   */
+    DSA_ERR_ALIGN = 5,        /* a pointer is not 16-byte aligned                */
+    DSA_ERR_WORKSPACE = 6,    /* workspace missing or too small                  */
+    DSA_ERR_HIP = 7           /* the HIP runtime reported an error at launch     */
+} dsa_status;
+
+typedef enum dsa_dtype {
+    DSA_F32 = 0,
+    DSA_BF16 = 1,
+    DSA_FP8_E4M3 = 2          /* OCP e4m3fn: bias 7, max 448, no inf, 0x7F = NaN */
+} dsa_dtype;
+
+/*
+ * Lightning-indexer scores ("DeepseekV3.2 拆解", section 核心组件, indexer
+ * equation; FP8 and ReLU chosen there for throughput):
+ *
+ *   scores[b,t,s] = k_scale[b,s] * sum_j (w[b,t,j] * q_scale[b,t,j])
+ *                                 * ReLU(sum_d q_idx[b,t,j,d] * k_idx[b,s,d])
+ *     for s <= t_pos,  and -INFINITY for t_pos < s < Lk.
+ *
+ * With positive scales this equals sum_j w * ReLU(qhat . khat) of the
+ * dequantised vectors.  The key vector k_idx[s] has no head index: one key per
+ * token serves every indexer head.
+ *
+ *   q_idx   [B,Lq,n_idx_heads,idx_dim]  FP8 e4m3 codes or fp32 (idx_dtype)
+ *   q_scale [B,Lq,n_idx_heads] fp32 > 0  (FP8 only; must be NULL for F32)
+ *   k_idx   [B,Lk,idx_dim]              same dtype as q_idx
+ *   k_scale [B,Lk] fp32 > 0             (FP8 only; must be NULL for F32)
+ *   w       [B,Lq,n_idx_heads] fp32     head weights, any sign
+ *   scores  [B,Lq,Lk] fp32              output
+ *
+ * Supported: FP8 with idx_dim == 128 and n_idx_heads == 64;
+ *            F32 with idx_dim % 4 == 0, idx_dim <= 256, n_idx_heads <= 64 and
+ *            n_idx_heads * idx_dim <= 8192.
+ */
+dsa_status dsa_indexer_scores(const void* q_idx, const float* q_scale,
+                              const void* k_idx, const float* k_scale,
+                              const float* w, float* scores,
+                              int B, int Lq, int Lk, int q_pos0,
+                              int n_idx_heads, int idx_dim, dsa_dtype idx_dtype,
+                              void* stream);
+
+/*
+ * Per-query top-k selection ("DeepseekV3.2 拆解", section 核心组件, the
+ * token-selection equation; k = 2048 in the section 创新点 table):
+ *
+ *   idx[b,t,:] = the min(k, t_pos+1) positions s <= t_pos with the largest
+ *                scores[b,t,s], ties resolved to the smaller s, written in
+ *                ascending s and padded with -1 up to k entries.
+ *
+ * -0.0 and +0.0 rank as one value.  Only scores[b,t,0..t_pos] is read (rows
+ * with t_pos + 1 <= k read nothing).  Scores must not be NaN.
+ *
+ *   scores [B,Lq,Lk] fp32;  idx [B,Lq,k] int32 (output).   Requires 1 <= k <= Lk.
+ */
+dsa_status dsa_topk(const float* scores, int32_t* idx,
+                    int B, int Lq, int Lk, int q_pos0, int k, void* stream);
+
+/*
+ * Sparse attention over the selected latent rows ("DeepseekV3.2 拆解",
+ * section 核心组件, u_t = Attn(h_t, {c_s : s selected})):
+ *
+ *   z_s        = softmax_scale * sum_{d<d_qk} q[b,t,h,d] * kv[b,s,d]
+ *   out[b,t,h] = sum_s softmax(z)_s * kv[b,s,0:d_v]
+ *   lse[b,t,h] = log sum_s exp(z_s)        (natural log; optional)
+ * over s in { idx[b,t,i] : 0 <= idx[b,t,i] < Lk }.  Entries outside [0, Lk)
+ * (such as the -1 padding) are skipped; an empty set gives out = 0 and
+ * lse = -inf.  Duplicate entries count once per occurrence.
+ *
+ *   q   [B,Lq,n_heads,d_qk]  bf16 or fp32 (io_dtype)
+ *   kv  [B,Lk,d_qk]          same dtype; one latent row per token shared by
+ *                            every head, value = its first d_v columns
+ *   idx [B,Lq,k] int32
+ *   out [B,Lq,n_heads,d_v]   same dtype (bf16 rounded to nearest even)
+ *   lse [B,Lq,n_heads] fp32  may be NULL
+ *
+ * Accumulation is fp32.  softmax_scale must be finite and > 0 (the MLA rows use
+ * 1/sqrt(d_h + d^R_h) = 1/sqrt(192), "DeepSeek模型架构创新解析" section 4.3).
+ * Supported: BF16 with n_heads % 16 == 0, n_heads <= 128, and
+ *            (d_qk, d_v) in {(576,512), (128,128), (64,64)};
+ *            F32 with d_qk <= 1024, d_v <= d_qk, n_heads <= 256.
+ */
+dsa_status dsa_sparse_attn(const void* q, const void* kv, const int32_t* idx,
+                           void* out, float* lse,
+                           int B, int Lq, int Lk, int q_pos0,
+                           int n_heads, int d_qk, int d_v, int k,
+                           float softmax_scale, dsa_dtype io_dtype, void* stream);
+
+/*
+ * Bytes of device workspace dsa_forward needs for these sizes.  q_tile_rows is
+ * the number of query rows (per batch entry) whose scores are held at once;
+ * 0 picks Lq, or fewer rows when Lq rows of scores would exceed 4 GiB.
+ * Returns 0 for an empty problem.
+ */
+size_t dsa_forward_workspace_size(int B, int Lq, int Lk, int k, int q_tile_rows);
+
+/*
+ * The whole forward: scores -> top-k -> sparse attention, processed in tiles of
+ * q_tile_rows query rows so that at most B * q_tile_rows * Lk scores exist at
+ * once (the full Lq x Lk matrix is never held when q_tile_rows < Lq).
+ *
+ * Results are identical, bit for bit, to calling dsa_indexer_scores, dsa_topk
+ * and dsa_sparse_attn in turn.  Rows with t_pos + 1 <= k select every
+ * preceding token, so their scores are not computed.
+ *
+ * Arguments are those of the three calls; idx_out [B,Lq,k] and lse may be NULL.
+ * workspace must hold dsa_forward_workspace_size(B, Lq, Lk, k, q_tile_rows)
+ * bytes, 256-byte aligned; its contents on entry do not matter.
+ */
+dsa_status dsa_forward(const void* q_idx, const float* q_scale,
+                       const void* k_idx, const float* k_scale, const float* w,
+                       int n_idx_heads, int idx_dim, dsa_dtype idx_dtype,
+                       const void* q, const void* kv,
+                       int n_heads, int d_qk, int d_v, dsa_dtype io_dtype,
+                       float softmax_scale,
+                       int B, int Lq, int Lk, int q_pos0, int k,
+                       int32_t* idx_out, void* out, float* lse,
+                       int q_tile_rows, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/* Static description of a status code. */
+const char* dsa_status_string(dsa_status s);
+
+/* Detail of the last non-OK status returned on this thread ("" if none). */
+const char* dsa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H */

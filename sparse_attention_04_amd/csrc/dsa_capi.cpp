@@ -1,0 +1,290 @@
+// C ABI of the DSA forward path: argument validation, dispatch to the gfx950
+// kernels, and the query-row tiling of the fused forward.  Every check runs
+// before any launch; failures return a status and leave a message in a
+// thread-local buffer.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/dsa.h"
+#include "launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+dsa_status fail(dsa_status st, const char* fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+dsa_status ok()
+{
+    g_err[0] = '\0';
+    return DSA_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+#define REQUIRE_PTR(p)                                                              \
+    do {                                                                            \
+        if ((p) == nullptr) return fail(DSA_ERR_NULL, "%s: %s is NULL", fn, #p);    \
+        if (!aligned16(p)) return fail(DSA_ERR_ALIGN, "%s: %s is not 16-byte aligned", fn, #p); \
+    } while (0)
+
+#define OPTIONAL_PTR(p)                                                             \
+    do {                                                                            \
+        if ((p) != nullptr && !aligned16(p))                                        \
+            return fail(DSA_ERR_ALIGN, "%s: %s is not 16-byte aligned", fn, #p);    \
+    } while (0)
+
+// Shared position checks.  Returns DSA_OK and sets *empty for B*Lq == 0.
+dsa_status check_positions(const char* fn, int B, int Lq, int Lk, int q_pos0, bool* empty)
+{
+    if (B < 0 || Lq < 0 || Lk < 0 || q_pos0 < 0)
+        return fail(DSA_ERR_SHAPE, "%s: negative size (B=%d Lq=%d Lk=%d q_pos0=%d)", fn, B, Lq, Lk, q_pos0);
+    if (B > 65535)
+        return fail(DSA_ERR_UNSUPPORTED, "%s: B=%d exceeds 65535", fn, B);
+    *empty = (B == 0 || Lq == 0);
+    if (*empty) return DSA_OK;
+    if ((int64_t)q_pos0 + Lq > Lk)
+        return fail(DSA_ERR_SHAPE, "%s: q_pos0 + Lq = %lld exceeds Lk = %d", fn,
+                    (long long)q_pos0 + Lq, Lk);
+    return DSA_OK;
+}
+
+dsa_status check_indexer(const char* fn, const void* q_idx, const float* q_scale, const void* k_idx,
+                         const float* k_scale, const float* w, int n_idx_heads, int idx_dim,
+                         dsa_dtype idx_dtype)
+{
+    REQUIRE_PTR(q_idx);
+    REQUIRE_PTR(k_idx);
+    REQUIRE_PTR(w);
+    if (n_idx_heads < 1 || idx_dim < 1)
+        return fail(DSA_ERR_SHAPE, "%s: n_idx_heads=%d idx_dim=%d must be >= 1", fn, n_idx_heads, idx_dim);
+    if (idx_dtype == DSA_FP8_E4M3) {
+        REQUIRE_PTR(q_scale);
+        REQUIRE_PTR(k_scale);
+        if (idx_dim != 128 || n_idx_heads != 64)
+            return fail(DSA_ERR_UNSUPPORTED, "%s: FP8 indexer implemented for 64 heads x 128 dims, got %d x %d",
+                        fn, n_idx_heads, idx_dim);
+    } else if (idx_dtype == DSA_F32) {
+        if (q_scale != nullptr || k_scale != nullptr)
+            return fail(DSA_ERR_DTYPE, "%s: scales are only defined for FP8 inputs; pass NULL for F32", fn);
+        if (idx_dim % 4 != 0 || idx_dim > 256 || n_idx_heads > 64 || n_idx_heads * idx_dim > 8192)
+            return fail(DSA_ERR_UNSUPPORTED,
+                        "%s: F32 indexer needs idx_dim %% 4 == 0, idx_dim <= 256, heads <= 64, heads*dim <= 8192", fn);
+    } else {
+        return fail(DSA_ERR_DTYPE, "%s: idx_dtype must be DSA_FP8_E4M3 or DSA_F32", fn);
+    }
+    return DSA_OK;
+}
+
+dsa_status check_attn(const char* fn, const void* q, const void* kv, void* out, float* lse,
+                      int n_heads, int d_qk, int d_v, int k, float softmax_scale, dsa_dtype io_dtype)
+{
+    REQUIRE_PTR(q);
+    REQUIRE_PTR(kv);
+    REQUIRE_PTR(out);
+    OPTIONAL_PTR(lse);
+    if (n_heads < 1 || d_qk < 1 || d_v < 1 || d_v > d_qk)
+        return fail(DSA_ERR_SHAPE, "%s: need n_heads >= 1 and 1 <= d_v <= d_qk (got %d, %d, %d)", fn,
+                    n_heads, d_qk, d_v);
+    if (!(std::isfinite(softmax_scale) && softmax_scale > 0.f))
+        return fail(DSA_ERR_SHAPE, "%s: softmax_scale must be finite and > 0", fn);
+    if (io_dtype == DSA_BF16) {
+        if (n_heads % 16 != 0 || n_heads > 128)
+            return fail(DSA_ERR_UNSUPPORTED, "%s: bf16 attention needs n_heads %% 16 == 0 and <= 128 (got %d)", fn, n_heads);
+        if (!dsa::sparse_attn_bf16_supported(d_qk, d_v))
+            return fail(DSA_ERR_UNSUPPORTED, "%s: bf16 attention built for (d_qk, d_v) in {(576,512),(128,128),(64,64)}, got (%d,%d)",
+                        fn, d_qk, d_v);
+    } else if (io_dtype == DSA_F32) {
+        if (n_heads > 256 || d_qk > 1024 || k > 4096)
+            return fail(DSA_ERR_UNSUPPORTED, "%s: f32 attention needs n_heads <= 256, d_qk <= 1024, k <= 4096", fn);
+    } else {
+        return fail(DSA_ERR_DTYPE, "%s: io_dtype must be DSA_BF16 or DSA_F32", fn);
+    }
+    return DSA_OK;
+}
+
+dsa_status check_k(const char* fn, int k, int Lk)
+{
+    if (k < 1 || k > Lk) return fail(DSA_ERR_SHAPE, "%s: k=%d must satisfy 1 <= k <= Lk=%d", fn, k, Lk);
+    return DSA_OK;
+}
+
+dsa_status hip_status(const char* fn, hipError_t e)
+{
+    if (e != hipSuccess) return fail(DSA_ERR_HIP, "%s: %s", fn, hipGetErrorString(e));
+    return ok();
+}
+
+int auto_tile_rows(int B, int Lq, int Lk)
+{
+    const uint64_t per_row = (uint64_t)B * (uint64_t)Lk * 4u;   // bytes of scores per query row
+    const uint64_t cap = 4ull << 30;
+    uint64_t t = per_row ? cap / per_row : (uint64_t)Lq;
+    if (t < 1) t = 1;
+    if (t > (uint64_t)Lq) t = (uint64_t)Lq;
+    return (int)t;
+}
+
+size_t round256(size_t x) { return (x + 255u) & ~(size_t)255u; }
+
+}  // namespace
+
+extern "C" {
+
+const char* dsa_status_string(dsa_status s)
+{
+    switch (s) {
+    case DSA_OK: return "ok";
+    case DSA_ERR_NULL: return "null pointer";
+    case DSA_ERR_SHAPE: return "inconsistent sizes";
+    case DSA_ERR_DTYPE: return "invalid dtype";
+    case DSA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case DSA_ERR_ALIGN: return "misaligned pointer";
+    case DSA_ERR_WORKSPACE: return "workspace missing or too small";
+    case DSA_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char* dsa_last_error(void) { return g_err; }
+
+dsa_status dsa_indexer_scores(const void* q_idx, const float* q_scale, const void* k_idx,
+                              const float* k_scale, const float* w, float* scores, int B, int Lq,
+                              int Lk, int q_pos0, int n_idx_heads, int idx_dim,
+                              dsa_dtype idx_dtype, void* stream)
+{
+    const char* fn = "dsa_indexer_scores";
+    bool empty = false;
+    dsa_status st = check_positions(fn, B, Lq, Lk, q_pos0, &empty);
+    if (st != DSA_OK || empty) return st == DSA_OK ? ok() : st;
+    st = check_indexer(fn, q_idx, q_scale, k_idx, k_scale, w, n_idx_heads, idx_dim, idx_dtype);
+    if (st != DSA_OK) return st;
+    REQUIRE_PTR(scores);
+    dsa::IndexerLaunch a{};
+    a.q = q_idx; a.q_scale = q_scale; a.k = k_idx; a.k_scale = k_scale; a.w = w; a.scores = scores;
+    a.B = B; a.Lq = Lq; a.Lk = Lk; a.q_pos0 = q_pos0; a.t_begin = 0; a.t_count = Lq;
+    a.sc_bstride = (int64_t)Lq * Lk; a.sc_rstride = Lk;
+    a.H = n_idx_heads; a.D = idx_dim; a.fp8 = (idx_dtype == DSA_FP8_E4M3);
+    a.write_masked = true; a.skip_upto_k = 0;
+    return hip_status(fn, dsa::launch_indexer(a, (hipStream_t)stream));
+}
+
+dsa_status dsa_topk(const float* scores, int32_t* idx, int B, int Lq, int Lk, int q_pos0, int k,
+                    void* stream)
+{
+    const char* fn = "dsa_topk";
+    bool empty = false;
+    dsa_status st = check_positions(fn, B, Lq, Lk, q_pos0, &empty);
+    if (st != DSA_OK || empty) return st == DSA_OK ? ok() : st;
+    REQUIRE_PTR(scores);
+    REQUIRE_PTR(idx);
+    st = check_k(fn, k, Lk);
+    if (st != DSA_OK) return st;
+    dsa::TopkLaunch a{};
+    a.scores = scores; a.idx = idx; a.B = B; a.Lq = Lq; a.Lk = Lk; a.q_pos0 = q_pos0;
+    a.t_begin = 0; a.t_count = Lq;
+    a.sc_bstride = (int64_t)Lq * Lk; a.sc_rstride = Lk; a.idx_bstride = (int64_t)Lq * k; a.k = k;
+    return hip_status(fn, dsa::launch_topk(a, (hipStream_t)stream));
+}
+
+dsa_status dsa_sparse_attn(const void* q, const void* kv, const int32_t* idx, void* out, float* lse,
+                           int B, int Lq, int Lk, int q_pos0, int n_heads, int d_qk, int d_v, int k,
+                           float softmax_scale, dsa_dtype io_dtype, void* stream)
+{
+    const char* fn = "dsa_sparse_attn";
+    bool empty = false;
+    dsa_status st = check_positions(fn, B, Lq, Lk, q_pos0, &empty);
+    if (st != DSA_OK || empty) return st == DSA_OK ? ok() : st;
+    REQUIRE_PTR(idx);
+    if (k < 1) return fail(DSA_ERR_SHAPE, "%s: k=%d must be >= 1", fn, k);
+    st = check_attn(fn, q, kv, out, lse, n_heads, d_qk, d_v, k, softmax_scale, io_dtype);
+    if (st != DSA_OK) return st;
+    dsa::AttnLaunch a{};
+    a.q = q; a.kv = kv; a.idx = idx; a.out = out; a.lse = lse;
+    a.B = B; a.Lq = Lq; a.Lk = Lk; a.t_begin = 0; a.t_count = Lq; a.idx_bstride = (int64_t)Lq * k;
+    a.H = n_heads; a.Dqk = d_qk; a.Dv = d_v; a.k = k; a.scale = softmax_scale;
+    a.bf16 = (io_dtype == DSA_BF16);
+    return hip_status(fn, dsa::launch_sparse_attn(a, (hipStream_t)stream));
+}
+
+size_t dsa_forward_workspace_size(int B, int Lq, int Lk, int k, int q_tile_rows)
+{
+    if (B <= 0 || Lq <= 0 || Lk <= 0 || k <= 0 || q_tile_rows < 0) return 0;
+    const int T = q_tile_rows > 0 ? (q_tile_rows < Lq ? q_tile_rows : Lq) : auto_tile_rows(B, Lq, Lk);
+    const size_t scores = round256((size_t)B * (size_t)T * (size_t)Lk * sizeof(float));
+    const size_t idx = round256((size_t)B * (size_t)T * (size_t)k * sizeof(int32_t));
+    return scores + idx;
+}
+
+dsa_status dsa_forward(const void* q_idx, const float* q_scale, const void* k_idx,
+                       const float* k_scale, const float* w, int n_idx_heads, int idx_dim,
+                       dsa_dtype idx_dtype, const void* q, const void* kv, int n_heads, int d_qk,
+                       int d_v, dsa_dtype io_dtype, float softmax_scale, int B, int Lq, int Lk,
+                       int q_pos0, int k, int32_t* idx_out, void* out, float* lse,
+                       int q_tile_rows, void* workspace, size_t workspace_bytes, void* stream)
+{
+    const char* fn = "dsa_forward";
+    bool empty = false;
+    dsa_status st = check_positions(fn, B, Lq, Lk, q_pos0, &empty);
+    if (st != DSA_OK || empty) return st == DSA_OK ? ok() : st;
+    st = check_indexer(fn, q_idx, q_scale, k_idx, k_scale, w, n_idx_heads, idx_dim, idx_dtype);
+    if (st != DSA_OK) return st;
+    st = check_k(fn, k, Lk);
+    if (st != DSA_OK) return st;
+    st = check_attn(fn, q, kv, out, lse, n_heads, d_qk, d_v, k, softmax_scale, io_dtype);
+    if (st != DSA_OK) return st;
+    OPTIONAL_PTR(idx_out);
+    if (q_tile_rows < 0) return fail(DSA_ERR_SHAPE, "%s: q_tile_rows=%d must be >= 0", fn, q_tile_rows);
+    const int T = q_tile_rows > 0 ? (q_tile_rows < Lq ? q_tile_rows : Lq) : auto_tile_rows(B, Lq, Lk);
+    const size_t need = dsa_forward_workspace_size(B, Lq, Lk, k, q_tile_rows);
+    if (workspace == nullptr || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0)
+        return fail(DSA_ERR_WORKSPACE, "%s: workspace needs %zu bytes, 256-byte aligned (got %zu at %p)",
+                    fn, need, workspace_bytes, workspace);
+
+    float* ws_scores = (float*)workspace;
+    int32_t* ws_idx = (int32_t*)((char*)workspace + round256((size_t)B * T * (size_t)Lk * sizeof(float)));
+    hipStream_t s = (hipStream_t)stream;
+
+    for (int t0 = 0; t0 < Lq; t0 += T) {
+        const int tc = (Lq - t0 < T) ? (Lq - t0) : T;
+        dsa::IndexerLaunch ia{};
+        ia.q = q_idx; ia.q_scale = q_scale; ia.k = k_idx; ia.k_scale = k_scale; ia.w = w;
+        ia.scores = ws_scores; ia.B = B; ia.Lq = Lq; ia.Lk = Lk; ia.q_pos0 = q_pos0;
+        ia.t_begin = t0; ia.t_count = tc; ia.sc_bstride = (int64_t)T * Lk; ia.sc_rstride = Lk;
+        ia.H = n_idx_heads; ia.D = idx_dim; ia.fp8 = (idx_dtype == DSA_FP8_E4M3);
+        ia.write_masked = false; ia.skip_upto_k = k;
+        hipError_t e = dsa::launch_indexer(ia, s);
+        if (e != hipSuccess) return hip_status(fn, e);
+
+        int32_t* idx_tile = idx_out ? idx_out + (int64_t)t0 * k : ws_idx;
+        const int64_t idx_bstride = idx_out ? (int64_t)Lq * k : (int64_t)T * k;
+        dsa::TopkLaunch ta{};
+        ta.scores = ws_scores; ta.idx = idx_tile; ta.B = B; ta.Lq = Lq; ta.Lk = Lk; ta.q_pos0 = q_pos0;
+        ta.t_begin = t0; ta.t_count = tc; ta.sc_bstride = (int64_t)T * Lk; ta.sc_rstride = Lk;
+        ta.idx_bstride = idx_bstride; ta.k = k;
+        e = dsa::launch_topk(ta, s);
+        if (e != hipSuccess) return hip_status(fn, e);
+
+        dsa::AttnLaunch aa{};
+        aa.q = q; aa.kv = kv; aa.idx = idx_tile; aa.out = out; aa.lse = lse;
+        aa.B = B; aa.Lq = Lq; aa.Lk = Lk; aa.t_begin = t0; aa.t_count = tc; aa.idx_bstride = idx_bstride;
+        aa.H = n_heads; aa.Dqk = d_qk; aa.Dv = d_v; aa.k = k; aa.scale = softmax_scale;
+        aa.bf16 = (io_dtype == DSA_BF16);
+        e = dsa::launch_sparse_attn(aa, s);
+        if (e != hipSuccess) return hip_status(fn, e);
+    }
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,88 @@
+// Device-side helpers for gfx950 (CDNA4): vector types, MFMA wrappers,
+// bf16 rounding and wave64 reductions.  Used by the kernels only.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// D(16x16 fp32) = A(16x128 e4m3) * B(128x16 e4m3) + C.  Lane l supplies row
+// (l % 16) of A / column (l % 16) of B with 32 bytes of the K dimension
+// chosen by (l / 16); A and B use the same K assignment, so a contiguous
+// 32-byte slice per lane gives the correct dot product.  Lane l receives
+// D[4*(l/16) + i][l % 16], i = 0..3.  Zero block scales select the unscaled
+// v_mfma_f32_16x16x128_f8f6f4 (format 0 = e4m3 for both operands).
+__device__ __forceinline__ v4f mfma_fp8_16x16x128(const v8i& a, const v8i& b, const v4f& c)
+{
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// D(16x16 fp32) = A(16x32 bf16) * B(32x16 bf16) + C; lane l supplies 8
+// consecutive K values (slot 8*(l/16)..) of row/column l % 16.
+__device__ __forceinline__ v4f mfma_bf16_16x16x32(const v8bf& a, const v8bf& b, const v4f& c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ v8bf as_bf8(const u32x4& u) { return __builtin_bit_cast(v8bf, u); }
+__device__ __forceinline__ v8i as_i8(const u32x4& lo, const u32x4& hi)
+{
+    v8i r;
+    r[0] = (int)lo[0]; r[1] = (int)lo[1]; r[2] = (int)lo[2]; r[3] = (int)lo[3];
+    r[4] = (int)hi[0]; r[5] = (int)hi[1]; r[6] = (int)hi[2]; r[7] = (int)hi[3];
+    return r;
+}
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// Order-preserving map of an fp32 score to uint32 (larger score -> larger key);
+// -0.0 is folded onto +0.0 first so the two rank as one value.
+__device__ __forceinline__ uint32_t score_key(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if (u == 0x80000000u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float wave_max(float v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane)
+{
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        uint32_t u = __shfl_up(v, o, kWave);
+        if (lane >= o) v += u;
+    }
+    return v;
+}
+
+}  // namespace dsa

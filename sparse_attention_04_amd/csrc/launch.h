@@ -1,0 +1,56 @@
+// Host-side launch descriptors shared by the C ABI (dsa_capi.cpp) and the
+// kernel files.  All row addressing is relative to a tile of query rows
+// [t_begin, t_begin + t_count) of every batch entry.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+struct IndexerLaunch {
+    const void* q;          // [B,Lq,H,D] fp8 codes or fp32
+    const float* q_scale;   // [B,Lq,H] (fp8 only)
+    const void* k;          // [B,Lk,D]
+    const float* k_scale;   // [B,Lk] (fp8 only)
+    const float* w;         // [B,Lq,H]
+    float* scores;          // row (b, t) at scores + b*sc_bstride + (t - t_begin)*sc_rstride
+    int B, Lq, Lk, q_pos0;
+    int t_begin, t_count;
+    int64_t sc_bstride, sc_rstride;
+    int H, D;
+    bool fp8;
+    bool write_masked;      // write -inf for t_pos < s < Lk
+    int skip_upto_k;        // > 0: skip query blocks whose rows all have t_pos + 1 <= this
+};
+
+struct TopkLaunch {
+    const float* scores;    // as IndexerLaunch::scores
+    int32_t* idx;           // row (b, t) at idx + b*idx_bstride + (t - t_begin)*k
+    int B, Lq, Lk, q_pos0;
+    int t_begin, t_count;
+    int64_t sc_bstride, sc_rstride, idx_bstride;
+    int k;
+};
+
+struct AttnLaunch {
+    const void* q;          // [B,Lq,H,Dqk]
+    const void* kv;         // [B,Lk,Dqk]
+    const int32_t* idx;     // as TopkLaunch::idx
+    void* out;              // [B,Lq,H,Dv]
+    float* lse;             // [B,Lq,H] or null
+    int B, Lq, Lk;
+    int t_begin, t_count;
+    int64_t idx_bstride;
+    int H, Dqk, Dv, k;
+    float scale;
+    bool bf16;
+};
+
+hipError_t launch_indexer(const IndexerLaunch& a, hipStream_t s);
+hipError_t launch_topk(const TopkLaunch& a, hipStream_t s);
+hipError_t launch_sparse_attn(const AttnLaunch& a, hipStream_t s);
+
+// Which (Dqk, Dv) pairs the bf16 attention kernel is instantiated for.
+bool sparse_attn_bf16_supported(int Dqk, int Dv);
+
+}  // namespace dsa

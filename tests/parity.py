@@ -1,0 +1,104 @@
+"""Comparators between the HIP path and the CPU oracle (test infrastructure).
+
+Tolerances (derivations in the design notes):
+  scores     |I_gpu - I_ref| <= 1e-3 |I_ref| + 1e-5 max_s |I_ref[t, s]|
+             The relative term is the required bound; the absolute term covers
+             fp32 rounding of the signed head sum, whose worst case is of order
+             (d^I + H^I) * 2^-24 * sum_j |w_j| ReLU(.) ~ 1.2e-5 * row maximum.
+  top-k      bit-exact where the oracle's gap (v_k - v_{k+1}) / |v_k| > 1e-3
+             (and the gap also exceeds twice the absolute score tolerance);
+             every row must be a valid top-k of the oracle's scores within the
+             score tolerance (size, range, order, distinctness, threshold).
+  attention  |o_gpu - o_ref| <= 1e-2 + half a bf16 ulp of o_ref (the output
+             must be rounded to bf16); 1e-4 for the fp32 path.  lse within 2e-3.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+SCORE_RTOL = 1e-3
+SCORE_ATOL_ROWMAX = 1e-5
+GAP_EXACT = 1e-3
+
+
+def score_tol(ref_rows: np.ndarray, t_pos: np.ndarray) -> np.ndarray:
+    """Per-element tolerance for score rows [n, Lk] (masked entries -inf)."""
+    fin = np.where(np.isfinite(ref_rows), np.abs(ref_rows), 0.0)
+    rowmax = fin.max(axis=1, keepdims=True)
+    return SCORE_RTOL * fin + SCORE_ATOL_ROWMAX * rowmax
+
+
+def check_scores(gpu_rows: np.ndarray, ref_rows: np.ndarray, t_pos: np.ndarray, masked_written=True):
+    """gpu_rows fp32 [n, Lk]; ref_rows float64 [n, Lk] with -inf past t_pos."""
+    n, Lk = ref_rows.shape
+    s = np.arange(Lk)[None, :]
+    valid = s <= t_pos[:, None]
+    g = gpu_rows.astype(np.float64)
+    tol = score_tol(ref_rows, t_pos)
+    err = np.where(valid, np.abs(g - np.where(valid, ref_rows, 0.0)), 0.0)
+    bad = err > tol
+    ratio = float((err / np.maximum(tol, 1e-300)).max()) if valid.any() else 0.0
+    assert not bad.any(), (
+        f"{int(bad.sum())} score mismatches; worst at {np.unravel_index(np.argmax(err - tol), err.shape)} "
+        f"err/tol={ratio:.3g}")
+    if masked_written:
+        assert np.all(gpu_rows[~valid] == -np.inf), "masked scores must be -inf"
+    return ratio
+
+
+def check_topk_rows(gpu_idx: np.ndarray, ref_scores: np.ndarray, t_pos: np.ndarray, k: int,
+                    ref_idx: np.ndarray):
+    """End-to-end top-k check against the oracle's float64 scores.
+
+    Returns (exact-match fraction, number of rows required to be exact)."""
+    n_rows = gpu_idx.shape[0]
+    exact = 0
+    required = 0
+    for r in range(n_rows):
+        n = int(t_pos[r]) + 1
+        g = gpu_idx[r]
+        m = min(k, n)
+        sel = g[:m]
+        assert np.all(g[m:] == -1), f"row {r}: padding"
+        assert np.all(sel >= 0) and np.all(sel <= t_pos[r]), f"row {r}: out of range"
+        assert np.all(np.diff(sel) > 0), f"row {r}: not ascending/distinct"
+        same = np.array_equal(g, ref_idx[r])
+        exact += same
+        if n > k:
+            v = ref_scores[r, :n]
+            order = np.lexsort((np.arange(n), -np.where(v == 0, 0.0, v)))
+            vk, vk1 = v[order[k - 1]], v[order[k]]
+            gap = (vk - vk1) / max(abs(vk), 1e-30)
+            atol = SCORE_ATOL_ROWMAX * np.abs(v).max()
+            if gap > GAP_EXACT and (vk - vk1) > 2 * atol:
+                required += 1
+                assert same, f"row {r}: gap {gap:.3g} > {GAP_EXACT} but sets differ"
+            tol = SCORE_RTOL * abs(vk) + SCORE_ATOL_ROWMAX * np.abs(v).max()
+            mask = np.zeros(n, bool)
+            mask[sel] = True
+            assert v[mask].min() >= vk - tol, f"row {r}: selected score below threshold"
+            if (~mask).any():
+                assert v[~mask].max() <= vk + tol, f"row {r}: unselected score above threshold"
+        else:
+            assert np.array_equal(sel, np.arange(n)), f"row {r}: short row must keep every token"
+    return exact / max(n_rows, 1), required
+
+
+def bf16_half_ulp(x: np.ndarray) -> np.ndarray:
+    ax = np.abs(x).astype(np.float64)
+    e = np.floor(np.log2(np.maximum(ax, 2.0 ** -126)))
+    return 0.5 * 2.0 ** (e - 7)
+
+
+def check_attention(gpu_out: np.ndarray, ref_out: np.ndarray, gpu_lse, ref_lse, bf16: bool):
+    g = gpu_out.astype(np.float64)
+    err = np.abs(g - ref_out)
+    tol = (1e-2 + bf16_half_ulp(ref_out)) if bf16 else 1e-4
+    worst = float((err - tol).max()) if err.size else -1.0
+    assert np.all(err <= tol), f"attention max err {err.max():.4g} (worst excess {worst:.3g})"
+    if gpu_lse is not None:
+        gl = gpu_lse.astype(np.float64)
+        both_inf = np.isneginf(gl) & np.isneginf(ref_lse)
+        le = np.where(both_inf, 0.0, np.abs(gl - ref_lse))
+        assert np.all(le <= 2e-3), f"lse max err {le.max():.4g}"
+    return float(err.max()) if err.size else 0.0

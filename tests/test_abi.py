@@ -1,0 +1,135 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, and
+rejects bad arguments with the documented status before any launch.
+
+No test here reaches a kernel launch: every call either fails validation or is
+an empty problem (B == 0 or Lq == 0), which returns before touching HIP.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+
+OK, NULL, SHAPE, DTYPE, UNSUP, ALIGN, WS, HIP = range(8)
+F32, BF16, FP8 = 0, 1, 2
+
+
+@pytest.fixture(scope="module")
+def L():
+    from sparse_attention_04_amd import lib
+    return lib
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsa_[a-z_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = _declared()
+    assert {"dsa_indexer_scores", "dsa_topk", "dsa_sparse_attn", "dsa_forward",
+            "dsa_forward_workspace_size", "dsa_status_string", "dsa_last_error"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    for s in range(8):
+        assert L.dsa_status_string(s)
+    assert L.dsa_status_string(0) == b"ok"
+
+
+A = 0x10000           # a fake, 16-byte aligned "device address": never dereferenced here
+MIS = A + 4
+
+
+def idx_scores(L, **kw):
+    a = dict(q=A, qs=A, k=A, ks=A, w=A, sc=A, B=1, Lq=8, Lk=8, q0=0, H=64, D=128, dt=FP8)
+    a.update(kw)
+    return L.dsa_indexer_scores(a["q"], a["qs"], a["k"], a["ks"], a["w"], a["sc"], a["B"], a["Lq"],
+                                a["Lk"], a["q0"], a["H"], a["D"], a["dt"], None)
+
+
+def test_indexer_validation(L):
+    assert idx_scores(L, q=None) == NULL
+    assert idx_scores(L, qs=None) == NULL
+    assert idx_scores(L, sc=None) == NULL
+    assert idx_scores(L, k=MIS) == ALIGN
+    assert idx_scores(L, Lq=9) == SHAPE                    # q_pos0 + Lq > Lk
+    assert idx_scores(L, q0=1) == SHAPE
+    assert idx_scores(L, Lk=-1) == SHAPE
+    assert idx_scores(L, H=32) == UNSUP                    # FP8 built for 64 x 128
+    assert idx_scores(L, D=64) == UNSUP
+    assert idx_scores(L, dt=BF16) == DTYPE
+    assert idx_scores(L, dt=F32) == DTYPE                  # scales given for F32
+    assert idx_scores(L, dt=F32, qs=None, ks=None, D=30, H=4) == UNSUP
+    assert b"q_pos0" in L.dsa_last_error() or L.dsa_last_error() != b""
+    # empty problems are valid and launch nothing
+    assert idx_scores(L, B=0) == OK
+    assert idx_scores(L, Lq=0) == OK and L.dsa_last_error() == b""
+
+
+def test_topk_validation(L):
+    f = L.dsa_topk
+    assert f(None, A, 1, 4, 4, 0, 2, None) == NULL
+    assert f(A, None, 1, 4, 4, 0, 2, None) == NULL
+    assert f(A, MIS, 1, 4, 4, 0, 2, None) == ALIGN
+    assert f(A, A, 1, 4, 4, 0, 0, None) == SHAPE           # k < 1
+    assert f(A, A, 1, 4, 4, 0, 5, None) == SHAPE           # k > Lk
+    assert f(A, A, 1, 4, 4, 2, 2, None) == SHAPE           # q_pos0 + Lq > Lk
+    assert f(A, A, 70000, 1, 4, 0, 2, None) == UNSUP       # grid y limit
+    assert f(A, A, 1, 0, 4, 0, 2, None) == OK
+
+
+def attn(L, **kw):
+    a = dict(q=A, kv=A, idx=A, out=A, lse=None, B=1, Lq=4, Lk=8, q0=0, H=128, dqk=576, dv=512,
+             k=4, scale=0.1, dt=BF16)
+    a.update(kw)
+    return L.dsa_sparse_attn(a["q"], a["kv"], a["idx"], a["out"], a["lse"], a["B"], a["Lq"], a["Lk"],
+                             a["q0"], a["H"], a["dqk"], a["dv"], a["k"], a["scale"], a["dt"], None)
+
+
+def test_attention_validation(L):
+    assert attn(L, q=None) == NULL
+    assert attn(L, idx=None) == NULL
+    assert attn(L, lse=MIS) == ALIGN
+    assert attn(L, dv=600) == SHAPE                        # d_v > d_qk
+    assert attn(L, scale=0.0) == SHAPE
+    assert attn(L, scale=float("nan")) == SHAPE
+    assert attn(L, k=0) == SHAPE
+    assert attn(L, H=24) == UNSUP                          # bf16 needs H % 16 == 0
+    assert attn(L, H=144) == UNSUP
+    assert attn(L, dqk=256, dv=256) == UNSUP
+    assert attn(L, dt=FP8) == DTYPE
+    assert attn(L, dt=F32, k=5000) == UNSUP
+    assert attn(L, B=0) == OK
+
+
+def test_forward_workspace(L):
+    ws = L.dsa_forward_workspace_size
+    assert ws(1, 32768, 32768, 2048, 0) == 32768 * 32768 * 4 + 32768 * 2048 * 4
+    assert ws(1, 131072, 131072, 2048, 4096) == 4096 * 131072 * 4 + 4096 * 2048 * 4
+    # auto tile caps the score tile at 4 GiB
+    assert ws(1, 131072, 131072, 2048, 0) == 8192 * 131072 * 4 + 8192 * 2048 * 4
+    assert ws(64, 1, 65536, 2048, 0) == 64 * 65536 * 4 + 64 * 2048 * 4
+    assert ws(0, 1, 1, 1, 0) == 0
+    need = ws(1, 8, 8, 4, 0)
+
+    def fwd(workspace, nbytes, **kw):
+        a = dict(H=64, D=128, dt=FP8, Hq=128, dqk=576, dv=512, io=BF16, k=4, T=0)
+        a.update(kw)
+        return L.dsa_forward(A, A, A, A, A, a["H"], a["D"], a["dt"], A, A, a["Hq"], a["dqk"], a["dv"],
+                             a["io"], 0.1, 1, 8, 8, 0, a["k"], None, A, None, a["T"], workspace,
+                             nbytes, None)
+
+    assert fwd(None, need) == WS
+    assert fwd(A, need - 1) == WS
+    assert fwd(A + 16, need) == WS                          # not 256-byte aligned
+    assert fwd(A, need, k=9) == SHAPE
+    assert fwd(A, need, T=-1) == SHAPE
+    assert fwd(A, need, H=16) == UNSUP
+    assert fwd(A, need, io=FP8) == DTYPE

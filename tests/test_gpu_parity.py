@@ -1,0 +1,283 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Inputs come from dsa_inputs (seeded, drawn on the device); the oracle gets the
+same bytes copied to the host.  Small cases compare every row; the full-size
+workloads compare a stratified sample of rows, computed one by one by the
+oracle, in the launch configuration the benchmark times.
+"""
+import math
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from dsa_inputs import CONFIGS, make_inputs
+from tests.parity import check_attention, check_scores, check_topk_rows
+
+pytestmark = pytest.mark.gpu
+
+E4M3, F32, BF16 = oracle.E4M3, oracle.F32, oracle.BF16
+
+
+@pytest.fixture(scope="module")
+def dsa(gpu):
+    import sparse_attention_04_amd as m
+    return m
+
+
+def _host(t):
+    return t.detach().cpu()
+
+
+def _sample_rows(Lq, k, n_random=24, seed=0):
+    """First rows, rows around k, a uniform stride, the last rows."""
+    g = np.random.default_rng(seed)
+    rows = set(range(min(Lq, 4)))
+    rows |= {r for r in (k - 2, k - 1, k, k + 1, k + 15) if 0 <= r < Lq}
+    rows |= set(np.linspace(0, Lq - 1, 12).astype(int).tolist())
+    rows |= set(g.integers(0, Lq, size=n_random).tolist())
+    rows |= set(range(max(0, Lq - 4), Lq))
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+def _oracle_rows(inp_h, cfg, b, rows):
+    """Oracle scores / top-k / attention for batch entry b and query rows."""
+    dt = E4M3 if cfg.idx_dtype == "fp8" else F32
+    io = BF16 if cfg.io_dtype == "bf16" else F32
+    t_pos = cfg.q_pos0 + rows
+    sc = oracle.indexer(inp_h["q_idx"][b][rows], inp_h["q_scale"][b][rows] if dt == E4M3 else None,
+                        inp_h["k_idx"][b], inp_h["k_scale"][b] if dt == E4M3 else None,
+                        inp_h["w"][b][rows], t_pos, dt)
+    ix = oracle.topk(sc, t_pos, cfg.k)
+    return sc, ix, t_pos
+
+
+def _run_case(dsa, cfg, rows_by_b, seed=0, check_forward=True, q_tile_rows=0):
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    inp = make_inputs(cfg, seed=seed, device=dev)
+    torch.cuda.synchronize()
+    fp8 = cfg.idx_dtype == "fp8"
+    scores = dsa.dsa_indexer_scores(inp["q_idx"], inp.get("q_scale"), inp["k_idx"], inp.get("k_scale"),
+                                    inp["w"], q_pos0=cfg.q_pos0)
+    idx = dsa.dsa_topk(scores, cfg.k, q_pos0=cfg.q_pos0)
+    out, lse = dsa.dsa_sparse_attn(inp["q"], inp["kv"], idx, cfg.d_v, cfg.softmax_scale, q_pos0=cfg.q_pos0)
+    torch.cuda.synchronize()
+    print(f"  [{cfg.name}] gpu stages done in {time.time() - t0:.1f}s", flush=True)
+
+    key_side = {k: _host(inp[k]) for k in ("k_idx", "k_scale", "kv") if k in inp}
+    stats = {"score_err_ratio": 0.0, "exact": [], "attn_err": 0.0}
+    for b, rows in rows_by_b.items():
+        rows = np.asarray(rows, dtype=np.int64)
+        rt = torch.as_tensor(rows)
+        q_side = {k: _host(inp[k][b].index_select(0, rt.to(dev))) for k in ("q_idx", "q_scale", "w", "q")
+                  if k in inp}
+        inp_h = {k: {b: v} for k, v in key_side.items()}
+        inp_h.update({k: {b: v} for k, v in q_side.items()})
+        sel = np.arange(len(rows))
+        t_pos = cfg.q_pos0 + rows
+        dt = E4M3 if fp8 else F32
+        sc_ref = oracle.indexer(q_side["q_idx"], q_side.get("q_scale"), key_side["k_idx"][b],
+                                key_side["k_scale"][b] if fp8 else None, q_side["w"], t_pos, dt)
+        ix_ref = oracle.topk(sc_ref, t_pos, cfg.k)
+        g_sc = _host(scores[b].index_select(0, rt.to(dev))).numpy()
+        stats["score_err_ratio"] = max(stats["score_err_ratio"], check_scores(g_sc, sc_ref, t_pos))
+        g_ix = _host(idx[b].index_select(0, rt.to(dev))).numpy()
+        frac, req = check_topk_rows(g_ix, sc_ref, t_pos, cfg.k, ix_ref)
+        stats["exact"].append(frac)
+        # top-k of the GPU's own fp32 scores: both sides decide in fp32, bit-exact
+        ix_same_prec = oracle.topk(g_sc.astype(np.float64), t_pos, cfg.k)
+        assert np.array_equal(g_ix, ix_same_prec), "top-k differs from the oracle on identical fp32 scores"
+        # attention over the GPU's selected sets
+        io = BF16 if cfg.io_dtype == "bf16" else F32
+        o_ref, l_ref = oracle.sparse_attn(q_side["q"], key_side["kv"][b], g_ix, cfg.d_v, cfg.softmax_scale, io)
+        g_o = _host(out[b].index_select(0, rt.to(dev))).float().numpy()
+        g_l = _host(lse[b].index_select(0, rt.to(dev))).numpy()
+        stats["attn_err"] = max(stats["attn_err"], check_attention(g_o, o_ref, g_l, l_ref, io == BF16))
+
+    if check_forward:
+        # fused forward == the three calls, bit for bit
+        fwd_idx = torch.empty_like(idx)
+        fwd_lse = torch.empty_like(lse)
+        fwd_out, _, _ = dsa.dsa_forward(inp["q_idx"], inp.get("q_scale"), inp["k_idx"], inp.get("k_scale"),
+                                        inp["w"], inp["q"], inp["kv"], k=cfg.k,
+                                        softmax_scale=cfg.softmax_scale, q_pos0=cfg.q_pos0,
+                                        idx=fwd_idx, lse=fwd_lse, d_v=cfg.d_v, q_tile_rows=q_tile_rows)
+        torch.cuda.synchronize()
+        assert torch.equal(fwd_idx, idx), "forward idx != top-k call"
+        assert torch.equal(fwd_out.view(torch.int16) if fwd_out.dtype == torch.bfloat16 else fwd_out,
+                           out.view(torch.int16) if out.dtype == torch.bfloat16 else out), "forward out differs"
+        assert torch.equal(fwd_lse, lse), "forward lse differs"
+    print(f"  [{cfg.name}] score err/tol {stats['score_err_ratio']:.3g}, top-k exact "
+          f"{np.mean(stats['exact']):.4f}, attn max err {stats['attn_err']:.3g}, total {time.time() - t0:.1f}s",
+          flush=True)
+    return stats
+
+
+# ------------------------------------------------------------------ small, all rows
+
+def test_tiny_fp32_all_rows(dsa):
+    cfg = CONFIGS["tiny_fp32_L256"]
+    _run_case(dsa, cfg, {0: np.arange(cfg.Lq)})
+
+
+def test_fp8_ragged_all_rows_tiled_forward(dsa):
+    cfg = CONFIGS["prefill_L4096"].with_(name="fp8_L300", Lq=300, Lk=300, k=64)
+    _run_case(dsa, cfg, {0: np.arange(cfg.Lq)}, q_tile_rows=48)
+
+
+def test_fp8_mla_heads_ragged(dsa):
+    cfg = CONFIGS["mla_prefill_L32768"].with_(name="mla_L333", Lq=333, Lk=333, k=100, n_heads=32)
+    _run_case(dsa, cfg, {0: np.arange(cfg.Lq)}, q_tile_rows=100)
+
+
+def test_decode_like_batch_with_offset(dsa):
+    cfg = CONFIGS["decode_B64_ctx65536"].with_(name="decode_small", B=3, Lq=5, Lk=1000, q_pos0=995,
+                                               k=128, n_heads=16)
+    _run_case(dsa, cfg, {b: np.arange(cfg.Lq) for b in range(cfg.B)})
+
+
+def test_head_dim_64(dsa):
+    cfg = CONFIGS["prefill_L4096"].with_(name="d64", Lq=200, Lk=260, q_pos0=60, k=50, n_heads=32,
+                                         d_qk=64, d_v=64, softmax_scale=0.125)
+    _run_case(dsa, cfg, {0: np.arange(cfg.Lq)})
+
+
+# ------------------------------------------------------------------ full-size workloads, sampled rows
+
+def test_prefill_L4096(dsa):
+    cfg = CONFIGS["prefill_L4096"]
+    _run_case(dsa, cfg, {0: _sample_rows(cfg.Lq, cfg.k)})
+
+
+def test_mla_prefill_L32768(dsa):
+    cfg = CONFIGS["mla_prefill_L32768"]
+    _run_case(dsa, cfg, {0: _sample_rows(cfg.Lq, cfg.k, n_random=16)})
+
+
+def test_decode_B64_ctx65536(dsa):
+    cfg = CONFIGS["decode_B64_ctx65536"]
+    _run_case(dsa, cfg, {b: np.array([0]) for b in (0, 1, 17, 63)})
+
+
+# ------------------------------------------------------------------ top-k on crafted scores (bit-exact)
+
+def _topk_exact(dsa, scores: torch.Tensor, k: int, q_pos0: int = 0):
+    idx = dsa.dsa_topk(scores, k, q_pos0=q_pos0)
+    torch.cuda.synchronize()
+    B, Lq, Lk = scores.shape
+    sc = scores.cpu().numpy().astype(np.float64)
+    for b in range(B):
+        t_pos = q_pos0 + np.arange(Lq)
+        ref = oracle.topk(sc[b], t_pos, k)
+        assert np.array_equal(idx[b].cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("case", ["normal", "ties", "const", "signed_zero", "k1", "k_eq_L", "around_k"])
+def test_topk_crafted_bit_exact(dsa, case):
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device="cpu").manual_seed(7)
+    L = 3000
+    k = {"k1": 1, "k_eq_L": L, "around_k": 1500}.get(case, 700)
+    if case == "normal":
+        s = torch.randn(1, L, L, generator=g)
+    elif case == "ties":
+        s = torch.randint(-3, 4, (1, L, L), generator=g).float()
+    elif case == "const":
+        s = torch.full((1, L, L), 0.25)
+    elif case == "signed_zero":
+        s = torch.where(torch.rand(1, L, L, generator=g) < 0.5, torch.tensor(-0.0), torch.tensor(0.0))
+        s[..., ::97] = 1.0
+    else:
+        s = torch.randn(1, L, L, generator=g)
+    _topk_exact(dsa, s.to(dev).contiguous(), k)
+
+
+def test_topk_long_rows(dsa):
+    """Rows of 131071 and 131072 candidates (the long-context row length)."""
+    dev = torch.device("cuda:0")
+    Lk = 131072
+    g = torch.Generator(device=dev).manual_seed(3)
+    s = torch.randn(2, 2, Lk, device=dev, generator=g)
+    s[1] = torch.randint(-50, 50, (2, Lk), device=dev, generator=g).float()   # many ties
+    _topk_exact(dsa, s.contiguous(), 2048, q_pos0=Lk - 2)
+
+
+# ------------------------------------------------------------------ attention on crafted index sets
+
+@pytest.mark.parametrize("H,dqk,dv,k", [(128, 576, 512, 2048), (16, 576, 512, 100), (16, 128, 128, 2048),
+                                        (32, 64, 64, 77)])
+def test_attention_crafted_sets(dsa, H, dqk, dv, k):
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(11)
+    B, Lq, Lk = 2, 6, 3000
+    q = torch.randn(B, Lq, H, dqk, device=dev, generator=g).to(torch.bfloat16)
+    kv = torch.randn(B, Lk, dqk, device=dev, generator=g).to(torch.bfloat16)
+    idx = torch.randint(0, Lk, (B, Lq, k), device=dev, generator=g, dtype=torch.int32)
+    idx[0, 1, k // 2:] = -1                    # padded tail
+    idx[0, 2, :] = -1                          # empty set
+    idx[0, 3, 1:] = -1                         # a single row: out == that row's value
+    idx[1, 0, ::3] = -1                        # holes
+    idx[1, 1, :] = idx[1, 1, :1]               # one row repeated k times
+    scale = 1.0 / math.sqrt(192.0)
+    out, lse = dsa.dsa_sparse_attn(q, kv, idx, dv, scale, q_pos0=Lk - Lq)
+    torch.cuda.synchronize()
+    for b in range(B):
+        o_ref, l_ref = oracle.sparse_attn(q[b].cpu(), kv[b].cpu(), idx[b].cpu().numpy(), dv, scale, BF16)
+        check_attention(out[b].float().cpu().numpy(), o_ref, lse[b].cpu().numpy(), l_ref, True)
+    single = out[0, 3].float().cpu()
+    row = kv[0, idx[0, 3, 0]].float().cpu()[:dv]
+    assert torch.equal(single, row.expand_as(single)), "a one-row set must return that row exactly"
+
+
+def test_attention_fp32_crafted(dsa):
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(5)
+    B, Lq, Lk, H, D, k = 1, 9, 500, 4, 64, 200
+    q = torch.randn(B, Lq, H, D, device=dev, generator=g)
+    kv = torch.randn(B, Lk, D, device=dev, generator=g)
+    idx = torch.randint(-1, Lk, (B, Lq, k), device=dev, generator=g, dtype=torch.int32)
+    out, lse = dsa.dsa_sparse_attn(q, kv, idx, 48, 0.125, q_pos0=Lk - Lq)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.sparse_attn(q[0].cpu(), kv[0].cpu(), idx[0].cpu().numpy(), 48, 0.125, F32)
+    check_attention(out[0].cpu().numpy(), o_ref, lse[0].cpu().numpy(), l_ref, False)
+
+
+# ------------------------------------------------------------------ special cases and determinism
+
+def test_k_ge_L_equals_causal_dense_attention(dsa):
+    """With k >= L every preceding token is selected: the forward must equal
+    causal dense attention (torch SDPA on the CPU in fp64)."""
+    dev = torch.device("cuda:0")
+    cfg = CONFIGS["prefill_L4096"].with_(name="dense", Lq=200, Lk=200, k=200)
+    inp = make_inputs(cfg, seed=2, device=dev)
+    out, idx, lse = dsa.dsa_forward(inp["q_idx"], inp["q_scale"], inp["k_idx"], inp["k_scale"], inp["w"],
+                                    inp["q"], inp["kv"], k=cfg.k, softmax_scale=cfg.softmax_scale,
+                                    d_v=cfg.d_v, idx=torch.empty(1, 200, 200, dtype=torch.int32, device=dev))
+    torch.cuda.synchronize()
+    Q = inp["q"][0].double().cpu().permute(1, 0, 2)
+    K = inp["kv"][0].double().cpu()[None].expand(cfg.n_heads, -1, -1)
+    ref = torch.nn.functional.scaled_dot_product_attention(Q, K, K, is_causal=True, scale=cfg.softmax_scale)
+    check_attention(out[0].float().cpu().numpy(), ref.permute(1, 0, 2).numpy(), None, None, True)
+
+
+def test_repeat_runs_are_bitwise_identical(dsa):
+    dev = torch.device("cuda:0")
+    cfg = CONFIGS["mla_prefill_L32768"].with_(name="det", Lq=2500, Lk=2500, k=2048)
+    inp = make_inputs(cfg, seed=4, device=dev)
+    f = dsa.Forward(1, cfg.Lq, cfg.Lk, cfg.k, cfg.n_heads, cfg.d_v, torch.bfloat16, dev)
+    o1, i1, l1 = [x.clone() for x in f(inp["q_idx"], inp["q_scale"], inp["k_idx"], inp["k_scale"], inp["w"],
+                                      inp["q"], inp["kv"], cfg.softmax_scale)]
+    o2, i2, l2 = f(inp["q_idx"], inp["q_scale"], inp["k_idx"], inp["k_scale"], inp["w"], inp["q"], inp["kv"],
+                   cfg.softmax_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(i1, i2) and torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
+def test_empty_problem_is_a_no_op(dsa):
+    dev = torch.device("cuda:0")
+    s = torch.empty(0, 5, 8, device=dev)
+    idx = dsa.dsa_topk(s, 4)
+    assert idx.shape == (0, 5, 4)
