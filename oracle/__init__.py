@@ -122,6 +122,19 @@ def indexer(q_idx, q_scale, k_idx, k_scale, w, t_pos, dtype: int) -> np.ndarray:
     return out
 
 
+def indexer_abs_mass(q_idx, q_scale, k_idx, k_scale, w, t_pos, dtype: int) -> np.ndarray:
+    """M[t,s] = sum_j |w_j| sum_d |qhat_jd| |khat_d|: the indexer evaluated on
+    absolute values.  It bounds every partial sum of the score, so eps * M
+    bounds accumulation error in any summation order (used for tolerances)."""
+    if dtype == E4M3:
+        qa = _np(q_idx).view(np.uint8) & 0x7F
+        ka = _np(k_idx).view(np.uint8) & 0x7F
+    else:
+        qa = np.abs(_np(q_idx, np.float32))
+        ka = np.abs(_np(k_idx, np.float32))
+    return indexer(qa, q_scale, ka, k_scale, np.abs(_np(w, np.float32)), t_pos, dtype)
+
+
 def topk(scores, t_pos, k: int) -> np.ndarray:
     """Top-k index sets [n_rows, k] int32 (ascending s, -1 padded)."""
     sc = _np(scores, np.float64)

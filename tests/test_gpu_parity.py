@@ -14,7 +14,7 @@ import torch
 
 import oracle
 from dsa_inputs import CONFIGS, make_inputs
-from tests.parity import check_attention, check_scores, check_topk_rows
+from tests.parity import check_attention, check_scores, check_topk_rows, eps_for
 
 pytestmark = pytest.mark.gpu
 
@@ -42,18 +42,6 @@ def _sample_rows(Lq, k, n_random=24, seed=0):
     return np.array(sorted(rows), dtype=np.int64)
 
 
-def _oracle_rows(inp_h, cfg, b, rows):
-    """Oracle scores / top-k / attention for batch entry b and query rows."""
-    dt = E4M3 if cfg.idx_dtype == "fp8" else F32
-    io = BF16 if cfg.io_dtype == "bf16" else F32
-    t_pos = cfg.q_pos0 + rows
-    sc = oracle.indexer(inp_h["q_idx"][b][rows], inp_h["q_scale"][b][rows] if dt == E4M3 else None,
-                        inp_h["k_idx"][b], inp_h["k_scale"][b] if dt == E4M3 else None,
-                        inp_h["w"][b][rows], t_pos, dt)
-    ix = oracle.topk(sc, t_pos, cfg.k)
-    return sc, ix, t_pos
-
-
 def _run_case(dsa, cfg, rows_by_b, seed=0, check_forward=True, q_tile_rows=0):
     dev = torch.device("cuda:0")
     t0 = time.time()
@@ -68,24 +56,26 @@ def _run_case(dsa, cfg, rows_by_b, seed=0, check_forward=True, q_tile_rows=0):
     print(f"  [{cfg.name}] gpu stages done in {time.time() - t0:.1f}s", flush=True)
 
     key_side = {k: _host(inp[k]) for k in ("k_idx", "k_scale", "kv") if k in inp}
-    stats = {"score_err_ratio": 0.0, "exact": [], "attn_err": 0.0}
+    stats = {"score_err_ratio": 0.0, "err_over_mass": 0.0, "exact": [], "attn_err": 0.0}
+    eps = eps_for(fp8, cfg.idx_dim, cfg.n_idx_heads)
     for b, rows in rows_by_b.items():
         rows = np.asarray(rows, dtype=np.int64)
         rt = torch.as_tensor(rows)
         q_side = {k: _host(inp[k][b].index_select(0, rt.to(dev))) for k in ("q_idx", "q_scale", "w", "q")
                   if k in inp}
-        inp_h = {k: {b: v} for k, v in key_side.items()}
-        inp_h.update({k: {b: v} for k, v in q_side.items()})
-        sel = np.arange(len(rows))
         t_pos = cfg.q_pos0 + rows
         dt = E4M3 if fp8 else F32
-        sc_ref = oracle.indexer(q_side["q_idx"], q_side.get("q_scale"), key_side["k_idx"][b],
-                                key_side["k_scale"][b] if fp8 else None, q_side["w"], t_pos, dt)
+        ind_args = (q_side["q_idx"], q_side.get("q_scale"), key_side["k_idx"][b],
+                    key_side["k_scale"][b] if fp8 else None, q_side["w"], t_pos, dt)
+        sc_ref = oracle.indexer(*ind_args)
+        mass = oracle.indexer_abs_mass(*ind_args)
         ix_ref = oracle.topk(sc_ref, t_pos, cfg.k)
         g_sc = _host(scores[b].index_select(0, rt.to(dev))).numpy()
-        stats["score_err_ratio"] = max(stats["score_err_ratio"], check_scores(g_sc, sc_ref, t_pos))
+        ratio, rel_mass = check_scores(g_sc, sc_ref, mass, t_pos, eps)
+        stats["score_err_ratio"] = max(stats["score_err_ratio"], ratio)
+        stats["err_over_mass"] = max(stats["err_over_mass"], rel_mass)
         g_ix = _host(idx[b].index_select(0, rt.to(dev))).numpy()
-        frac, req = check_topk_rows(g_ix, sc_ref, t_pos, cfg.k, ix_ref)
+        frac, req = check_topk_rows(g_ix, sc_ref, mass, eps, t_pos, cfg.k, ix_ref)
         stats["exact"].append(frac)
         # top-k of the GPU's own fp32 scores: both sides decide in fp32, bit-exact
         ix_same_prec = oracle.topk(g_sc.astype(np.float64), t_pos, cfg.k)
@@ -110,7 +100,7 @@ def _run_case(dsa, cfg, rows_by_b, seed=0, check_forward=True, q_tile_rows=0):
         assert torch.equal(fwd_out.view(torch.int16) if fwd_out.dtype == torch.bfloat16 else fwd_out,
                            out.view(torch.int16) if out.dtype == torch.bfloat16 else out), "forward out differs"
         assert torch.equal(fwd_lse, lse), "forward lse differs"
-    print(f"  [{cfg.name}] score err/tol {stats['score_err_ratio']:.3g}, top-k exact "
+    print(f"  [{cfg.name}] score err/tol {stats['score_err_ratio']:.3g} (err/mass {stats['err_over_mass']:.3g}), top-k exact "
           f"{np.mean(stats['exact']):.4f}, attn max err {stats['attn_err']:.3g}, total {time.time() - t0:.1f}s",
           flush=True)
     return stats
@@ -160,6 +150,44 @@ def test_mla_prefill_L32768(dsa):
 def test_decode_B64_ctx65536(dsa):
     cfg = CONFIGS["decode_B64_ctx65536"]
     _run_case(dsa, cfg, {b: np.array([0]) for b in (0, 1, 17, 63)})
+
+
+# ------------------------------------------------------------------ FP8 MFMA dot-product arithmetic
+
+def test_fp8_dot_block_precision(dsa):
+    """Characterises the FP8 MFMA accumulation the indexer relies on.
+
+    One head with q = 1.0 everywhere and w = 1, so the score is the plain sum
+    of a key's 128 e4m3 values.  Sums whose terms lie within 2^10 of each
+    other come out exact; terms 14+ bits below the largest product of their
+    block are dropped (truncation, never an overshoot), so the error stays
+    below 2^-10 of the absolute sum even in these adversarial cases."""
+    dev = torch.device("cuda:0")
+    L, H, D = 16, 64, 128
+    e4 = lambda v: torch.tensor(v, dtype=torch.float32).to(torch.float8_e4m3fn).view(torch.uint8)
+    q = torch.zeros(1, L, H, D, dtype=torch.uint8)
+    q[:, :, 0, :] = e4(1.0)
+    w = torch.zeros(1, L, H)
+    w[:, :, 0] = 1.0
+    keys = [[1.0] * 128, [1.0] + [2.0 ** -9] * 127, [0.5 + 2 ** -4] * 128, [240.0] + [0.125] * 127,
+            [448.0 * (-1) ** i for i in range(128)],                      # exact cases
+            [448.0] + [2.0 ** -9] * 127, [256.0] + [2.0 ** -6] * 127, [448.0] + [1 / 64] * 127,
+            [448.0, -448.0] + [2.0 ** -9] * 126]                          # truncating cases
+    k = torch.zeros(1, L, D, dtype=torch.uint8)
+    for s, vals in enumerate(keys):
+        k[0, s] = e4(vals)
+    sc = dsa.dsa_indexer_scores(q.to(dev), torch.ones(1, L, H, device=dev), k.to(dev),
+                                torch.ones(1, L, device=dev), w.to(dev))
+    torch.cuda.synchronize()
+    got = sc[0, L - 1].double().cpu().numpy()
+    for s, vals in enumerate(keys):
+        v = k[0, s].view(torch.float8_e4m3fn).double()
+        exact = max(float(v.sum()), 0.0)
+        absum = float(v.abs().sum())
+        if s < 5:
+            assert got[s] == exact, (s, got[s], exact)
+        else:
+            assert got[s] <= exact and exact - got[s] <= absum * 2.0 ** -10, (s, got[s], exact)
 
 
 # ------------------------------------------------------------------ top-k on crafted scores (bit-exact)

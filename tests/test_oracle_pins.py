@@ -296,3 +296,18 @@ def test_forward_rows_selects_from_indexer_scores():
     for i, r in enumerate(rows):
         sc = res["scores"][i]
         assert np.array_equal(res["idx"][i], _topk_bruteforce(sc, int(r), cfg.k))
+
+
+def test_abs_mass_bounds_the_score():
+    """M = sum_j |w_j| sum_d |q_jd k_d| >= |I| everywhere (triangle inequality),
+    with equality when every term is non-negative."""
+    L, H, D = 30, 4, 16
+    Q, K, w = _f32(L, H, D), _f32(L, D), _f32(L, H)
+    tp = np.arange(L)
+    I = oracle.indexer(Q, None, K, None, w, tp, F32)
+    M = oracle.indexer_abs_mass(Q, None, K, None, w, tp, F32)
+    m = np.tril(np.ones((L, L), bool))
+    assert np.all(M[m] >= np.abs(I[m]) - 1e-12)
+    Qp, Kp, wp = np.abs(Q), np.abs(K), np.abs(w)
+    assert np.allclose(oracle.indexer(Qp, None, Kp, None, wp, tp, F32)[m],
+                       oracle.indexer_abs_mass(Q, None, K, None, w, tp, F32)[m], rtol=1e-12)
