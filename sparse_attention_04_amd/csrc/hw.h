@@ -11,6 +11,10 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) v4s lds_v4s;
 
 constexpr int kWave = 64;
 
@@ -31,6 +35,51 @@ __device__ __forceinline__ v4f mfma_bf16_16x16x32(const v8bf& a, const v8bf& b, 
 {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+
+// D(32x32 fp32) = A(32x16 bf16) * B(16x32 bf16) + C; lane l supplies 8
+// consecutive K values (slot 8*(l/32)..) of row/column l % 32 and receives
+// D[8*(v/4) + 4*(l/32) + (v%4)][l % 32] in element v = 0..15.
+__device__ __forceinline__ v16f mfma_bf16_32x32x16(const v8bf& a, const v8bf& b, const v16f& c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// LDS transpose read of 16-bit data (ds_read_b64_tr_b16).  Within each group
+// of 16 lanes, lane i receives in element j the (i % 4)-th 16-bit value of the
+// 8 bytes addressed by lane 4*j + i/4 of the same group.
+__device__ __forceinline__ v4s lds_read_tr16(const void* lds_ptr)
+{
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)lds_ptr);
+}
+
+// Asynchronous 16-byte copy global -> LDS.  Lane l's 16 bytes land at
+// lds_base + 16*l (lds_base must be the same for the whole wave); the global
+// address is per lane.  Completion is tracked by vmcnt.
+__device__ __forceinline__ void global_to_lds16(const void* gptr, void* lds_base)
+{
+    __builtin_amdgcn_global_load_lds(gptr, (lds_void*)lds_base, 16, 0, 0);
+}
+
+// The same copy written as a single asm block, for pipelines that fence it
+// themselves (s_waitcnt vmcnt(0) + a barrier before the slot is read).  The
+// compiler then does not see an LDS write here, so it adds no conservative
+// vmcnt wait in front of unrelated LDS reads.  `lds_byte_addr` is the
+// wave-uniform LDS byte address of lane 0's 16 bytes.  m0 is used only here.
+__device__ __forceinline__ void global_to_lds16_async(const void* gptr, uint32_t lds_byte_addr)
+{
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(gptr), "s"(lds_byte_addr)
+                 : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_byte_address(const void* p)
+{
+    return (uint32_t)(uintptr_t)(lds_void*)p;
+}
+
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left unconstrained).
+__device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 __device__ __forceinline__ v8bf as_bf8(const u32x4& u) { return __builtin_bit_cast(v8bf, u); }
 __device__ __forceinline__ v8i as_i8(const u32x4& lo, const u32x4& hi)

@@ -163,6 +163,217 @@ void sparse_attn_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __r
         lse[((int64_t)b * Lq + t) * H + h] = (l > 0.f) ? (m + log2f(l)) * 0.69314718055994531f : -INFINITY;
 }
 
+// bf16 kernel for n_heads % 32 == 0 (the MLA workload): one workgroup per
+// query row, one wave per 32 heads, v_mfma_f32_32x32x16_bf16 throughout.
+//  - The selected latent rows stream through a two-slot LDS ring, 32 rows per
+//    chunk, row-major with one pad piece per row.  Each chunk is copied with
+//    asynchronous 16-byte global->LDS loads issued one chunk ahead, so the
+//    gather of chunk c+1 overlaps the MFMA work of chunk c; one workgroup
+//    barrier per chunk.
+//  - S^T[32 rows x 32 heads] = K_chunk . Q^T, with the wave's Q^T fragments
+//    (32 heads x d_qk) held in registers.
+//  - Softmax in fp32 (exp2 domain) against a per-head reference maximum m
+//    fixed at the first chunk holding a valid row, so O is never rescaled
+//    (no VALU work on the 256 accumulator registers).  Probabilities
+//    exp2(z - m) may exceed 1 by up to 2^64, which bf16 and fp32 carry
+//    without overflow; the final division by the same-frame sum l makes the
+//    result independent of m.  If any logit exceeds m by more than 64 the
+//    pass only keeps tracking the true maximum and the query is recomputed
+//    once with it (workgroup-uniform decision, at most two passes).
+//  - O^T[32 dims x 32 heads] += V^T . P^T, where P^T is the S^T accumulator
+//    converted to bf16 in place (its lane layout is the B-operand layout) and
+//    V^T fragments come straight from the row-major chunk through LDS
+//    transpose reads (no transposed copy of V).
+template <int DQK, int DV>
+struct W32Shape {
+    static constexpr int NC = 32;                         // rows per chunk
+    static constexpr int PIECES = DQK / 8 + 1;            // 16-byte pieces per LDS row (+1 pad)
+    static constexpr int PITCH = PIECES * 8;              // bf16 elements per LDS row
+    static constexpr int BUF_BYTES = NC * PIECES * 16;
+    static constexpr int SLOTS = (NC * PIECES + 63) / 64; // 64-piece copy slots per chunk
+    static constexpr int QC = DQK / 16;                   // MFMA K steps for Q.K
+    // The last QL steps of the query operand live in LDS instead of registers
+    // (for d_qk = 576: the last 128 dims, RoPE part included), which keeps the 32-head
+    // working set (query 4*(QC-QL) + accumulator 256 registers) spill-free.
+    static constexpr int QL = DQK > 256 ? 8 : 0;
+    static constexpr int QR = QC - QL;
+    static constexpr int DT = DV / 32;                    // 32-wide value tiles
+};
+
+template <int DQK, int DV>
+__global__ __launch_bounds__(256)
+void sparse_attn_bf16_w32_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
+                                 const int32_t* __restrict__ idx, uint16_t* __restrict__ out,
+                                 float* __restrict__ lse, int Lq, int Lk, int t_begin, int H, int k,
+                                 int64_t idx_bstride, float scale_log2)
+{
+    using S = W32Shape<DQK, DV>;
+    constexpr int NC = S::NC;
+    __shared__ __attribute__((aligned(16))) uint8_t ring0[S::BUF_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t ring1[S::BUF_BYTES];
+    __shared__ __attribute__((aligned(16))) u32x4 qlds[S::QL > 0 ? 4 * S::QL * 64 : 1];   // [wave][step][lane]
+
+    const int row = blockIdx.x, b = blockIdx.y;
+    const int t = t_begin + row;
+    const int tid = threadIdx.x, lane = tid & 63, nwaves = blockDim.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+    const int col = lane & 31, hi = lane >> 5;
+    const int h = wave * 32 + col;
+
+    const uint16_t* qrow = q + (((int64_t)b * Lq + t) * H + h) * DQK;
+    v8bf qf[S::QR];
+#pragma unroll
+    for (int c = 0; c < S::QR; ++c) qf[c] = as_bf8(*(const u32x4*)(qrow + c * 16 + hi * 8));
+    u32x4* qw = qlds + wave * S::QL * 64 + lane;
+#pragma unroll
+    for (int c = 0; c < S::QL; ++c) qw[c * 64] = *(const u32x4*)(qrow + (S::QR + c) * 16 + hi * 8);
+
+    v16f o[S::DT];
+#pragma unroll
+    for (int i = 0; i < S::DT; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[i][v] = 0.f;
+    float m = -INFINITY, l = 0.f;
+
+    const int32_t* irow = idx + (int64_t)b * idx_bstride + (int64_t)row * k;
+    const uint16_t* kvb = kv + (int64_t)b * Lk * DQK;
+    const int nchunks = (k + NC - 1) / NC;
+
+    // lane r < NC: raw entry r of chunk c (validated only where it is used, so
+    // that the load stays in flight behind the chunk's copies)
+    auto load_idx = [&](int c) -> int {
+        const int i = c * NC + lane;
+        return (lane < NC && i < k) ? irow[i] : -1;
+    };
+    auto valid_row = [&](int s) -> int { return (s >= 0 && s < Lk) ? s : -1; };
+    // queue the asynchronous copy of one chunk (rows given by `rows`) into `dst`
+    auto issue = [&](int rows, uint8_t* dst) {
+        const uint32_t base = __builtin_amdgcn_readfirstlane(lds_byte_address(dst));
+#pragma unroll 1
+        for (int slot = wave; slot < S::SLOTS; slot += nwaves) {
+            const int p = slot * 64 + lane;
+            const int pc = min(p, NC * S::PIECES - 1);
+            const int r = pc / S::PIECES, piece = pc - r * S::PIECES;
+            int s = __shfl(rows, r, kWave);
+            s = s < 0 ? 0 : s;                              // padding rows copy row 0; masked below
+            const int dp = piece < S::PIECES - 1 ? piece : S::PIECES - 2;   // pad piece: any in-row data
+            if (p < NC * S::PIECES)
+                global_to_lds16_async(kvb + (int64_t)s * DQK + dp * 8,
+                                      __builtin_amdgcn_readfirstlane(base + (uint32_t)slot * 1024u));
+        }
+    };
+
+    const int js = (lane & 15) >> 2, qs = lane & 3, g2 = (lane >> 4) & 1;
+    constexpr float kHeadroom = 64.f;                        // log2 units
+    float m_seen = -INFINITY;                                // running true maximum (log2 domain)
+    for (int pass = 0; pass < 2; ++pass) {
+        bool overflow = false;
+        int rows_cur = valid_row(load_idx(0));
+        issue(rows_cur, ring0);
+        int rows_next = nchunks > 1 ? load_idx(1) : -1;
+        for (int c = 0; c < nchunks; ++c) {
+            uint8_t* cur = (c & 1) ? ring1 : ring0;
+            uint8_t* nxt = (c & 1) ? ring0 : ring1;
+            wait_vmcnt0();                                   // this wave's copies of chunk c landed
+            __syncthreads();                                 // all copies landed; chunk c-1 consumed
+            const uint64_t vmask = __ballot(lane < NC && rows_cur >= 0);
+            int rows_after = -1;
+            if (c + 1 < nchunks) {
+                rows_next = valid_row(rows_next);
+                issue(rows_next, nxt);
+                if (c + 2 < nchunks) rows_after = load_idx(c + 2);
+            }
+
+            // S^T (32 rows x 32 heads)
+            v16f sacc;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) sacc[v] = 0.f;
+            const uint16_t* kb = (const uint16_t*)cur + col * S::PITCH + hi * 8;
+            // key fragments are read kPre steps ahead of their MFMA
+            constexpr int kPre = 3;
+            u32x4 kf[kPre + 1];
+#pragma unroll
+            for (int i = 0; i < kPre; ++i) kf[i] = *(const u32x4*)(kb + i * 16);
+#pragma unroll
+            for (int c2 = 0; c2 < S::QC; ++c2) {
+                if (c2 + kPre < S::QC) kf[(c2 + kPre) % (kPre + 1)] = *(const u32x4*)(kb + (c2 + kPre) * 16);
+                const v8bf bq = (c2 < S::QR) ? qf[c2 < S::QR ? c2 : 0] : as_bf8(qw[(c2 - S::QR) * 64]);
+                sacc = mfma_bf16_32x32x16(as_bf8(kf[c2 % (kPre + 1)]), bq, sacc);
+            }
+
+            // logits of head h over the chunk's rows 8*(v/4) + 4*hi + v%4
+            float cmax = -INFINITY;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int r = 8 * (v >> 2) + 4 * hi + (v & 3);
+                const float z = ((vmask >> r) & 1ull) ? sacc[v] * scale_log2 : -INFINITY;
+                sacc[v] = z;
+                cmax = fmaxf(cmax, z);
+            }
+            cmax = fmaxf(cmax, __shfl_xor(cmax, 32, kWave));
+            m_seen = fmaxf(m_seen, cmax);
+            if (m == -INFINITY) m = cmax;                     // first chunk with a valid row fixes m
+            overflow = overflow || (cmax > m + kHeadroom);
+            if (__any(overflow)) {                           // only the maximum is still tracked
+                rows_cur = rows_next;
+                rows_next = rows_after;
+                continue;
+            }
+            float psum = 0.f;
+            uint32_t pw[8];
+#pragma unroll
+            for (int v = 0; v < 16; v += 2) {
+                const float p0 = (sacc[v] == -INFINITY) ? 0.f : exp2f(sacc[v] - m);
+                const float p1 = (sacc[v + 1] == -INFINITY) ? 0.f : exp2f(sacc[v + 1] - m);
+                psum += p0 + p1;
+                pw[v >> 1] = f32_to_bf16_bits(p0) | (f32_to_bf16_bits(p1) << 16);
+            }
+            psum += __shfl_xor(psum, 32, kWave);
+            l += psum;
+
+            // O^T += V^T . P^T, two 16-row K steps
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+                const v8bf pfrag = as_bf8(u32x4{pw[4 * tt], pw[4 * tt + 1], pw[4 * tt + 2], pw[4 * tt + 3]});
+                const uint16_t* vb = (const uint16_t*)cur + (16 * tt + 4 * hi + js) * S::PITCH + 16 * g2 + 4 * qs;
+#pragma unroll
+                for (int dt = 0; dt < S::DT; ++dt) {
+                    const v4s lo4 = lds_read_tr16(vb + dt * 32);
+                    const v4s hi4 = lds_read_tr16(vb + 8 * S::PITCH + dt * 32);
+                    const u32x2 a = __builtin_bit_cast(u32x2, lo4);
+                    const u32x2 bq = __builtin_bit_cast(u32x2, hi4);
+                    o[dt] = mfma_bf16_32x32x16(as_bf8(u32x4{a[0], a[1], bq[0], bq[1]}), pfrag, o[dt]);
+                }
+            }
+            rows_cur = rows_next;
+            rows_next = rows_after;
+        }
+        // every wave must agree before the ring is reused by a second pass
+        if (!__syncthreads_or(overflow ? 1 : 0)) break;
+        // recompute with the true maximum as the reference
+        m = m_seen;
+        l = 0.f;
+#pragma unroll
+        for (int i = 0; i < S::DT; ++i)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) o[i][v] = 0.f;
+    }
+
+    const float inv = (l > 0.f) ? 1.f / l : 0.f;
+    uint16_t* orow = out + (((int64_t)b * Lq + t) * H + h) * DV;
+#pragma unroll
+    for (int dt = 0; dt < S::DT; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int d0 = dt * 32 + 8 * g + 4 * hi;
+            const uint32_t w0 = f32_to_bf16_bits(o[dt][4 * g] * inv) | (f32_to_bf16_bits(o[dt][4 * g + 1] * inv) << 16);
+            const uint32_t w1 = f32_to_bf16_bits(o[dt][4 * g + 2] * inv) | (f32_to_bf16_bits(o[dt][4 * g + 3] * inv) << 16);
+            *(u32x2*)(orow + d0) = u32x2{w0, w1};
+        }
+    if (lse != nullptr && hi == 0)
+        lse[((int64_t)b * Lq + t) * H + h] = (l > 0.f) ? (m + log2f(l)) * 0.69314718055994531f : -INFINITY;
+}
+
 // fp32 kernel for small problems: one workgroup per query row; heads in turn.
 constexpr int kF32T = 256;
 
@@ -255,9 +466,25 @@ bool sparse_attn_bf16_supported(int Dqk, int Dv)
     return (Dqk == 576 && Dv == 512) || (Dqk == 128 && Dv == 128) || (Dqk == 64 && Dv == 64);
 }
 
+template <int DQK, int DV>
+hipError_t launch_bf16_w32(const AttnLaunch& a, hipStream_t s)
+{
+    const int threads = (a.H / 32) * kWave;
+    const float scale_log2 = a.scale * 1.4426950408889634f;
+    hipLaunchKernelGGL((sparse_attn_bf16_w32_kernel<DQK, DV>), dim3(a.t_count, a.B), dim3(threads), 0, s,
+                       (const uint16_t*)a.q, (const uint16_t*)a.kv, a.idx, (uint16_t*)a.out, a.lse,
+                       a.Lq, a.Lk, a.t_begin, a.H, a.k, a.idx_bstride, scale_log2);
+    return hipGetLastError();
+}
+
 hipError_t launch_sparse_attn(const AttnLaunch& a, hipStream_t s)
 {
     if (a.B == 0 || a.t_count == 0) return hipSuccess;
+    if (a.bf16 && a.H % 32 == 0) {
+        if (a.Dqk == 576 && a.Dv == 512) return launch_bf16_w32<576, 512>(a, s);
+        if (a.Dqk == 128 && a.Dv == 128) return launch_bf16_w32<128, 128>(a, s);
+        if (a.Dqk == 64 && a.Dv == 64) return launch_bf16_w32<64, 64>(a, s);
+    }
     if (a.bf16) {
         if (a.Dqk == 576 && a.Dv == 512) return launch_bf16<576, 512>(a, s);
         if (a.Dqk == 128 && a.Dv == 128) return launch_bf16<128, 128>(a, s);
