@@ -73,10 +73,30 @@ __device__ __forceinline__ void global_to_lds16_async(const void* gptr, uint32_t
                  : "memory");
 }
 
+// 4-byte variant: lane l's 4 bytes land at lds_byte_addr + 4*l.
+__device__ __forceinline__ void global_to_lds4_async(const void* gptr, uint32_t lds_byte_addr)
+{
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+                 :
+                 : "v"(gptr), "s"(lds_byte_addr)
+                 : "memory");
+}
+
+// s_waitcnt vmcnt(N) for a compile-time N (expcnt and lgkmcnt unconstrained).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
 __device__ __forceinline__ uint32_t lds_byte_address(const void* p)
 {
     return (uint32_t)(uintptr_t)(lds_void*)p;
 }
+
+// s_waitcnt lgkmcnt(0) (vmcnt and expcnt left unconstrained).
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left unconstrained).
 __device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
@@ -90,15 +110,17 @@ __device__ __forceinline__ v8i as_i8(const u32x4& lo, const u32x4& hi)
     return r;
 }
 
-// fp32 -> bf16 bits, round to nearest even (finite inputs).
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f)
-{
-    uint32_t u = __float_as_uint(f);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return u >> 16;
-}
-
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// Two fp32 -> packed bf16x2 (low half = a), round to nearest even, with the
+// gfx950 conversion instruction (v_cvt_pk_bf16_f32).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
+{
+    const f32x2_t v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
 
 // Order-preserving map of an fp32 score to uint32 (larger score -> larger key);
 // -0.0 is folded onto +0.0 first so the two rank as one value.

@@ -131,7 +131,7 @@ void sparse_attn_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __r
             const float p0 = (z[a0] == -INFINITY) ? 0.f : exp2f(z[a0] - m_new);
             const float p1 = (z[a1] == -INFINITY) ? 0.f : exp2f(z[a1] - m_new);
             psum += p0 + p1;
-            pb[i] = f32_to_bf16_bits(p0) | (f32_to_bf16_bits(p1) << 16);
+            pb[i] = pack_bf16x2(p0, p1);
         }
         psum += __shfl_xor(psum, 16, kWave);
         psum += __shfl_xor(psum, 32, kWave);
@@ -155,8 +155,8 @@ void sparse_attn_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __r
     uint16_t* orow = out + (((int64_t)b * Lq + t) * H + h) * DV;
 #pragma unroll
     for (int dt = 0; dt < S::DT; ++dt) {
-        const uint32_t w0 = f32_to_bf16_bits(o[dt][0] * inv) | (f32_to_bf16_bits(o[dt][1] * inv) << 16);
-        const uint32_t w1 = f32_to_bf16_bits(o[dt][2] * inv) | (f32_to_bf16_bits(o[dt][3] * inv) << 16);
+        const uint32_t w0 = pack_bf16x2(o[dt][0] * inv, o[dt][1] * inv);
+        const uint32_t w1 = pack_bf16x2(o[dt][2] * inv, o[dt][3] * inv);
         *(u32x2*)(orow + dt * 16 + grp * 4) = u32x2{w0, w1};
     }
     if (lse != nullptr && grp == 0)
@@ -165,13 +165,24 @@ void sparse_attn_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __r
 
 // bf16 kernel for n_heads % 32 == 0 (the MLA workload): one workgroup per
 // query row, one wave per 32 heads, v_mfma_f32_32x32x16_bf16 throughout.
-//  - The selected latent rows stream through a two-slot LDS ring, 32 rows per
-//    chunk, row-major with one pad piece per row.  Each chunk is copied with
-//    asynchronous 16-byte global->LDS loads issued one chunk ahead, so the
-//    gather of chunk c+1 overlaps the MFMA work of chunk c; one workgroup
-//    barrier per chunk.
-//  - S^T[32 rows x 32 heads] = K_chunk . Q^T, with the wave's Q^T fragments
-//    (32 heads x d_qk) held in registers.
+//  - The selected latent rows stream through a two-slot LDS ring, 32 rows
+//    per chunk, copied with asynchronous global->LDS loads issued one chunk
+//    ahead, so the copy of chunk c+1 overlaps the MFMA work on chunk c.  A row is stored as its value part (the first d_v columns, one
+//    copy instruction of 64 x 16 bytes, whose source row is wave-uniform) and
+//    its tail (the remaining d_qk - d_v columns, 8 rows per copy
+//    instruction), so the copies need no per-lane row lookups.  The query's
+//    whole index list (k <= 2048) is staged in LDS once, so the only memory
+//    traffic inside the loop is the row copies: s_waitcnt vmcnt(0) plus one
+//    workgroup barrier per chunk publishes a chunk and frees the other slot.
+//  - Value parts sit at a pitch of 1040 bytes (one 16-byte skew per row) and
+//    S^T row slot m = 16t + 8a + 4h + j holds chunk row 16t + 2a + h + 4j.
+//    With that order both the key-fragment reads (16 rows per quarter-wave)
+//    and the transpose reads (rows 4 apart, 8 bytes per lane) cover all 64
+//    LDS banks exactly once, and every fragment address is one per-lane base
+//    plus an immediate.  Tails are packed 8 rows per 1 KB with piece c of
+//    row r at position c ^ (r % 8).
+//  - S^T[32 rows x 32 heads] = K_chunk . Q^T, the query operand held in
+//    registers except its last QL steps (kept in LDS to stay spill-free).
 //  - Softmax in fp32 (exp2 domain) against a per-head reference maximum m
 //    fixed at the first chunk holding a valid row, so O is never rescaled
 //    (no VALU work on the 256 accumulator registers).  Probabilities
@@ -184,38 +195,50 @@ void sparse_attn_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __r
 //    converted to bf16 in place (its lane layout is the B-operand layout) and
 //    V^T fragments come straight from the row-major chunk through LDS
 //    transpose reads (no transposed copy of V).
-template <int DQK, int DV>
+template <int DQK, int DV, int NW>
 struct W32Shape {
     static constexpr int NC = 32;                         // rows per chunk
-    static constexpr int PIECES = DQK / 8 + 1;            // 16-byte pieces per LDS row (+1 pad)
-    static constexpr int PITCH = PIECES * 8;              // bf16 elements per LDS row
-    static constexpr int BUF_BYTES = NC * PIECES * 16;
-    static constexpr int SLOTS = (NC * PIECES + 63) / 64; // 64-piece copy slots per chunk
+    static constexpr int NBUF = 2;                        // ring slots
+    static constexpr int VP = DV / 8;                     // 16-byte pieces of the value part
+    static constexpr int TP = (DQK - DV) / 8;             // pieces of the tail
+    static constexpr int VPITCH = VP * 16 + 16;           // bytes per value part in LDS (+1 skew piece)
+    static constexpr int VBYTES = NC * VPITCH;            // value parts of one chunk
+    static constexpr int TBYTES = NC * TP * 16;           // tails of one chunk
+    static constexpr int BUF_BYTES = VBYTES + TBYTES;
+    static constexpr int RPW = NC / NW;                   // value rows copied per wave
+    static constexpr int TI = TBYTES / 1024;              // tail copy instructions per chunk
+    static constexpr int SPW = RPW + TI / NW;             // copy instructions per wave per chunk
     static constexpr int QC = DQK / 16;                   // MFMA K steps for Q.K
-    // The last QL steps of the query operand live in LDS instead of registers
-    // (for d_qk = 576: the last 128 dims, RoPE part included), which keeps the 32-head
-    // working set (query 4*(QC-QL) + accumulator 256 registers) spill-free.
-    static constexpr int QL = DQK > 256 ? 8 : 0;
+    static constexpr int QL = DQK > 256 ? 19 : 0;         // query steps kept in LDS
     static constexpr int QR = QC - QL;
     static constexpr int DT = DV / 32;                    // 32-wide value tiles
+    static constexpr int KMAX = 2048;                     // largest k whose index list is staged in LDS
+    static_assert(VP == 64, "one copy instruction per value part");
+    static_assert(TP == 8 && TI == 4 && TI % NW == 0, "8-piece tails, 8 rows per copy");
 };
 
-template <int DQK, int DV>
-__global__ __launch_bounds__(256)
+// chunk row held by S^T row slot m (a permutation of 0..31, see above)
+__device__ __forceinline__ constexpr int slot_row(int m)
+{
+    return (m & 16) | (((m >> 3) & 1) << 1) | ((m >> 2) & 1) | ((m & 3) << 2);
+}
+
+template <int DQK, int DV, int NW>
+__global__ __launch_bounds__(64 * NW)
 void sparse_attn_bf16_w32_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
                                  const int32_t* __restrict__ idx, uint16_t* __restrict__ out,
                                  float* __restrict__ lse, int Lq, int Lk, int t_begin, int H, int k,
                                  int64_t idx_bstride, float scale_log2)
 {
-    using S = W32Shape<DQK, DV>;
+    using S = W32Shape<DQK, DV, NW>;
     constexpr int NC = S::NC;
-    __shared__ __attribute__((aligned(16))) uint8_t ring0[S::BUF_BYTES];
-    __shared__ __attribute__((aligned(16))) uint8_t ring1[S::BUF_BYTES];
-    __shared__ __attribute__((aligned(16))) u32x4 qlds[S::QL > 0 ? 4 * S::QL * 64 : 1];   // [wave][step][lane]
+    __shared__ __attribute__((aligned(16))) uint8_t ring[S::NBUF][S::BUF_BYTES];
+    __shared__ __attribute__((aligned(16))) int32_t sel[S::KMAX];   // the query's index list (-1 padded)
+    __shared__ __attribute__((aligned(16))) u32x4 qlds[S::QL > 0 ? NW * S::QL * 64 : 1];   // [wave][step][lane]
 
     const int row = blockIdx.x, b = blockIdx.y;
     const int t = t_begin + row;
-    const int tid = threadIdx.x, lane = tid & 63, nwaves = blockDim.x >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int col = lane & 31, hi = lane >> 5;
     const int h = wave * 32 + col;
@@ -239,27 +262,45 @@ void sparse_attn_bf16_w32_kernel(const uint16_t* __restrict__ q, const uint16_t*
     const uint16_t* kvb = kv + (int64_t)b * Lk * DQK;
     const int nchunks = (k + NC - 1) / NC;
 
-    // lane r < NC: raw entry r of chunk c (validated only where it is used, so
-    // that the load stays in flight behind the chunk's copies)
-    auto load_idx = [&](int c) -> int {
-        const int i = c * NC + lane;
-        return (lane < NC && i < k) ? irow[i] : -1;
+    // stage the index list; entries that cannot be read become -1
+    for (int i = tid; i < S::KMAX; i += 64 * NW) {
+        const int sidx = (i < k) ? irow[i] : -1;
+        sel[i] = (sidx >= 0 && sidx < Lk) ? sidx : -1;
+    }
+    __syncthreads();
+    // bit r set when entry r of chunk c is a real row
+    auto valid_mask = [&](int c) -> uint32_t {
+        return (uint32_t)__ballot(lane < NC && sel[c * NC + (lane & 31)] >= 0);
     };
-    auto valid_row = [&](int s) -> int { return (s >= 0 && s < Lk) ? s : -1; };
-    // queue the asynchronous copy of one chunk (rows given by `rows`) into `dst`
-    auto issue = [&](int rows, uint8_t* dst) {
-        const uint32_t base = __builtin_amdgcn_readfirstlane(lds_byte_address(dst));
-#pragma unroll 1
-        for (int slot = wave; slot < S::SLOTS; slot += nwaves) {
-            const int p = slot * 64 + lane;
-            const int pc = min(p, NC * S::PIECES - 1);
-            const int r = pc / S::PIECES, piece = pc - r * S::PIECES;
-            int s = __shfl(rows, r, kWave);
-            s = s < 0 ? 0 : s;                              // padding rows copy row 0; masked below
-            const int dp = piece < S::PIECES - 1 ? piece : S::PIECES - 2;   // pad piece: any in-row data
-            if (p < NC * S::PIECES)
-                global_to_lds16_async(kvb + (int64_t)s * DQK + dp * 8,
-                                      __builtin_amdgcn_readfirstlane(base + (uint32_t)slot * 1024u));
+    // this wave's copies of chunk c: RPW value parts, then its share of tails.
+    // Padding entries copy row 0; they are masked in the softmax.
+    auto issue_chunk = [&](int c) {
+        const int32_t* rr_ = &sel[c * NC];
+        int vr[S::RPW];
+#pragma unroll
+        for (int e = 0; e < S::RPW; e += 4) {
+            const u32x4 x = *(const u32x4*)(rr_ + wave * S::RPW + e);   // same address on every lane
+            vr[e] = (int)x[0]; vr[e + 1] = (int)x[1]; vr[e + 2] = (int)x[2]; vr[e + 3] = (int)x[3];
+        }
+        int trow[S::TI / NW];
+#pragma unroll
+        for (int j = 0; j < S::TI / NW; ++j) trow[j] = rr_[8 * (wave * (S::TI / NW) + j) + (lane >> 3)];
+        const uint32_t vbase = __builtin_amdgcn_readfirstlane(lds_byte_address(ring[c % S::NBUF]));
+#pragma unroll
+        for (int e = 0; e < S::RPW; ++e) {
+            const int r = wave * S::RPW + e;
+            const int sr = max(__builtin_amdgcn_readfirstlane(vr[e]), 0);
+            global_to_lds16_async(kvb + (int64_t)sr * DQK + lane * 8,
+                                  __builtin_amdgcn_readfirstlane(vbase + (uint32_t)r * S::VPITCH));
+        }
+#pragma unroll
+        for (int j = 0; j < S::TI / NW; ++j) {
+            const int ti = wave * (S::TI / NW) + j;          // tail instruction: rows 8*ti .. 8*ti+7
+            const int r = 8 * ti + (lane >> 3);
+            const int sr = max(trow[j], 0);
+            const int piece = (lane & 7) ^ (r & 7);
+            global_to_lds16_async(kvb + (int64_t)sr * DQK + DV + piece * 8,
+                                  __builtin_amdgcn_readfirstlane(vbase + (uint32_t)(S::VBYTES + ti * 1024)));
         }
     };
 
@@ -268,85 +309,108 @@ void sparse_attn_bf16_w32_kernel(const uint16_t* __restrict__ q, const uint16_t*
     float m_seen = -INFINITY;                                // running true maximum (log2 domain)
     for (int pass = 0; pass < 2; ++pass) {
         bool overflow = false;
-        int rows_cur = valid_row(load_idx(0));
-        issue(rows_cur, ring0);
-        int rows_next = nchunks > 1 ? load_idx(1) : -1;
-        for (int c = 0; c < nchunks; ++c) {
-            uint8_t* cur = (c & 1) ? ring1 : ring0;
-            uint8_t* nxt = (c & 1) ? ring0 : ring1;
-            wait_vmcnt0();                                   // this wave's copies of chunk c landed
-            __syncthreads();                                 // all copies landed; chunk c-1 consumed
-            const uint64_t vmask = __ballot(lane < NC && rows_cur >= 0);
-            int rows_after = -1;
-            if (c + 1 < nchunks) {
-                rows_next = valid_row(rows_next);
-                issue(rows_next, nxt);
-                if (c + 2 < nchunks) rows_after = load_idx(c + 2);
-            }
+        // Iteration `it` computes chunk `it` and, once every wave is past
+        // chunk it-1, issues chunk it+1 into the freed slot.
+        for (int it = -1; it < nchunks; ++it) {
+            wait_vmcnt0();                                   // this wave's copies of chunk it landed
+            __syncthreads();                                 // all of chunk it visible; chunk it-1 consumed
+            const int c = it < 0 ? 0 : it;
+            const uint32_t vmask = valid_mask(c);
+            const uint8_t* cur = ring[c % S::NBUF];
 
-            // S^T (32 rows x 32 heads)
+            // S^T (32 rows x 32 heads); key fragments read kPre steps ahead.
+            // Step c2 < DV/16 reads value-part piece 2*c2 + hi of row
+            // slot_row(col); later steps read the tail.
             v16f sacc;
 #pragma unroll
             for (int v = 0; v < 16; ++v) sacc[v] = 0.f;
-            const uint16_t* kb = (const uint16_t*)cur + col * S::PITCH + hi * 8;
-            // key fragments are read kPre steps ahead of their MFMA
-            constexpr int kPre = 3;
-            u32x4 kf[kPre + 1];
+            if (it >= 0) {
+                const int krow_i = slot_row(col);
+                const uint8_t* vrow = cur + krow_i * S::VPITCH + hi * 16;
+                const uint8_t* trow = cur + S::VBYTES + krow_i * (S::TP * 16);
+                const int tsw = krow_i & 7;
+                auto kfrag = [&](int c2) -> u32x4 {
+                    if (c2 < DV / 16) return *(const u32x4*)(vrow + 32 * c2);
+                    return *(const u32x4*)(trow + (((2 * (c2 - DV / 16) + hi) ^ tsw) << 4));
+                };
+                constexpr int kPre = 7;
+                u32x4 kf[kPre + 1];
 #pragma unroll
-            for (int i = 0; i < kPre; ++i) kf[i] = *(const u32x4*)(kb + i * 16);
+                for (int i = 0; i < kPre; ++i) kf[i] = kfrag(i);
 #pragma unroll
-            for (int c2 = 0; c2 < S::QC; ++c2) {
-                if (c2 + kPre < S::QC) kf[(c2 + kPre) % (kPre + 1)] = *(const u32x4*)(kb + (c2 + kPre) * 16);
-                const v8bf bq = (c2 < S::QR) ? qf[c2 < S::QR ? c2 : 0] : as_bf8(qw[(c2 - S::QR) * 64]);
-                sacc = mfma_bf16_32x32x16(as_bf8(kf[c2 % (kPre + 1)]), bq, sacc);
+                for (int c2 = 0; c2 < S::QC; ++c2) {
+                    if (c2 + kPre < S::QC) kf[(c2 + kPre) % (kPre + 1)] = kfrag(c2 + kPre);
+                    const v8bf bq = (c2 < S::QR) ? qf[c2 < S::QR ? c2 : 0] : as_bf8(qw[(c2 - S::QR) * 64]);
+                    sacc = mfma_bf16_32x32x16(as_bf8(kf[c2 % (kPre + 1)]), bq, sacc);
+                }
             }
+            // queue the next chunk (while the last QK MFMAs drain)
+            if (it + 1 < nchunks) issue_chunk(it + 1);
+            if (it < 0) continue;
 
-            // logits of head h over the chunk's rows 8*(v/4) + 4*hi + v%4
-            float cmax = -INFINITY;
+            // Softmax of head h over the chunk's rows.  Probabilities only
+            // need the reference m (fixed at the first chunk with a valid row),
+            // so they feed the PV product right away; the chunk maximum (for
+            // the overflow check) is taken afterwards, off the critical path.
+            if (vmask == 0u) continue;                       // nothing selected here (uniform)
+            if (vmask != 0xFFFFFFFFu) {
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int r = 8 * (v >> 2) + 4 * hi + (v & 3);
-                const float z = ((vmask >> r) & 1ull) ? sacc[v] * scale_log2 : -INFINITY;
-                sacc[v] = z;
-                cmax = fmaxf(cmax, z);
+                for (int v = 0; v < 16; ++v) {
+                    const int r = slot_row(8 * (v >> 2) + 4 * hi + (v & 3));
+                    sacc[v] = ((vmask >> r) & 1u) ? sacc[v] : -INFINITY;
+                }
             }
-            cmax = fmaxf(cmax, __shfl_xor(cmax, 32, kWave));
-            m_seen = fmaxf(m_seen, cmax);
-            if (m == -INFINITY) m = cmax;                     // first chunk with a valid row fixes m
-            overflow = overflow || (cmax > m + kHeadroom);
+            if (__any(m == -INFINITY)) {                     // first chunk holding a valid row
+                float cmax0 = -INFINITY;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) cmax0 = fmaxf(cmax0, sacc[v]);
+                m = fmaxf(cmax0, __shfl_xor(cmax0, 32, kWave)) * scale_log2;
+            }
             if (__any(overflow)) {                           // only the maximum is still tracked
-                rows_cur = rows_next;
-                rows_next = rows_after;
+                float cm = -INFINITY;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) cm = fmaxf(cm, sacc[v]);
+                m_seen = fmaxf(m_seen, fmaxf(cm, __shfl_xor(cm, 32, kWave)) * scale_log2);
                 continue;
             }
-            float psum = 0.f;
+            const float negm = -m;
             uint32_t pw[8];
+            float psum = 0.f, cmax = -INFINITY;
 #pragma unroll
             for (int v = 0; v < 16; v += 2) {
-                const float p0 = (sacc[v] == -INFINITY) ? 0.f : exp2f(sacc[v] - m);
-                const float p1 = (sacc[v + 1] == -INFINITY) ? 0.f : exp2f(sacc[v + 1] - m);
+                // masked entries are -inf: exp2(-inf) = 0
+                const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[v], scale_log2, negm));
+                const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[v + 1], scale_log2, negm));
                 psum += p0 + p1;
-                pw[v >> 1] = f32_to_bf16_bits(p0) | (f32_to_bf16_bits(p1) << 16);
+                cmax = fmaxf(cmax, fmaxf(sacc[v], sacc[v + 1]));
+                pw[v >> 1] = pack_bf16x2(p0, p1);
             }
-            psum += __shfl_xor(psum, 32, kWave);
-            l += psum;
 
-            // O^T += V^T . P^T, two 16-row K steps
+            // O^T += V^T . P^T, two 16-row K steps.  K slot (a, j) of lane group
+            // hi is S^T row slot 16*tt + 8a + 4*hi + j, i.e. chunk row
+            // 16*tt + 2a + hi + 4j; the lane reads dims dt*32 + 16*g2 + 4*qs ..
+            // +3 of its source row (8 bytes at 64*dt + 32*g2 + 8*qs).
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) {
                 const v8bf pfrag = as_bf8(u32x4{pw[4 * tt], pw[4 * tt + 1], pw[4 * tt + 2], pw[4 * tt + 3]});
-                const uint16_t* vb = (const uint16_t*)cur + (16 * tt + 4 * hi + js) * S::PITCH + 16 * g2 + 4 * qs;
+                const int r0 = 16 * tt + hi + 4 * js, r1 = r0 + 2;
+                const uint8_t* v0 = cur + r0 * S::VPITCH + 32 * g2 + 8 * qs;
+                const uint8_t* v1 = cur + r1 * S::VPITCH + 32 * g2 + 8 * qs;
 #pragma unroll
                 for (int dt = 0; dt < S::DT; ++dt) {
-                    const v4s lo4 = lds_read_tr16(vb + dt * 32);
-                    const v4s hi4 = lds_read_tr16(vb + 8 * S::PITCH + dt * 32);
+                    const v4s lo4 = lds_read_tr16(v0 + 64 * dt);
+                    const v4s hi4 = lds_read_tr16(v1 + 64 * dt);
                     const u32x2 a = __builtin_bit_cast(u32x2, lo4);
                     const u32x2 bq = __builtin_bit_cast(u32x2, hi4);
                     o[dt] = mfma_bf16_32x32x16(as_bf8(u32x4{a[0], a[1], bq[0], bq[1]}), pfrag, o[dt]);
                 }
             }
-            rows_cur = rows_next;
-            rows_next = rows_after;
+            // bookkeeping that overlaps the PV MFMAs: sum and maximum
+            psum += __shfl_xor(psum, 32, kWave);
+            l += psum;
+            cmax = fmaxf(cmax, __shfl_xor(cmax, 32, kWave)) * scale_log2;
+            m_seen = fmaxf(m_seen, cmax);
+            overflow = overflow || (cmax > m + kHeadroom);
         }
         // every wave must agree before the ring is reused by a second pass
         if (!__syncthreads_or(overflow ? 1 : 0)) break;
@@ -366,8 +430,8 @@ void sparse_attn_bf16_w32_kernel(const uint16_t* __restrict__ q, const uint16_t*
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const int d0 = dt * 32 + 8 * g + 4 * hi;
-            const uint32_t w0 = f32_to_bf16_bits(o[dt][4 * g] * inv) | (f32_to_bf16_bits(o[dt][4 * g + 1] * inv) << 16);
-            const uint32_t w1 = f32_to_bf16_bits(o[dt][4 * g + 2] * inv) | (f32_to_bf16_bits(o[dt][4 * g + 3] * inv) << 16);
+            const uint32_t w0 = pack_bf16x2(o[dt][4 * g] * inv, o[dt][4 * g + 1] * inv);
+            const uint32_t w1 = pack_bf16x2(o[dt][4 * g + 2] * inv, o[dt][4 * g + 3] * inv);
             *(u32x2*)(orow + d0) = u32x2{w0, w1};
         }
     if (lse != nullptr && hi == 0)
@@ -466,24 +530,37 @@ bool sparse_attn_bf16_supported(int Dqk, int Dv)
     return (Dqk == 576 && Dv == 512) || (Dqk == 128 && Dv == 128) || (Dqk == 64 && Dv == 64);
 }
 
-template <int DQK, int DV>
+template <int DQK, int DV, int NW>
 hipError_t launch_bf16_w32(const AttnLaunch& a, hipStream_t s)
 {
-    const int threads = (a.H / 32) * kWave;
     const float scale_log2 = a.scale * 1.4426950408889634f;
-    hipLaunchKernelGGL((sparse_attn_bf16_w32_kernel<DQK, DV>), dim3(a.t_count, a.B), dim3(threads), 0, s,
+    hipLaunchKernelGGL((sparse_attn_bf16_w32_kernel<DQK, DV, NW>), dim3(a.t_count, a.B), dim3(64 * NW), 0, s,
                        (const uint16_t*)a.q, (const uint16_t*)a.kv, a.idx, (uint16_t*)a.out, a.lse,
                        a.Lq, a.Lk, a.t_begin, a.H, a.k, a.idx_bstride, scale_log2);
     return hipGetLastError();
 }
 
+template <int DQK, int DV>
+hipError_t launch_bf16_w32_any(const AttnLaunch& a, hipStream_t s, bool* handled)
+{
+    *handled = true;
+    switch (a.H / 32) {
+    case 1: return launch_bf16_w32<DQK, DV, 1>(a, s);
+    case 2: return launch_bf16_w32<DQK, DV, 2>(a, s);
+    case 4: return launch_bf16_w32<DQK, DV, 4>(a, s);
+    }
+    *handled = false;
+    return hipSuccess;
+}
+
 hipError_t launch_sparse_attn(const AttnLaunch& a, hipStream_t s)
 {
     if (a.B == 0 || a.t_count == 0) return hipSuccess;
-    if (a.bf16 && a.H % 32 == 0) {
-        if (a.Dqk == 576 && a.Dv == 512) return launch_bf16_w32<576, 512>(a, s);
-        if (a.Dqk == 128 && a.Dv == 128) return launch_bf16_w32<128, 128>(a, s);
-        if (a.Dqk == 64 && a.Dv == 64) return launch_bf16_w32<64, 64>(a, s);
+    if (a.bf16 && a.H % 32 == 0 && a.k <= 2048) {
+        bool handled = false;
+        hipError_t e = hipSuccess;
+        if (a.Dqk == 576 && a.Dv == 512) e = launch_bf16_w32_any<576, 512>(a, s, &handled);
+        if (handled) return e;
     }
     if (a.bf16) {
         if (a.Dqk == 576 && a.Dv == 512) return launch_bf16<576, 512>(a, s);
