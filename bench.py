@@ -86,7 +86,9 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="mla_prefill_L32768")
-    ap.add_argument("--cpu-rows", type=int, default=48, help="oracle sample size (0 = skip)")
+    ap.add_argument("--cpu-rows", type=int, default=768, help="oracle sample size in query rows (0 = skip)")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB before timing (counter calibration)")
     ap.add_argument("--no-stages", action="store_true", help="skip the per-stage timing loops")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -107,6 +109,16 @@ def main():
     inp = make_inputs(cfg, seed=0, device=dev)
     torch.cuda.synchronize()
     work = algorithmic(cfg)
+    if args.copy_mib > 0:
+        # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE counter readings
+        # calibrate the HBM traffic counters of the kernels below
+        n = args.copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     fwd = dsa.Forward(cfg.B, cfg.Lq, cfg.Lk, cfg.k, cfg.n_heads, cfg.d_v, inp["q"].dtype, dev,
                       q_tile_rows=cfg.q_tile_rows)

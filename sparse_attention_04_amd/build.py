@@ -12,8 +12,27 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdsa.so")
-SOURCES = ["dsa_capi.cpp", "indexer.hip", "topk.hip", "sparse_attn.hip"]
+OBJ_DIR = os.path.join(HERE, "_build")
 ARCH = "gfx950"
+# Per-source extra flags.  The indexer's MFMA results are consumed by vector
+# fmas at once, so its MFMAs are built in the VGPR-destination form (an AGPR
+# destination would need a copy-out instruction per element); the attention
+# kernel keeps its accumulators in AGPRs.
+SOURCES = [
+    ("dsa_capi.cpp", []),
+    ("indexer.hip", ["-mllvm", "-amdgpu-mfma-vgpr-form"]),
+    ("topk.hip", []),
+    ("sparse_attn.hip", []),
+]
+COMMON = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+    # packed fp32 VALU forms are disabled on purpose: plain v_fma/v_mul only
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function", "-Wno-unknown-pragmas",
+    "-I", os.path.join(os.path.dirname(HERE), "include"),
+]
+# hipcc's host pass does not know the packed-fp32 feature; that warning is noise
+_NOISE = "'-packed-fp32-ops' is not a recognized feature"
 
 
 def hipcc() -> str:
@@ -23,32 +42,40 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libdsa.so)")
 
 
-def command(out: str = LIB, extra=()) -> list:
-    return [
-        hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-        # packed fp32 VALU forms are disabled on purpose: plain v_fma/v_mul only
-        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        "-Wall", "-Wno-unused-function", "-Wno-unknown-pragmas",
-        "-I", os.path.join(os.path.dirname(HERE), "include"),
-        *extra,
-        "-o", out,
-        "-x", "hip", *[os.path.join(CSRC, s) for s in SOURCES],
-    ]
+def compile_command(src: str, obj: str, extra=()) -> list:
+    flags = dict(SOURCES)[src]
+    return [hipcc(), *COMMON, *flags, *extra, "-c", "-x", "hip", os.path.join(CSRC, src), "-o", obj]
+
+
+def link_command(objs, out: str) -> list:
+    return [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", out, *objs]
+
+
+def _run(cmds, verbose: bool):
+    procs = []
+    for cmd in cmds:
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)))
+    errors = []
+    for cmd, p in procs:
+        out, err = p.communicate()
+        err = "\n".join(l for l in err.splitlines() if _NOISE not in l)
+        if p.returncode != 0:
+            errors.append(f"{' '.join(cmd)}\n(exit {p.returncode}):\n{err}")
+        elif verbose and err.strip():
+            print(err, file=sys.stderr)
+    if errors:
+        raise RuntimeError("hipcc failed:\n" + "\n\n".join(errors))
 
 
 def build(verbose: bool = False) -> str:
+    """Compile every source for gfx950 (in parallel) and link libdsa.so."""
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    objs = [os.path.join(OBJ_DIR, os.path.splitext(s)[0] + ".o") for s, _ in SOURCES]
+    _run([compile_command(s, o) for (s, _), o in zip(SOURCES, objs)], verbose)
     tmp = LIB + ".tmp"
-    cmd = command(tmp)
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    # hipcc's host pass does not know the packed-fp32 feature; drop that noise
-    noise = "'-packed-fp32-ops' is not a recognized feature"
-    err = "\n".join(l for l in r.stderr.splitlines() if noise not in l)
-    if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{err}")
-    if verbose and err.strip():
-        print(err, file=sys.stderr)
+    _run([link_command(objs, tmp)], verbose)
     os.replace(tmp, LIB)
     return LIB
 

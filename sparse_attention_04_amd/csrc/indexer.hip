@@ -4,17 +4,27 @@
 // for s <= t_pos ("DeepseekV3.2 拆解", section 核心组件, indexer equation; the
 // FP8 format and the ReLU are the page's choices for throughput).
 //
-// FP8 kernel layout (H^I = 64 heads, d^I = 128):
+// FP8 kernel.  With ReLU(x) = (x + |x|) / 2 the score splits into a linear part
+// and an absolute part:
+//   I[t,s] = k_scale[s] * ( c[t,:] . k8[s,:]  +  sum_j v[t,j] * |q8[t,j,:] . k8[s,:]| )
+//   v[t,j] = w[t,j] * q_scale[t,j] / 2,   c[t,d] = sum_j v[t,j] * q8[t,j,d].
+// The absolute part costs one fused multiply-add per (query, key, head) (the
+// |.| is a free source modifier), half the vector work of max + fma; the
+// linear part is one 128-long dot product per (query, key), done on the bf16
+// matrix cores with c split into three bf16 parts (keys are exact in bf16).
+//
+// Layout (H^I = 64 heads, d^I = 128):
 //  - one workgroup = 4 waves = one block of 16 query rows;
 //  - wave w keeps the e4m3 query fragments of heads 16w..16w+15 for the 16
-//    rows in registers (one 16x128 MFMA operand per head, 8 VGPRs each);
-//  - keys stream through LDS in groups of 64 (8 KB); every key fragment is
-//    reused for the wave's 16 heads;
-//  - per head, one v_mfma_f32_16x16x128_f8f6f4 forms the 16-key x 16-query dot
-//    products with a fresh fp32 accumulator (K = 128 = d^I, so there is no
-//    long FP8 accumulation chain), and the epilogue applies ReLU and the
-//    per-(query, head) weight in fp32 registers;
-//  - the four waves' partial head sums meet in LDS, are multiplied by the key
+//    rows in registers (one 16x128 MFMA operand per head, 8 VGPRs each) and
+//    the bf16 parts of c for dims {32g + 8w + e : g < 4, e < 8};
+//  - keys stream through a two-slot LDS tile in groups of 64 (8 KB), copied
+//    global -> LDS asynchronously one group ahead;
+//  - per 16-key tile a wave runs 3 bf16 MFMAs (its slice of the linear part)
+//    and 16 v_mfma_f32_16x16x128_f8f6f4 (one per head, fresh fp32 accumulator:
+//    K = 128 = d^I, so there is no long FP8 accumulation chain), each followed
+//    by four |.|-fmas into the tile's accumulator;
+//  - the four waves' partial sums meet in LDS, are multiplied by the key
 //    scale, masked causally and written as fp32.
 // The MFMA operand roles are A = keys (M), B = queries (N), so a lane's four
 // outputs are four consecutive keys of one query and its head weight is one
@@ -33,6 +43,14 @@ constexpr int kH = 64;         // indexer heads
 constexpr int kHPW = 16;       // heads per wave
 constexpr int kThreads = 256;  // 4 waves
 
+// Byte offset of 16-byte chunk `c` (0..7) of row `r` of the LDS key tile.  The
+// chunks of a row are permuted by (r >> 1) & 7, so 16 consecutive rows read at
+// one logical chunk cover all 64 banks exactly once.
+__device__ __forceinline__ int ktile_off(int r, int c) { return r * kD + ((c ^ ((r >> 1) & 7)) << 4); }
+
+// Round to bf16 (nearest even) and return the rounded value as fp32.
+__device__ __forceinline__ float round_bf16(float x) { return bf16_bits_to_f32(pack_bf16x2(x, 0.f) & 0xFFFFu); }
+
 __global__ __launch_bounds__(kThreads)
 void indexer_fp8_kernel(const uint8_t* __restrict__ q8, const float* __restrict__ q_scale,
                         const uint8_t* __restrict__ k8, const float* __restrict__ k_scale,
@@ -40,8 +58,9 @@ void indexer_fp8_kernel(const uint8_t* __restrict__ q8, const float* __restrict_
                         int Lq, int Lk, int q_pos0, int t_begin, int t_count,
                         int64_t sc_bstride, int64_t sc_rstride, int write_masked, int skip_upto_k)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t ktile[kKG * kD];
-    __shared__ __attribute__((aligned(16))) v4f red[4][4][kWave];   // [wave][tile][lane]
+    __shared__ __attribute__((aligned(16))) uint8_t ktile[2][kKG * kD];
+    __shared__ __attribute__((aligned(16))) v4f red[2][4][4][kWave];     // [buffer][wave][tile][lane]
+    __shared__ __attribute__((aligned(16))) uint32_t cpart[3][kQB][kD / 2]; // bf16 pairs: hi, mid, lo
 
     const int nqb = (t_count + kQB - 1) / kQB;
     const int qb = nqb - 1 - (int)blockIdx.x;          // longest rows first
@@ -53,82 +72,157 @@ void indexer_fp8_kernel(const uint8_t* __restrict__ q8, const float* __restrict_
         return;
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 15, grp = lane >> 4;
 
-    // Query operand (B): row t0 + col, head j, bytes [32*grp, 32*grp + 32).
+    // Absolute part, operand B: row t0 + col, head j, bytes [32*grp, 32*grp + 32).
     const int tq = t0 + min(col, rows_here - 1);
     const int64_t qrow = (int64_t)b * Lq + tq;
     v8i qf[kHPW];
-    float wq[kHPW];
+    float wv[kHPW];
 #pragma unroll
     for (int h = 0; h < kHPW; ++h) {
         const int j = wave * kHPW + h;
         const u32x4* p = (const u32x4*)(q8 + (qrow * kH + j) * kD + grp * 32);
         qf[h] = as_i8(p[0], p[1]);
-        wq[h] = w[qrow * kH + j] * q_scale[qrow * kH + j];
+        wv[h] = 0.5f * w[qrow * kH + j] * q_scale[qrow * kH + j];
+    }
+
+    // Linear part: thread (row r, dims d0..d0+7) forms c[r, d] from all heads
+    // (four interleaved partial sums, then a pairwise combine) and stores its
+    // three-way bf16 split.
+    {
+        const int r = tid >> 4, d0 = (tid & 15) * 8;
+        const int64_t row = (int64_t)b * Lq + t0 + min(r, rows_here - 1);
+        float part[4][8];
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) part[p][e] = 0.f;
+#pragma unroll 4
+        for (int j = 0; j < kH; ++j) {
+            const float v = 0.5f * w[row * kH + j] * q_scale[row * kH + j];
+            const u32x2 u = *(const u32x2*)(q8 + (row * kH + j) * kD + d0);
+            float x[8];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)u[h], false);
+                const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)u[h], true);
+                x[4 * h] = lo[0]; x[4 * h + 1] = lo[1]; x[4 * h + 2] = hi[0]; x[4 * h + 3] = hi[1];
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) part[j & 3][e] = fmaf(v, x[e], part[j & 3][e]);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+            float hv[2], mv[2], lv[2];
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const float c = (part[0][e + k] + part[1][e + k]) + (part[2][e + k] + part[3][e + k]);
+                hv[k] = round_bf16(c);
+                const float r1 = c - hv[k];
+                mv[k] = round_bf16(r1);
+                lv[k] = r1 - mv[k];
+            }
+            cpart[0][r][(d0 + e) / 2] = pack_bf16x2(hv[0], hv[1]);
+            cpart[1][r][(d0 + e) / 2] = pack_bf16x2(mv[0], mv[1]);
+            cpart[2][r][(d0 + e) / 2] = pack_bf16x2(lv[0], lv[1]);
+        }
     }
 
     const int nkeys = tpos_last + 1;
     const int ngroups = (nkeys + kKG - 1) / kKG;
-    const int ld_key = tid >> 2, ld_part = tid & 3;     // 64 keys x 4 parts of 32 B
     const v4f zero = {0.f, 0.f, 0.f, 0.f};
 
+    // Keys of group g go global -> LDS by direct copies: chunk p (16 B) of the
+    // swizzled tile is row p / 8, physical chunk p % 8, so each lane fetches the
+    // logical chunk that belongs there.  Rows past Lk repeat key Lk - 1; their
+    // outputs are never stored.
+    const uint32_t ktile_lds = lds_byte_address(&ktile[0][0]);
+    auto issue_keys = [&](int g, int slot) {
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+            const int p = n * kThreads + tid;
+            const int r = p >> 3, c = (p & 7) ^ ((r >> 1) & 7);
+            const int s = min(g * kKG + r, Lk - 1);
+            const uint8_t* src = k8 + ((int64_t)b * Lk + s) * kD + c * 16;
+            const uint32_t dst = ktile_lds + slot * (kKG * kD) + (n * kThreads + wave * kWave) * 16;
+            global_to_lds16_async(src, __builtin_amdgcn_readfirstlane(dst));
+        }
+    };
+    issue_keys(0, 0);
+    wait_vmcnt0();
+    __syncthreads();
+
+    // Linear part, operand B: query col, dims 32*grp + 8*wave + (0..7).
+    v8bf cb[3];
+#pragma unroll
+    for (int p = 0; p < 3; ++p)
+        cb[p] = as_bf8(*(const u32x4*)&cpart[p][col][(32 * grp + 8 * wave) / 2]);
+    const int lin_chunk = 2 * grp + (wave >> 1), lin_byte = 8 * (wave & 1);
+
+    // Per group: the copy of group g+1 into the other tile slot runs while g
+    // is computed; one wait + barrier publishes both the next key tile and
+    // this group's partial sums (the reduction buffer is double-buffered too).
     for (int g = 0; g < ngroups; ++g) {
         const int s0 = g * kKG;
-        // stage keys [s0, s0 + 64) in LDS
-        {
-            const int s = s0 + ld_key;
-            u32x4 lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
-            if (s < Lk) {
-                const u32x4* p = (const u32x4*)(k8 + ((int64_t)b * Lk + s) * kD + ld_part * 32);
-                lo = p[0];
-                hi = p[1];
-            }
-            __syncthreads();                            // previous group fully consumed
-            u32x4* d = (u32x4*)(ktile + ld_key * kD + ld_part * 32);
-            d[0] = lo;
-            d[1] = hi;
-            __syncthreads();
-        }
-        // key operand (A) fragments of the 4 tiles
-        v8i af[4];
+        const int kb = g & 1;
+        const uint8_t* kt = ktile[kb];
+        if (g + 1 < ngroups) issue_keys(g + 1, kb ^ 1);
+        // key scales of the four keys this thread finishes after the barrier,
+        // fetched now so the epilogue does not wait on memory
+        const int sb = s0 + wave * 16 + grp * 4;
+        float ksc[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ksc[r] = k_scale[(int64_t)b * Lk + min(sb + r, Lk - 1)];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const u32x4* p = (const u32x4*)(ktile + (i * 16 + col) * kD + grp * 32);
-            af[i] = as_i8(p[0], p[1]);
-        }
-        v4f acc[4] = {zero, zero, zero, zero};
+            const int kr = i * 16 + col;
+            // linear part: this wave's 32 dims of c[col] . k[kr]
+            const u32x2 kk = *(const u32x2*)(kt + ktile_off(kr, lin_chunk) + lin_byte);
+            u32x4 kbf;
+            kbf[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kk[0], 1.0f, false));
+            kbf[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kk[0], 1.0f, true));
+            kbf[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kk[1], 1.0f, false));
+            kbf[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kk[1], 1.0f, true));
+            const v8bf ka = as_bf8(kbf);
+            v4f acc = mfma_bf16_16x16x32(ka, cb[2], zero);
+            acc = mfma_bf16_16x16x32(ka, cb[1], acc);
+            acc = mfma_bf16_16x16x32(ka, cb[0], acc);
+            // absolute part over the wave's 16 heads
+            const v8i af = as_i8(*(const u32x4*)(kt + ktile_off(kr, 2 * grp)),
+                                 *(const u32x4*)(kt + ktile_off(kr, 2 * grp + 1)));
+            // software-pipelined: the MFMA of head h + 1 is in flight while
+            // the result of head h is folded in
+            v4f d = mfma_fp8_16x16x128(af, qf[0], zero);
 #pragma unroll
-        for (int h = 0; h < kHPW; ++h) {
+            for (int h = 0; h < kHPW; ++h) {
+                const v4f dn = (h + 1 < kHPW) ? mfma_fp8_16x16x128(af, qf[(h + 1) % kHPW], zero) : d;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const v4f d = mfma_fp8_16x16x128(af[i], qf[h], zero);
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    acc[i][r] = fmaf(wq[h], fmaxf(d[r], 0.f), acc[i][r]);
+                for (int r = 0; r < 4; ++r) acc[r] = fmaf(wv[h], fabsf(d[r]), acc[r]);
+                d = dn;
             }
+            red[kb][wave][i][lane] = acc;
         }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) red[wave][i][lane] = acc[i];
+        wait_vmcnt0();
         __syncthreads();
-        // thread (wave = tile i, lane): sum the four waves' head partials
-        v4f sum = red[0][wave][lane];
+        // thread (wave = tile i, lane): sum the four waves' partials
+        v4f sum = red[kb][0][wave][lane];
 #pragma unroll
         for (int ww = 1; ww < 4; ++ww) {
-            const v4f x = red[ww][wave][lane];
+            const v4f x = red[kb][ww][wave][lane];
             sum[0] += x[0]; sum[1] += x[1]; sum[2] += x[2]; sum[3] += x[3];
         }
         if (col < rows_here) {
             const int t = t0 + col;
             const int tpos = q_pos0 + t;
-            const int sb = s0 + wave * 16 + grp * 4;
             float* dst = scores + (int64_t)b * sc_bstride + (int64_t)(t - t_begin) * sc_rstride + sb;
             float v[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int s = sb + r;
-                v[r] = (s <= tpos) ? sum[r] * k_scale[(int64_t)b * Lk + min(s, Lk - 1)] : -INFINITY;
+                v[r] = (s <= tpos) ? sum[r] * ksc[r] : -INFINITY;
             }
             const bool vec_ok = ((uintptr_t)dst & 15u) == 0;
             if (vec_ok && sb + 3 < Lk && (write_masked || sb + 3 <= tpos)) {
