@@ -12,6 +12,10 @@ Tolerances:
                           (a term 14+ bits below the block's largest product is
                           dropped), so it is not fp32-exact; on N(0,1) data the
                           measured error is <= 1.2e-6 M, and 2^-18 = 3.8e-6.
+                          A kernel that evaluates ReLU(x) = (x + |x|)/2 as a
+                          linear part plus an absolute part stays inside the
+                          same bound: each half has weight 1/2 and the linear
+                          part's own mass sum_d |c_d k_d| is at most M/2.
   top-k      bit-exact where the oracle's gap (v_k - v_{k+1}) / |v_k| > 1e-3
              and the gap exceeds twice the absolute score tolerance; every row
              must be a valid top-k of the oracle's scores within the score
