@@ -145,15 +145,22 @@ __device__ __forceinline__ float wave_sum(float v)
     return v;
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave.
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane)
+// Inclusive prefix sum over the 64 lanes of a wave, with DPP lane moves: row
+// shifts by 1, 2, 4 and 8 give prefixes within each 16-lane row, then the two
+// row broadcasts (lane 15 into row 1 and 3, lane 31 into rows 2 and 3) carry
+// the row totals forward.  Lanes whose source is outside the pattern add 0.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int /*lane*/)
 {
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        uint32_t u = __shfl_up(v, o, kWave);
-        if (lane >= o) v += u;
-    }
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false);   // row_shr:1
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false);   // row_shr:2
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false);   // row_shr:4
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false);   // row_shr:8
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);   // row_bcast:15
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);   // row_bcast:31
     return v;
 }
+
+// Value of lane 63 (e.g. the total of an inclusive scan), wave-uniform.
+__device__ __forceinline__ uint32_t wave_last(uint32_t v) { return __builtin_amdgcn_readlane(v, 63); }
 
 }  // namespace dsa
