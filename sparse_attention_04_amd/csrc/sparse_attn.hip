@@ -342,6 +342,8 @@ void sparse_attn_bf16_w32_kernel(const uint16_t* __restrict__ q, const uint16_t*
                     if (c2 + kPre < S::QC) kf[(c2 + kPre) % (kPre + 1)] = kfrag(c2 + kPre);
                     const v8bf bq = (c2 < S::QR) ? qf[c2 < S::QR ? c2 : 0] : as_bf8(qw[(c2 - S::QR) * 64]);
                     sacc = mfma_bf16_32x32x16(as_bf8(kf[c2 % (kPre + 1)]), bq, sacc);
+                    // keep the reads kPre steps ahead: no instruction crosses this point
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
             // queue the next chunk (while the last QK MFMAs drain)
@@ -354,10 +356,12 @@ void sparse_attn_bf16_w32_kernel(const uint16_t* __restrict__ q, const uint16_t*
             // the overflow check) is taken afterwards, off the critical path.
             if (vmask == 0u) continue;                       // nothing selected here (uniform)
             if (vmask != 0xFFFFFFFFu) {
+                // element v holds chunk row slot_row(8 (v/4) + 4 hi + v%4) = hi + rv(v)
+                const uint32_t vmh = vmask >> hi;
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
-                    const int r = slot_row(8 * (v >> 2) + 4 * hi + (v & 3));
-                    sacc[v] = ((vmask >> r) & 1u) ? sacc[v] : -INFINITY;
+                    const int rv = slot_row(8 * (v >> 2) + (v & 3));
+                    sacc[v] = ((vmh >> rv) & 1u) ? sacc[v] : -INFINITY;
                 }
             }
             if (__any(m == -INFINITY)) {                     // first chunk holding a valid row
