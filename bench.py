@@ -24,6 +24,13 @@ PEAK_FP8 = 5.0e15        # dense FP8 MFMA, MI355X
 PEAK_BF16 = 2.5e15       # dense BF16 MFMA, MI355X
 PEAK_HBM = 8.0e12        # HBM3E bytes/s
 
+# HBM traffic of one attention launch at the bench workload, from rocprofv3
+# FETCH_SIZE / WRITE_SIZE runs scaled by a 1 GiB plain copy measured in the same
+# runs (fetch factor 2.0, write factor 1.0).  Valid only for the attention
+# source it was measured on; any other source reports null.
+ATTN_TRAFFIC = {"source_sha256_16": "39d58af19fed1c15", "fetch_bytes": 37357777640.0,
+                "write_bytes": 7110473536.0}
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -41,6 +48,16 @@ def algorithmic(cfg):
         "topk_bytes": 4.0 * n_topk_read + 4.0 * cfg.B * cfg.Lq * cfg.k,
         "attn_gather_bytes": 2.0 * cfg.d_qk * n_sel,
     }
+
+
+def attn_traffic_bytes():
+    import hashlib
+    src = os.path.join(ROOT, "sparse_attention_04_amd", "csrc", "sparse_attn.hip")
+    with open(src, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()[:16]
+    if sha != ATTN_TRAFFIC["source_sha256_16"]:
+        return None
+    return ATTN_TRAFFIC["fetch_bytes"] + ATTN_TRAFFIC["write_bytes"]
 
 
 def time_loop(fn, steps, stream):
@@ -176,7 +193,7 @@ def main():
         att = work["attn_flop"] / t_att
         res["roofline"] = {"bound": "mfma", "kernel": "sparse_attn_bf16", "achieved": att / 1e12,
                            "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s", "frac": att / PEAK_BF16,
-                           "traffic": None}
+                           "traffic": attn_traffic_bytes() if cfg.name == "mla_prefill_L32768" else None}
         res["indexer_frac_fp8_peak"] = work["indexer_flop"] / t_idx / PEAK_FP8
         res["stages_ms"] = stages
         res["stage_roofline"] = {
