@@ -181,8 +181,8 @@ void sparse_attn_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __r
 //    LDS banks exactly once, and every fragment address is one per-lane base
 //    plus an immediate.  Tails are packed 8 rows per 1 KB with piece c of
 //    row r at position c ^ (r % 8).
-//  - S^T[32 rows x 32 heads] = K_chunk . Q^T, the query operand held in
-//    registers except its last QL steps (kept in LDS to stay spill-free).
+//  - S^T[32 rows x 32 heads] = K_chunk . Q^T, the query operand (36 steps of
+//    32 heads x 16 dims) held in registers for the whole row.
 //  - Softmax in fp32 (exp2 domain) against a per-head reference maximum m
 //    fixed at the first chunk holding a valid row, so O is never rescaled
 //    (no VALU work on the 256 accumulator registers).  Probabilities
@@ -208,9 +208,7 @@ struct W32Shape {
     static constexpr int RPW = NC / NW;                   // value rows copied per wave
     static constexpr int TI = TBYTES / 1024;              // tail copy instructions per chunk
     static constexpr int SPW = RPW + TI / NW;             // copy instructions per wave per chunk
-    static constexpr int QC = DQK / 16;                   // MFMA K steps for Q.K
-    static constexpr int QL = DQK > 256 ? 19 : 0;         // query steps kept in LDS
-    static constexpr int QR = QC - QL;
+    static constexpr int QC = DQK / 16;                   // MFMA K steps for Q.K (all held in registers)
     static constexpr int DT = DV / 32;                    // 32-wide value tiles
     static constexpr int KMAX = 2048;                     // largest k whose index list is staged in LDS
     static_assert(VP == 64, "one copy instruction per value part");
@@ -234,7 +232,7 @@ void sparse_attn_bf16_w32_kernel(const uint16_t* __restrict__ q, const uint16_t*
     constexpr int NC = S::NC;
     __shared__ __attribute__((aligned(16))) uint8_t ring[S::NBUF][S::BUF_BYTES];
     __shared__ __attribute__((aligned(16))) int32_t sel[S::KMAX];   // the query's index list (-1 padded)
-    __shared__ __attribute__((aligned(16))) u32x4 qlds[S::QL > 0 ? NW * S::QL * 64 : 1];   // [wave][step][lane]
+    __shared__ int wlast[NW];                                       // per wave: last valid list position
 
     const int row = blockIdx.x, b = blockIdx.y;
     const int t = t_begin + row;
@@ -244,12 +242,9 @@ void sparse_attn_bf16_w32_kernel(const uint16_t* __restrict__ q, const uint16_t*
     const int h = wave * 32 + col;
 
     const uint16_t* qrow = q + (((int64_t)b * Lq + t) * H + h) * DQK;
-    v8bf qf[S::QR];
+    v8bf qf[S::QC];
 #pragma unroll
-    for (int c = 0; c < S::QR; ++c) qf[c] = as_bf8(*(const u32x4*)(qrow + c * 16 + hi * 8));
-    u32x4* qw = qlds + wave * S::QL * 64 + lane;
-#pragma unroll
-    for (int c = 0; c < S::QL; ++c) qw[c * 64] = *(const u32x4*)(qrow + (S::QR + c) * 16 + hi * 8);
+    for (int c = 0; c < S::QC; ++c) qf[c] = as_bf8(*(const u32x4*)(qrow + c * 16 + hi * 8));
 
     v16f o[S::DT];
 #pragma unroll
@@ -260,14 +255,22 @@ void sparse_attn_bf16_w32_kernel(const uint16_t* __restrict__ q, const uint16_t*
 
     const int32_t* irow = idx + (int64_t)b * idx_bstride + (int64_t)row * k;
     const uint16_t* kvb = kv + (int64_t)b * Lk * DQK;
-    const int nchunks = (k + NC - 1) / NC;
-
-    // stage the index list; entries that cannot be read become -1
+    // Stage the index list; entries that cannot be read become -1.  Chunks
+    // past the last valid entry (a short row's -1 padding) are not visited.
+    int last = -1;
     for (int i = tid; i < S::KMAX; i += 64 * NW) {
         const int sidx = (i < k) ? irow[i] : -1;
-        sel[i] = (sidx >= 0 && sidx < Lk) ? sidx : -1;
+        const bool ok = sidx >= 0 && sidx < Lk;
+        sel[i] = ok ? sidx : -1;
+        last = ok ? i : last;
     }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) last = max(last, __shfl_xor(last, o, kWave));
+    if (lane == 0) wlast[wave] = last;
     __syncthreads();
+#pragma unroll
+    for (int w = 0; w < NW; ++w) last = max(last, wlast[w]);
+    const int nchunks = (last + NC) / NC;                   // last = -1: nothing to attend
     // bit r set when entry r of chunk c is a real row
     auto valid_mask = [&](int c) -> uint32_t {
         return (uint32_t)__ballot(lane < NC && sel[c * NC + (lane & 31)] >= 0);
@@ -340,8 +343,7 @@ void sparse_attn_bf16_w32_kernel(const uint16_t* __restrict__ q, const uint16_t*
 #pragma unroll
                 for (int c2 = 0; c2 < S::QC; ++c2) {
                     if (c2 + kPre < S::QC) kf[(c2 + kPre) % (kPre + 1)] = kfrag(c2 + kPre);
-                    const v8bf bq = (c2 < S::QR) ? qf[c2 < S::QR ? c2 : 0] : as_bf8(qw[(c2 - S::QR) * 64]);
-                    sacc = mfma_bf16_32x32x16(as_bf8(kf[c2 % (kPre + 1)]), bq, sacc);
+                    sacc = mfma_bf16_32x32x16(as_bf8(kf[c2 % (kPre + 1)]), qf[c2], sacc);
                     // keep the reads kPre steps ahead: no instruction crosses this point
                     __builtin_amdgcn_sched_barrier(0);
                 }
