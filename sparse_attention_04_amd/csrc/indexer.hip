@@ -247,6 +247,119 @@ void indexer_fp8_kernel(const uint8_t* __restrict__ q8, const float* __restrict_
     }
 }
 
+// FP8 kernel for few query rows per sequence (decode): one workgroup per
+// (query row, range of kRowKeys keys).  The MFMA's N dimension carries 16
+// heads instead of 16 queries, so no work is spent on absent query rows:
+// per 16-key tile a wave runs four v_mfma_f32_16x16x128_f8f6f4 (64 heads),
+// folds ReLU and the head weights into four fp32 partial sums per lane, and
+// sums them over the 16 lanes that hold the 16 heads of a key.  Keys are read
+// straight from memory into the A operand, kTileAhead tiles ahead; the four
+// waves take alternate tiles and need no workgroup synchronisation.
+constexpr int kRowKeys = 2048;     // keys per workgroup
+constexpr int kTileAhead = 8;      // key tiles in flight per wave
+
+// Sum over each 16-lane row of the wave (every lane of the row gets it): DPP
+// row rotations by 8, 4, 2 and 1.
+__device__ __forceinline__ float row16_sum(float x)
+{
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xF, 0xF, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x122, 0xF, 0xF, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x121, 0xF, 0xF, false));
+    return x;
+}
+
+__global__ __launch_bounds__(kThreads)
+void indexer_fp8_row_kernel(const uint8_t* __restrict__ q8, const float* __restrict__ q_scale,
+                            const uint8_t* __restrict__ k8, const float* __restrict__ k_scale,
+                            const float* __restrict__ w, float* __restrict__ scores,
+                            int Lq, int Lk, int q_pos0, int t_begin,
+                            int64_t sc_bstride, int64_t sc_rstride, int write_masked, int skip_upto_k)
+{
+    const int t = t_begin + blockIdx.x;
+    const int b = blockIdx.y;
+    const int tpos = q_pos0 + t;
+    if (skip_upto_k > 0 && tpos + 1 <= skip_upto_k)
+        return;
+    const int s_begin = blockIdx.z * kRowKeys;
+    const int s_stop = min(s_begin + kRowKeys, Lk);           // this workgroup's key range
+    const int s_end = min(s_stop, tpos + 1);                  // keys that get a score
+    float* dst = scores + (int64_t)b * sc_bstride + (int64_t)(t - t_begin) * sc_rstride;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    if (write_masked)
+        for (int s = max(s_end, s_begin) + tid; s < s_stop; s += kThreads) dst[s] = -INFINITY;
+    if (s_end <= s_begin)
+        return;
+
+    // B operand: head 16 h + (lane % 16), bytes [32 (lane / 16), +32) of the query row
+    const int hcol = lane & 15, grp = lane >> 4;
+    const int64_t qrow = (int64_t)b * Lq + t;
+    v8i qf[4];
+    float wq[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+        const int j = 16 * h + hcol;
+        const u32x4* p = (const u32x4*)(q8 + (qrow * kH + j) * kD + grp * 32);
+        qf[h] = as_i8(p[0], p[1]);
+        wq[h] = w[qrow * kH + j] * q_scale[qrow * kH + j];
+    }
+    const v4f zero = {0.f, 0.f, 0.f, 0.f};
+    const int ntiles = (s_end - s_begin + 15) >> 4;
+    // Tile i: A operand = key s_begin + 16 i + (lane % 16), 32-byte slice
+    // lane / 16; and the key scales of keys s_begin + 16 i + 4 (lane / 16) + r,
+    // which this lane's row of sums will hold.  Both are fetched together so
+    // no load is waited on inside the MFMA step.
+    struct Tile {
+        v8i a;
+        float ks[4];
+    };
+    auto load_tile = [&](int i) -> Tile {
+        Tile tl;
+        const int key = min(s_begin + 16 * i + hcol, Lk - 1);
+        const u32x4* p = (const u32x4*)(k8 + ((int64_t)b * Lk + key) * kD + grp * 32);
+        tl.a = as_i8(p[0], p[1]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            tl.ks[r] = k_scale[(int64_t)b * Lk + min(s_begin + 16 * i + 4 * grp + r, Lk - 1)];
+        return tl;
+    };
+    Tile tf[kTileAhead];
+#pragma unroll
+    for (int a = 0; a < kTileAhead; ++a) {
+        const int i = wave + 4 * a;
+        if (i < ntiles) tf[a] = load_tile(i);
+    }
+    for (int i0 = wave; i0 < ntiles; i0 += 4 * kTileAhead) {
+#pragma unroll
+        for (int a = 0; a < kTileAhead; ++a) {
+            const int i = i0 + 4 * a;
+            if (i >= ntiles) break;                               // wave-uniform
+            const Tile cur = tf[a];
+            if (i + 4 * kTileAhead < ntiles) tf[a] = load_tile(i + 4 * kTileAhead);
+            v4f acc = zero;
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                const v4f d = mfma_fp8_16x16x128(cur.a, qf[h], zero);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    acc[r] = fmaf(wq[h], __int_as_float(max(__float_as_int(d[r]), 0)), acc[r]);
+            }
+            // sum over the 16 lanes (heads) that share keys 4 (lane / 16) + r
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[r] = row16_sum(acc[r]);
+            if (hcol == 0) {
+                const int sb = s_begin + 16 * i + 4 * grp;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int s = sb + r;
+                    if (s < s_end) dst[s] = acc[r] * cur.ks[r];
+                }
+            }
+        }
+    }
+}
+
 // fp32 indexer for small problems: one workgroup per query row, one thread per
 // key.  The query row lives in LDS; dot products are plain fp32 FMAs.
 constexpr int kF32Threads = 256;
@@ -289,7 +402,15 @@ void indexer_f32_kernel(const float* __restrict__ q, const float* __restrict__ k
 hipError_t launch_indexer(const IndexerLaunch& a, hipStream_t s)
 {
     if (a.B == 0 || a.t_count == 0) return hipSuccess;
-    if (a.fp8) {
+    if (a.fp8 && a.t_count < kQB / 2) {
+        // few query rows per sequence: split the keys instead of blocking queries
+        const int last = a.write_masked ? a.Lk : min(a.Lk, a.q_pos0 + a.t_begin + a.t_count);
+        const int nz = (last + kRowKeys - 1) / kRowKeys;
+        hipLaunchKernelGGL(indexer_fp8_row_kernel, dim3(a.t_count, a.B, nz), dim3(kThreads), 0, s,
+                           (const uint8_t*)a.q, a.q_scale, (const uint8_t*)a.k, a.k_scale, a.w,
+                           a.scores, a.Lq, a.Lk, a.q_pos0, a.t_begin,
+                           a.sc_bstride, a.sc_rstride, (int)a.write_masked, a.skip_upto_k);
+    } else if (a.fp8) {
         const int nqb = (a.t_count + kQB - 1) / kQB;
         hipLaunchKernelGGL(indexer_fp8_kernel, dim3(nqb, a.B), dim3(kThreads), 0, s,
                            (const uint8_t*)a.q, a.q_scale, (const uint8_t*)a.k, a.k_scale, a.w,

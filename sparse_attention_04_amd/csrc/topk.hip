@@ -177,15 +177,33 @@ void topk_radix_kernel(const float* __restrict__ scores, int32_t* __restrict__ i
         }
     };
 
-    // 1. Lower bound: the first digit of the sample's j-th largest key, j set so
-    //    that about 2k row keys are expected at or above it.
+    // 1. Lower bound from evenly spaced sample keys: about 2k row keys are
+    //    expected at or above the sample's j-th largest key.  A row held in
+    //    registers takes that key's first digit (11 bits) from 1024 samples;
+    //    a longer row, where one first-digit bin holds too many keys for the
+    //    list, takes its first two digits (22 bits) from 2048 samples.
     uint32_t lbound = 0;
     const int64_t target = 2 * (int64_t)k;
     if (target < n) {
-        const uint32_t j = (uint32_t)((target * kT + n - 1) / n);      // 1 <= j <= kT
-        const uint32_t sample = score_key(src[(int)(((int64_t)tid * n) / kT)]);   // kT evenly spaced positions
-        radix_step<11>(sh, 21, 0u, 0u, j, [&](auto&& fn) { fn(sample); });
-        lbound = sh.bin << 21;
+        const int ns = in_regs ? kT : 2 * kT;
+        const uint32_t j = (uint32_t)((target * ns + n - 1) / n);      // 1 <= j <= ns
+        uint32_t sample[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+            sample[e] = (e == 0 || !in_regs) ? score_key(src[(int)(((int64_t)(tid + e * kT) * n) / ns)]) : 0u;
+        auto each_sample = [&](auto&& fn) {
+            fn(sample[0]);
+            if (!in_regs) fn(sample[1]);
+        };
+        radix_step<11>(sh, 21, 0u, 0u, j, each_sample);
+        const uint32_t b1 = sh.bin;
+        lbound = b1 << 21;
+        if (!in_regs) {
+            const uint32_t above = sh.above;
+            __syncthreads();                       // sh.bin / sh.above are rewritten below
+            radix_step<11>(sh, 10, b1 << 21, 0x7FFu << 21, j - above, each_sample);
+            lbound |= sh.bin << 10;
+        }
     } else {
         __syncthreads();                           // publishes sh.ncand = 0
     }
