@@ -147,6 +147,13 @@ def test_mla_prefill_L32768(dsa):
     _run_case(dsa, cfg, {0: _sample_rows(cfg.Lq, cfg.k, n_random=16)})
 
 
+def test_prefill_L131072_query_tiles(dsa):
+    """L = 131072 with the forward in query-row tiles of 4096 (the score
+    workspace never holds L x L); the stage calls run on the whole problem."""
+    cfg = CONFIGS["prefill_L131072"]
+    _run_case(dsa, cfg, {0: _sample_rows(cfg.Lq, cfg.k, n_random=6)}, q_tile_rows=cfg.q_tile_rows)
+
+
 def test_decode_B64_ctx65536(dsa):
     cfg = CONFIGS["decode_B64_ctx65536"]
     _run_case(dsa, cfg, {b: np.array([0]) for b in (0, 1, 17, 63)})
