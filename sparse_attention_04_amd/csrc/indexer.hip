@@ -239,10 +239,18 @@ void indexer_fp8_kernel(const uint8_t* __restrict__ q8, const float* __restrict_
 
     if (write_masked) {
         // -inf beyond the last computed group for every row of the block
+        // (16-byte stores where the row allows, the ragged end one by one)
         const int s_from = ngroups * kKG;
+        const v4f ninf = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
         for (int r = 0; r < rows_here; ++r) {
             float* dst = scores + (int64_t)b * sc_bstride + (int64_t)(t0 + r - t_begin) * sc_rstride;
-            for (int s = s_from + tid; s < Lk; s += kThreads) dst[s] = -INFINITY;
+            int s_vec = s_from, s_end = Lk;
+            if (s_from < Lk && (((uintptr_t)(dst + s_from)) & 15u) == 0) {
+                const int nvec = (Lk - s_from) >> 2;
+                for (int i = tid; i < nvec; i += kThreads) *(v4f*)(dst + s_from + 4 * i) = ninf;
+                s_vec = s_from + 4 * nvec;
+            }
+            for (int s = s_vec + tid; s < s_end; s += kThreads) dst[s] = -INFINITY;
         }
     }
 }
