@@ -48,15 +48,16 @@ struct TopkShared {
     uint32_t cand[kCand];
     int32_t sel[kSelCap];
     uint32_t bin, above, ncand;
+    uint32_t cmax, nsmall, tkey, tgt;
 };
 
-// Histogram of the digit at `shift` over the keys matching (prefix, pmask);
-// leaves in sh.bin the digit holding the need-th largest matching key and in
-// sh.above the number of matching keys in larger digits.  Requires at least
-// `need` matching keys.  Every thread calls it; it ends with a barrier.
-template <int kWidth, typename ForEachKey>
-__device__ __forceinline__ void radix_step(TopkShared& sh, int shift, uint32_t prefix, uint32_t pmask,
-                                           uint32_t need, ForEachKey for_each_key)
+// Histogram over nb = 2^kWidth bins of the bins `for_each_bin` yields
+// (fn(bin), bin < nb; larger bins ordered higher); leaves in sh.bin the bin
+// holding the need-th largest entry and in sh.above the number of entries in
+// higher bins.  Requires at least `need` entries.  Every thread calls it; it
+// ends with a barrier.
+template <int kWidth, typename ForEachBin>
+__device__ __forceinline__ void bin_step(TopkShared& sh, uint32_t need, ForEachBin for_each_bin)
 {
     constexpr uint32_t nb = 1u << kWidth;
     constexpr uint32_t per = nb / kWave;           // bins per lane in the scan
@@ -64,9 +65,7 @@ __device__ __forceinline__ void radix_step(TopkShared& sh, int shift, uint32_t p
     for (uint32_t i = tid; i < nb * kCopies; i += kT) sh.hist[i] = 0;
     __syncthreads();
     const uint32_t copy = (uint32_t)lane & (kCopies - 1);
-    for_each_key([&](uint32_t key) {
-        if ((key & pmask) == prefix) atomicAdd(&sh.hist[((key >> shift) & (nb - 1)) * kCopies + copy], 1u);
-    });
+    for_each_bin([&](uint32_t bin) { atomicAdd(&sh.hist[bin * kCopies + copy], 1u); });
     __syncthreads();
     for (uint32_t i = tid; i < nb; i += kT) {
         const u32x4 c = *(const u32x4*)&sh.hist[i * kCopies];
@@ -97,6 +96,19 @@ __device__ __forceinline__ void radix_step(TopkShared& sh, int shift, uint32_t p
         }
     }
     __syncthreads();
+}
+
+// bin_step over the digit at `shift` of the keys matching (prefix, pmask).
+template <int kWidth, typename ForEachKey>
+__device__ __forceinline__ void radix_step(TopkShared& sh, int shift, uint32_t prefix, uint32_t pmask,
+                                           uint32_t need, ForEachKey for_each_key)
+{
+    constexpr uint32_t mask = (1u << kWidth) - 1;
+    bin_step<kWidth>(sh, need, [&](auto&& fn) {
+        for_each_key([&](uint32_t key) {
+            if ((key & pmask) == prefix) fn((key >> shift) & mask);
+        });
+    });
 }
 
 // Three radix steps (11, 11, 10 bits) over the keys `each` enumerates; returns
@@ -141,7 +153,11 @@ void topk_radix_kernel(const float* __restrict__ scores, int32_t* __restrict__ i
     const float* src = scores + (int64_t)b * sc_bstride + (int64_t)row * sc_rstride;
     const bool in_regs = n <= kRegRow;
     const bool vec = ((uintptr_t)src & 15u) == 0;
-    if (tid == 0) sh.ncand = 0;                    // published by the first barrier below
+    if (tid == 0) {                                // published by the first barrier below
+        sh.ncand = 0;
+        sh.cmax = 0;
+        sh.nsmall = 0;
+    }
 
     // keys of positions s0..s0+3 (0 past the row)
     auto load4 = [&](int s0, uint32_t (&kk)[4]) {
@@ -210,6 +226,7 @@ void topk_radix_kernel(const float* __restrict__ scores, int32_t* __restrict__ i
 
     // 2. Copy the keys >= lbound to the LDS list: per step one wave scan and one
     //    atomic per wave.
+    uint32_t cmax = 0;                             // largest key in the list (this thread's part)
     for_each_step([&](int s0, const uint32_t (&kk)[4]) {
         uint32_t c = 0;
 #pragma unroll
@@ -223,9 +240,13 @@ void topk_radix_kernel(const float* __restrict__ scores, int32_t* __restrict__ i
             if ((s0 + e < n) && kk[e] >= lbound) {
                 if (base < (uint32_t)kCand) sh.cand[base] = kk[e];
                 ++base;
+                cmax = max(cmax, kk[e]);
             }
         }
     });
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) cmax = max(cmax, (uint32_t)__shfl_xor((int)cmax, o, kWave));
+    if (lane == 0) atomicMax(&sh.cmax, cmax);
     __syncthreads();
     const uint32_t nc = sh.ncand;
 
@@ -233,10 +254,60 @@ void topk_radix_kernel(const float* __restrict__ scores, int32_t* __restrict__ i
     //    k keys >= lbound) and fits; otherwise from the whole row.
     uint32_t need = (uint32_t)k;
     uint32_t T;
+    bool done = false;
     if (nc >= (uint32_t)k && nc <= (uint32_t)kCand) {
-        T = radix_select(sh, need, [&](auto&& fn) {
-            for (uint32_t i = tid; i < nc; i += kT) fn(sh.cand[i]);
+        // One histogram of (key - lbound) >> sft, sft chosen so the list's
+        // range [lbound, cmax] spans at most 2048 bins; the threshold bin then
+        // holds few keys, ranked by brute force.
+        const uint32_t lb = lbound, range = sh.cmax - lb;
+        const int sft = max(0, (range ? 32 - __clz(range) : 0) - 11);
+        bin_step<11>(sh, need, [&](auto&& fn) {
+            for (uint32_t i = tid; i < nc; i += kT) fn((sh.cand[i] - lb) >> sft);
         });
+        const uint32_t bstar = sh.bin, above = sh.above;
+        if (sft == 0) {
+            T = lb + bstar;                        // one key value per bin
+            need -= above;
+            done = true;
+        } else {
+            // the threshold bin's keys, in the (now free) histogram storage
+            uint32_t* small = sh.hist;
+            for (uint32_t i = tid; i < nc; i += kT) {
+                const uint32_t key = sh.cand[i];
+                if (((key - lb) >> sft) == bstar) {
+                    const uint32_t pos = atomicAdd(&sh.nsmall, 1u);
+                    if (pos < (uint32_t)kT) small[pos] = key;
+                }
+            }
+            __syncthreads();
+            const uint32_t cs = sh.nsmall;
+            if (cs <= (uint32_t)kT) {
+                const uint32_t nb_ = need - above;   // rank wanted inside the bin (1-based)
+                if ((uint32_t)tid < cs) {
+                    const uint32_t x = small[tid];
+                    uint32_t gt = 0, eq = 0;
+                    for (uint32_t j = 0; j < cs; ++j) {
+                        const uint32_t y = small[j];
+                        gt += y > x;
+                        eq += y == x;
+                    }
+                    if (gt < nb_ && nb_ <= gt + eq) {   // every copy of the key writes the same
+                        sh.tkey = x;
+                        sh.tgt = gt;
+                    }
+                }
+                __syncthreads();
+                T = sh.tkey;
+                need = nb_ - sh.tgt;
+                done = true;
+            }
+        }
+        if (!done) {
+            T = radix_select(sh, need, [&](auto&& fn) {
+                for (uint32_t i = tid; i < nc; i += kT) fn(sh.cand[i]);
+            });
+            done = true;
+        }
     } else {
         T = radix_select(sh, need, [&](auto&& fn) {
             for (int s0 = tid * 4; s0 < n; s0 += kTile) {
