@@ -135,6 +135,19 @@ def test_head_dim_64(dsa):
     _run_case(dsa, cfg, {0: np.arange(cfg.Lq)})
 
 
+@pytest.mark.parametrize("Lq", [1, 3, 7])
+@pytest.mark.parametrize("where", ["decode", "chunk_edge", "short_rows"])
+def test_few_query_rows_split_keys(dsa, Lq, where):
+    """Fewer than 8 query rows per sequence: the FP8 indexer splits each row's
+    keys over workgroups of 2048.  Lk = 5003 leaves a ragged last chunk (not a
+    multiple of 16); rows that end before Lk - 1 leave whole chunks masked."""
+    Lk = 5003
+    q_pos0 = {"decode": Lk - Lq, "chunk_edge": 4094, "short_rows": 2045}[where]
+    cfg = CONFIGS["decode_B64_ctx65536"].with_(name=f"rows{Lq}_{where}", B=2, Lq=Lq, Lk=Lk, q_pos0=q_pos0,
+                                               n_heads=16)
+    _run_case(dsa, cfg, {b: np.arange(cfg.Lq) for b in range(cfg.B)}, seed=Lq)
+
+
 # ------------------------------------------------------------------ full-size workloads, sampled rows
 
 def test_prefill_L4096(dsa):
@@ -238,6 +251,63 @@ def test_topk_long_rows(dsa):
     s = torch.randn(2, 2, Lk, device=dev, generator=g)
     s[1] = torch.randint(-50, 50, (2, Lk), device=dev, generator=g).float()   # many ties
     _topk_exact(dsa, s.contiguous(), 2048, q_pos0=Lk - 2)
+
+
+def _topk_pattern_row(pattern: str, n: int, g: torch.Generator) -> torch.Tensor:
+    """One row of n scores shaped to steer the selection down one route."""
+    if pattern == "normal":
+        return torch.randn(n, generator=g)
+    if pattern == "ties":
+        return torch.randint(-50, 50, (n,), generator=g).float()
+    if pattern == "const":                         # every key equal: the candidate list overflows
+        return torch.full((n,), 0.25)
+    if pattern == "cluster_outlier":
+        # 5000 keys within 1e-3 of 1.0 and one huge key: the list's histogram
+        # puts the whole cluster in one bin, which is then ranked by radix passes
+        r = torch.randn(n, generator=g) * 0.1 - 3.0
+        pos = torch.randperm(n, generator=g)[:5001]
+        r[pos[:5000]] = 1.0 + torch.rand(5000, generator=g) * 1e-3
+        r[pos[5000]] = 1e30
+        return r
+    if pattern == "ulp_cluster":
+        # 5000 keys within 1000 ulps of 1.0: one key value per histogram bin
+        r = torch.randn(n, generator=g) * 0.1 - 3.0
+        pos = torch.randperm(n, generator=g)[:5000]
+        ulps = torch.randint(0, 1000, (5000,), generator=g, dtype=torch.int32)
+        r[pos] = (torch.tensor(1.0).view(torch.int32) + ulps).view(torch.float32)
+        return r
+    if pattern == "sample_trap":
+        # a large value at every other evenly spaced sample position: the
+        # sampled bound overestimates and fewer than k keys pass it
+        ns = 1024 if n <= 32768 else 2048
+        r = torch.randn(n, generator=g)
+        r[(torch.arange(0, ns, 2) * n) // ns] = 10.0
+        return r
+    raise ValueError(pattern)
+
+
+@pytest.mark.parametrize("n", [32767, 32768, 100003, 131072])
+def test_topk_routes_bit_exact(dsa, n):
+    """Rows held in registers (n <= 32768) and rows read again per pass, each
+    with a score pattern for every route of the selection: candidate list with
+    one key per bin, a crowded threshold bin, an overflowing list, a list
+    holding fewer than k keys.  Compared exactly with the oracle."""
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device="cpu").manual_seed(n)
+    pats = ["normal", "ties", "const", "cluster_outlier", "ulp_cluster", "sample_trap"]
+    s = torch.stack([_topk_pattern_row(p, n, g) for p in pats])[:, None, :]
+    _topk_exact(dsa, s.to(dev).contiguous(), 2048, q_pos0=n - 1)
+
+
+@pytest.mark.parametrize("k", [2047, 3000, 4096])
+def test_topk_k_beyond_lds_assembly(dsa, k):
+    """k around and above the 2048 positions assembled in LDS (written to
+    memory directly past that), on register-resident and long rows."""
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device="cpu").manual_seed(k)
+    for n in (20000, 70001):
+        s = torch.stack([_topk_pattern_row(p, n, g) for p in ("normal", "ties", "cluster_outlier")])[:, None, :]
+        _topk_exact(dsa, s.to(dev).contiguous(), k, q_pos0=n - 1)
 
 
 # ------------------------------------------------------------------ attention on crafted index sets
