@@ -51,6 +51,12 @@ def lib():
         L.orc_topk.restype = i32
         L.orc_sparse_attn.argtypes = [vp, vp, i32, vp, i32, i32, i32, i32, i32, i32, dp, vp, vp]
         L.orc_sparse_attn.restype = i32
+        L.orc_e4m3_encode.argtypes = [ctypes.c_float]
+        L.orc_e4m3_encode.restype = i32
+        L.orc_quantize_e4m3.argtypes = [vp, i32, i64, i32, i32, ctypes.c_float, vp, vp]
+        L.orc_quantize_e4m3.restype = i32
+        L.orc_rope_rows.argtypes = [vp, vp, i64, i32, i32, i32, vp, dp, vp]
+        L.orc_rope_rows.restype = i32
         L.orc_num_threads.argtypes = []
         L.orc_num_threads.restype = i32
         _lib = L
@@ -171,6 +177,55 @@ def sparse_attn(q, kv, idx, d_v: int, scale: float, dtype: int) -> Tuple[np.ndar
     if rc != 0:
         raise ValueError("orc_sparse_attn: bad arguments")
     return out, lse
+
+
+def e4m3_encode(y: float) -> int:
+    """Nearest e4m3fn code to the fp32 value y (ties to even, saturating)."""
+    return int(lib().orc_e4m3_encode(float(y)))
+
+
+def quantize_e4m3(x, token_dims: int = 1, repeat: int = 1, margin: float = 1.0):
+    """Per-token FP8 quantisation of x (fp32 array or bf16/fp32 torch tensor).
+
+    A token is the trailing ``token_dims`` dimensions.  Returns (codes uint8
+    with x's shape, scales float32 [n_tokens, repeat])."""
+    dtype = F32
+    try:
+        import torch
+        if isinstance(x, torch.Tensor) and x.dtype == torch.bfloat16:
+            dtype = BF16
+    except ImportError:
+        pass
+    a = _np(x) if dtype == BF16 else _np(x, np.float32)
+    shape = a.shape
+    tok_len = int(np.prod(shape[len(shape) - token_dims:]))
+    n_tok = int(a.size // tok_len) if tok_len else 0
+    codes = np.empty(shape, dtype=np.uint8)
+    scales = np.empty((n_tok, repeat), dtype=np.float32)
+    rc = lib().orc_quantize_e4m3(_ptr(a), dtype, n_tok, tok_len, int(repeat), float(margin),
+                                 _ptr(codes), _ptr(scales))
+    if rc != 0:
+        raise ValueError("orc_quantize_e4m3: bad arguments")
+    return codes, scales
+
+
+def rope_rows(nope, rope, pos, base: float = 10000.0) -> np.ndarray:
+    """Assembled rows [n_tok, heads, d_nope + d_rope] float64.
+
+    nope [n_tok, heads, d_nope] and rope [n_tok, heads, d_rope] as bf16 bit
+    patterns (or bf16 torch tensors); pos [n_tok] int64 positions."""
+    nn = _np(nope).view(np.uint16)
+    rr = _np(rope).view(np.uint16)
+    n_tok, heads, d_nope = nn.shape
+    d_rope = rr.shape[2]
+    assert rr.shape[:2] == (n_tok, heads)
+    pp = _np(pos, np.int64)
+    out = np.empty((n_tok, heads, d_nope + d_rope), dtype=np.float64)
+    rc = lib().orc_rope_rows(_ptr(nn), _ptr(rr), n_tok, heads, d_nope, d_rope, _ptr(pp), float(base),
+                             _ptr(out))
+    if rc != 0:
+        raise ValueError("orc_rope_rows: bad arguments")
+    return out
 
 
 def forward_rows(inp: dict, cfg, rows, with_scores: bool = False):

@@ -16,7 +16,11 @@
  *  - attention of the query over the selected latent rows only, with the row's
  *    first d_qk columns as key and first d_v columns as value ("DeepSeek模型架构
  *    创新解析" section 1.1: the up-projection is absorbed so attention runs on the
- *    latent row) and a softmax scale supplied by the caller.
+ *    latent row) and a softmax scale supplied by the caller;
+ *  - on the input side, per-token FP8 e4m3 quantisation (nearest code by
+ *    exhaustive search, scale and division in fp32, the precision the codes
+ *    are decided in) and the assembly of a row from its compressed part and
+ *    its rotary part (section 1.1 of the same page).
  *
  * Inputs are the same bytes the GPU consumes.  FP8 e4m3fn codes are decoded
  * with a table built here from the OCP E4M3 definition (1 sign bit, 4 exponent
@@ -280,6 +284,112 @@ int orc_sparse_attn(const void* q, const void* kv, int dtype, const int32_t* idx
         free(rows);
     }
     return bad ? -1 : 0;
+}
+
+/* ---- input side: FP8 quantisation, latent-row assembly ------------------ */
+
+/*
+ * e4m3fn code nearest to y, ties to the even code (round to nearest even),
+ * magnitudes beyond 448 saturating to 448.  Found by exhaustive search over
+ * the 127 non-negative finite codes of the table above; the sign bit is y's
+ * (so -0.0 and negative values that round to zero give 0x80).  NaN gives 0x7F.
+ */
+int orc_e4m3_encode(float y)
+{
+    e4m3_table_init();
+    if (isnan(y))
+        return 0x7F;
+    double a = fabs((double)y);
+    int best = 0;
+    double bd = a;                                   /* distance to code 0 (= 0.0) */
+    for (int c = 1; c <= 0x7E; ++c) {
+        double d = fabs(a - (double)g_e4m3[c]);
+        if (d < bd || (d == bd && (c & 1) == 0)) {
+            best = c;
+            bd = d;
+        }
+    }
+    return signbit(y) ? (best | 0x80) : best;
+}
+
+/*
+ * Per-token FP8 quantisation ("DeepseekV3.2 拆解", section 核心组件: the
+ * indexer runs in FP8; "DeepSeek模型架构创新解析" section 4.3: an optional
+ * safety margin on the scale against FP8 overflow).  For each token i of
+ * tok_len values x:
+ *   amax  = max |x|
+ *   scale = fp32(fp32(amax * margin) / 448), or 1 when amax == 0
+ *   code  = e4m3(clamp(fp32(x / scale), -448, 448))
+ * and the scale is written `repeat` times (scales[i * repeat + r]).  The
+ * scale and the division are fp32 operations, the precision the codes are
+ * decided in.  x is fp32 or bf16 (dtype).  Returns 0, or -1 on bad arguments.
+ */
+int orc_quantize_e4m3(const void* x, int dtype, int64_t n_tok, int tok_len, int repeat,
+                      float margin, uint8_t* codes, float* scales)
+{
+    if ((dtype != ORC_F32 && dtype != ORC_BF16) || n_tok < 0 || tok_len < 1 || repeat < 1)
+        return -1;
+    e4m3_table_init();
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n_tok; ++i) {
+        const int64_t off = i * tok_len;
+        float amax = 0.0f;
+        for (int j = 0; j < tok_len; ++j) {
+            float a = fabsf(load_elem(x, dtype, off + j));
+            if (a > amax) amax = a;
+        }
+        float scale = 1.0f;
+        if (amax > 0.0f) {
+            float t = amax * margin;
+            scale = t / 448.0f;
+        }
+        for (int j = 0; j < tok_len; ++j) {
+            float y = load_elem(x, dtype, off + j) / scale;
+            if (y > 448.0f) y = 448.0f;
+            if (y < -448.0f) y = -448.0f;
+            codes[off + j] = (uint8_t)orc_e4m3_encode(y);
+        }
+        for (int r = 0; r < repeat; ++r)
+            scales[i * repeat + r] = scale;
+    }
+    return 0;
+}
+
+/*
+ * Row assembly with the decoupled rotary part ("DeepSeek模型架构创新解析",
+ * section 1.1: the rotary part is a separate d^R_h-wide vector, one shared
+ * key per token and one query part per head, concatenated to the compressed
+ * part).  For token i at position pos[i] and head h:
+ *   out[i][h][0:d_nope]          = nope[i][h][:]
+ *   out[i][h][d_nope + 2p]       = r[2p] cos(a_p) - r[2p+1] sin(a_p)
+ *   out[i][h][d_nope + 2p + 1]   = r[2p] sin(a_p) + r[2p+1] cos(a_p)
+ *   a_p = pos[i] * base^(-2p / d_rope),  p < d_rope / 2,   r = rope[i][h][:]
+ * (the rotary embedding of adjacent pairs; the pages name RoPE without
+ * restating it).  Inputs are bf16 bit patterns; out is float64.
+ */
+int orc_rope_rows(const uint16_t* nope, const uint16_t* rope, int64_t n_tok, int heads,
+                  int d_nope, int d_rope, const int64_t* pos, double base, double* out)
+{
+    if (n_tok < 0 || heads < 1 || d_nope < 0 || d_rope < 0 || (d_rope & 1) || !(base > 0.0))
+        return -1;
+    const int w = d_nope + d_rope;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n_tok; ++i) {
+        for (int h = 0; h < heads; ++h) {
+            const int64_t row = i * heads + h;
+            double* o = out + row * w;
+            for (int d = 0; d < d_nope; ++d)
+                o[d] = (double)bf16_to_float(nope[row * d_nope + d]);
+            for (int p = 0; p < d_rope / 2; ++p) {
+                double a = (double)pos[i] * pow(base, -2.0 * p / (double)d_rope);
+                double x0 = (double)bf16_to_float(rope[row * d_rope + 2 * p]);
+                double x1 = (double)bf16_to_float(rope[row * d_rope + 2 * p + 1]);
+                o[d_nope + 2 * p] = x0 * cos(a) - x1 * sin(a);
+                o[d_nope + 2 * p + 1] = x0 * sin(a) + x1 * cos(a);
+            }
+        }
+    }
+    return 0;
 }
 
 /* Number of threads OpenMP would use for the loops above. */
