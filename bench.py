@@ -73,6 +73,45 @@ def time_loop(fn, steps, stream):
     return e0.elapsed_time(e1) / steps
 
 
+def input_side(cfg, dev, stream, steps):
+    """The input-side kernels at this workload's sizes, each timed alone (not
+    part of the forward step): per-token FP8 quantisation of fp32 q_I and k_I,
+    and assembly of the attention queries and latent rows from their
+    compressed and rotary parts.  All four are HBM-bound; bytes are the
+    algorithmic ones (every input read once, every output written once)."""
+    import torch
+    import sparse_attention_04_amd as dsa
+    g = torch.Generator(device=dev).manual_seed(5)
+    B, L, HI, DI, H = cfg.B, cfg.Lq, cfg.n_idx_heads, cfg.idx_dim, cfg.n_heads
+    d_rope = cfg.d_qk - cfg.d_v
+    res = {}
+    qi = torch.randn(B, L, HI, DI, device=dev, generator=g)
+    ki = torch.randn(B, cfg.Lk, DI, device=dev, generator=g)
+    qc, qs = torch.empty(qi.shape, dtype=torch.uint8, device=dev), torch.empty(B, L, HI, device=dev)
+    kc, ks = torch.empty(ki.shape, dtype=torch.uint8, device=dev), torch.empty(B, cfg.Lk, device=dev)
+    jobs = [("quantize_q_idx", lambda: dsa.dsa_quantize_e4m3(qi, 2, HI, codes=qc, scales=qs, stream=stream),
+             qi.numel() * 5 + qs.numel() * 4),
+            ("quantize_k_idx", lambda: dsa.dsa_quantize_e4m3(ki, 1, 1, codes=kc, scales=ks, stream=stream),
+             ki.numel() * 5 + ks.numel() * 4)]
+    if d_rope >= 8 and cfg.io_dtype == "bf16":
+        qn = torch.randn(B, L, H, cfg.d_v, device=dev, generator=g).to(torch.bfloat16)
+        qr = torch.randn(B, L, H, d_rope, device=dev, generator=g).to(torch.bfloat16)
+        cn = torch.randn(B, cfg.Lk, 1, cfg.d_v, device=dev, generator=g).to(torch.bfloat16)
+        cr = torch.randn(B, cfg.Lk, 1, d_rope, device=dev, generator=g).to(torch.bfloat16)
+        qo = torch.empty(B, L, H, cfg.d_qk, dtype=torch.bfloat16, device=dev)
+        co = torch.empty(B, cfg.Lk, 1, cfg.d_qk, dtype=torch.bfloat16, device=dev)
+        jobs += [("rope_assemble_q", lambda: dsa.dsa_rope_assemble(qn, qr, pos0=cfg.q_pos0, out=qo, stream=stream),
+                  4 * qo.numel()),
+                 ("rope_assemble_kv", lambda: dsa.dsa_rope_assemble(cn, cr, out=co, stream=stream), 4 * co.numel())]
+    for name, f, nbytes in jobs:
+        f()
+        t = time_loop(f, steps, stream)
+        res[name] = {"ms": t, "bytes": nbytes, "achieved_gbs": nbytes / (t * 1e-3) / 1e9,
+                     "frac_hbm_peak": nbytes / (t * 1e-3) / PEAK_HBM}
+        log(f"[bench] input side {name}: {t:.3f} ms ({res[name]['achieved_gbs']:.0f} GB/s)")
+    return res
+
+
 def cpu_baseline(cfg, inp, n_rows):
     """The oracle, as it stands, on a uniform sample of query rows."""
     import numpy as np
@@ -168,6 +207,7 @@ def main():
             stages[name] = time_loop(f, max(1, args.steps), stream)
             log(f"[bench] stage {name}: {stages[name]:.3f} ms")
         del scores, idx, out, lse
+        torch.cuda.empty_cache()
 
     res = {
         "metric": METRIC,
@@ -207,6 +247,8 @@ def main():
         }
         floor = max(work["indexer_flop"] / PEAK_FP8, 0) + work["topk_bytes"] / PEAK_HBM + work["attn_flop"] / PEAK_BF16
         res["e2e_frac_of_floor"] = floor / (ms * 1e-3)
+        res["input_side"] = input_side(cfg, dev, stream, max(1, args.steps))
+        torch.cuda.empty_cache()
     if args.cpu_rows > 0:
         log(f"[bench] oracle on {args.cpu_rows} sampled rows")
         res["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_rows)

@@ -166,6 +166,62 @@ dsa_status dsa_forward(const void* q_idx, const float* q_scale,
                        int q_tile_rows, void* workspace, size_t workspace_bytes,
                        void* stream);
 
+/*
+ * Per-token FP8 e4m3 quantisation of the indexer vectors ("DeepseekV3.2 拆解",
+ * section 核心组件: the indexer computes in FP8; "DeepSeek模型架构创新解析"
+ * section 4.3: enlarge the scale's safety margin, e.g. 1.2x, against FP8
+ * overflow).  For each token i, the tok_len consecutive values x[i,:]:
+ *
+ *   amax           = max_j |x[i,j]|
+ *   scale          = (amax * margin) / 448 in fp32 arithmetic; 1 if amax == 0
+ *   codes[i,j]     = e4m3(clamp(x[i,j] / scale, -448, 448)), fp32 IEEE
+ *                    division, round to nearest even
+ *   scales[i*scale_repeat + r] = scale  for r < scale_repeat
+ *
+ * Decoding code * scale gives back x to within half an e4m3 step.  Layouts for
+ * the indexer inputs of dsa_indexer_scores:
+ *   k_I [B,Lk,d_I]:      n_tok = B*Lk, tok_len = d_I, scale_repeat = 1
+ *                        -> k_scale [B,Lk];
+ *   q_I [B,Lq,H_I,d_I]:  n_tok = B*Lq, tok_len = H_I*d_I, scale_repeat = H_I
+ *                        -> q_scale [B,Lq,H_I] (one scale per token, broadcast
+ *                        to its heads); or n_tok = B*Lq*H_I, tok_len = d_I,
+ *                        scale_repeat = 1 for one scale per head.
+ *
+ *   x      [n_tok, tok_len] fp32 or bf16 (x_dtype), finite values
+ *   codes  [n_tok, tok_len] e4m3 (output)
+ *   scales [n_tok, scale_repeat] fp32 (output)
+ * Requires tok_len % 8 == 0, 8 <= tok_len <= 16384, 1 <= scale_repeat <=
+ * 65536, margin finite and > 0 (margin < 1 saturates the largest values).
+ */
+dsa_status dsa_quantize_e4m3(const void* x, dsa_dtype x_dtype, uint8_t* codes, float* scales,
+                             int64_t n_tok, int tok_len, int scale_repeat, float margin,
+                             void* stream);
+
+/*
+ * Row assembly with the decoupled rotary part ("DeepSeek模型架构创新解析",
+ * section 1.1: the rotary position code lives in a separate d^R_h = d_h/2
+ * wide part, one key part k^R shared by all heads per token and one query part
+ * per head, beside the compressed latent c^KV / the absorbed query).  For
+ * batch entry b, token t at position pos0 + t and head h:
+ *
+ *   out[b,t,h, 0:d_nope]              = nope[b,t,h, :]
+ *   out[b,t,h, d_nope+2p], [.. +2p+1] = (r0 cos a - r1 sin a, r0 sin a + r1 cos a)
+ *       (r0, r1) = rope[b,t,h, 2p:2p+2],  a = (pos0 + t) * rope_base^(-2p/d_rope),
+ *       p < d_rope/2  (the rotary embedding of adjacent pairs).
+ *
+ * heads = 1 builds the cached latent rows kv = [c^KV ; RoPE(k^R)] (576 = 512 +
+ * 64 on the MLA rows); heads = n_h builds the attention queries.
+ *   nope [B,L,heads,d_nope] bf16 (NULL when d_nope == 0)
+ *   rope [B,L,heads,d_rope] bf16
+ *   out  [B,L,heads,d_nope+d_rope] bf16 (output, round to nearest even)
+ * Angles are evaluated in fp64, the rotation in fp32.  Requires
+ * d_nope % 8 == 0, d_rope % 8 == 0, 8 <= d_rope <= 128, pos0 >= 0 and
+ * rope_base finite and > 1.
+ */
+dsa_status dsa_rope_assemble(const void* nope, const void* rope, void* out,
+                             int B, int L, int heads, int d_nope, int d_rope, int pos0,
+                             double rope_base, void* stream);
+
 /* Static description of a status code. */
 const char* dsa_status_string(dsa_status s);
 

@@ -5,7 +5,8 @@ kernels.  Tensors are torch CUDA (ROCm) tensors, used for device memory and the
 current stream.  The functions carry the C names:
 
     dsa_indexer_scores, dsa_topk, dsa_sparse_attn,
-    dsa_forward_workspace_size, dsa_forward
+    dsa_forward_workspace_size, dsa_forward,
+    dsa_quantize_e4m3, dsa_rope_assemble         (input side)
 
 If the built library is missing the import fails loudly; there is no fallback.
 """
@@ -23,7 +24,7 @@ LIB_PATH = os.path.join(_HERE, "libdsa.so")
 
 DSA_F32, DSA_BF16, DSA_FP8_E4M3 = 0, 1, 2
 EXPORTS = ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_attn", "dsa_forward_workspace_size",
-           "dsa_forward", "dsa_status_string", "dsa_last_error")
+           "dsa_forward", "dsa_quantize_e4m3", "dsa_rope_assemble", "dsa_status_string", "dsa_last_error")
 
 
 class DSAError(RuntimeError):
@@ -47,7 +48,11 @@ def _load() -> ctypes.CDLL:
                               vp, vp, i32, i32, i32, i32, f32,
                               i32, i32, i32, i32, i32,
                               vp, vp, vp, i32, vp, sz, vp]
-    for fn in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_attn", "dsa_forward"):
+    i64, f64 = ctypes.c_int64, ctypes.c_double
+    L.dsa_quantize_e4m3.argtypes = [vp, i32, vp, vp, i64, i32, i32, f32, vp]
+    L.dsa_rope_assemble.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, f64, vp]
+    for fn in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_attn", "dsa_forward", "dsa_quantize_e4m3",
+               "dsa_rope_assemble"):
         getattr(L, fn).restype = i32
     L.dsa_status_string.argtypes = [i32]
     L.dsa_status_string.restype = ctypes.c_char_p
@@ -184,3 +189,47 @@ def dsa_forward(q_idx, q_scale, k_idx, k_scale, w, q, kv, k: int = 2048,
         B, Lq, Lk, q_pos0, k, _p(idx), _p(out), _p(lse), q_tile_rows,
         _p(workspace), workspace.numel(), _stream(stream)))
     return out, idx, lse
+
+
+def dsa_quantize_e4m3(x: torch.Tensor, token_dims: int = 1, scale_repeat: int = 1, margin: float = 1.0,
+                      codes: Optional[torch.Tensor] = None, scales: Optional[torch.Tensor] = None,
+                      stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Per-token FP8 e4m3 codes of x (fp32 or bf16); a token is the trailing
+    ``token_dims`` dimensions.  Returns (codes uint8 with x's shape, scales
+    fp32 of shape x.shape[:-token_dims] (+ (scale_repeat,) when > 1))."""
+    if x.dtype == torch.float32:
+        xd = DSA_F32
+    elif x.dtype == torch.bfloat16:
+        xd = DSA_BF16
+    else:
+        raise TypeError(f"x must be fp32 or bf16, got {x.dtype}")
+    lead = tuple(x.shape[:x.dim() - token_dims])
+    tok_len = math.prod(x.shape[x.dim() - token_dims:])
+    n_tok = math.prod(lead)
+    if codes is None:
+        codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(lead + ((scale_repeat,) if scale_repeat > 1 else ()), dtype=torch.float32,
+                             device=x.device)
+    _check("dsa_quantize_e4m3", lib.dsa_quantize_e4m3(
+        _p(x), xd, _p(codes), _p(scales), n_tok, tok_len, scale_repeat, float(margin), _stream(stream)))
+    return codes, scales
+
+
+def dsa_rope_assemble(nope: Optional[torch.Tensor], rope: torch.Tensor, pos0: int = 0,
+                      rope_base: float = 10000.0, out: Optional[torch.Tensor] = None,
+                      stream=None) -> torch.Tensor:
+    """Rows [B,L,heads,d_nope+d_rope] bf16 = [nope ; rotary(rope, pos0 + t)].
+    nope [B,L,heads,d_nope] (None when d_nope = 0) and rope [B,L,heads,d_rope]
+    are bf16; pass heads = 1 for the cached latent rows."""
+    B, L, heads, d_rope = rope.shape
+    d_nope = 0 if nope is None else nope.shape[3]
+    if nope is not None and tuple(nope.shape[:3]) != (B, L, heads):
+        raise ValueError("nope and rope must agree in [B, L, heads]")
+    if rope.dtype != torch.bfloat16 or (nope is not None and nope.dtype != torch.bfloat16):
+        raise TypeError("nope and rope must be bf16")
+    if out is None:
+        out = torch.empty((B, L, heads, d_nope + d_rope), dtype=torch.bfloat16, device=rope.device)
+    _check("dsa_rope_assemble", lib.dsa_rope_assemble(
+        _p(nope), _p(rope), _p(out), B, L, heads, d_nope, d_rope, pos0, float(rope_base), _stream(stream)))
+    return out

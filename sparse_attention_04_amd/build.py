@@ -23,6 +23,7 @@ SOURCES = [
     ("indexer.hip", ["-mllvm", "-amdgpu-mfma-vgpr-form"]),
     ("topk.hip", []),
     ("sparse_attn.hip", []),
+    ("inputs.hip", []),
 ]
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

@@ -287,4 +287,58 @@ dsa_status dsa_forward(const void* q_idx, const float* q_scale, const void* k_id
     return ok();
 }
 
+dsa_status dsa_quantize_e4m3(const void* x, dsa_dtype x_dtype, uint8_t* codes, float* scales,
+                             int64_t n_tok, int tok_len, int scale_repeat, float margin, void* stream)
+{
+    const char* fn = "dsa_quantize_e4m3";
+    if (n_tok < 0)
+        return fail(DSA_ERR_SHAPE, "%s: negative n_tok (%lld)", fn, (long long)n_tok);
+    if (tok_len < 8 || tok_len > 16384 || tok_len % 8 != 0)
+        return fail(DSA_ERR_UNSUPPORTED, "%s: tok_len=%d must be a multiple of 8 in [8, 16384]", fn, tok_len);
+    if (scale_repeat < 1 || scale_repeat > 65536)
+        return fail(DSA_ERR_SHAPE, "%s: scale_repeat=%d outside [1, 65536]", fn, scale_repeat);
+    if (!(margin > 0.f) || !std::isfinite(margin))
+        return fail(DSA_ERR_SHAPE, "%s: margin must be finite and > 0", fn);
+    if (x_dtype != DSA_F32 && x_dtype != DSA_BF16)
+        return fail(DSA_ERR_DTYPE, "%s: x must be fp32 or bf16", fn);
+    if (n_tok == 0) return ok();
+    if (n_tok > (int64_t)1 << 40)
+        return fail(DSA_ERR_UNSUPPORTED, "%s: n_tok=%lld too large", fn, (long long)n_tok);
+    REQUIRE_PTR(x);
+    REQUIRE_PTR(codes);
+    REQUIRE_PTR(scales);
+    dsa::QuantLaunch a{};
+    a.x = x; a.codes = codes; a.scales = scales; a.n_tok = n_tok; a.tok_len = tok_len;
+    a.repeat = scale_repeat; a.margin = margin; a.bf16 = (x_dtype == DSA_BF16);
+    return hip_status(fn, dsa::launch_quantize_e4m3(a, (hipStream_t)stream));
+}
+
+dsa_status dsa_rope_assemble(const void* nope, const void* rope, void* out, int B, int L, int heads,
+                             int d_nope, int d_rope, int pos0, double rope_base, void* stream)
+{
+    const char* fn = "dsa_rope_assemble";
+    if (B < 0 || L < 0 || heads < 1 || d_nope < 0 || pos0 < 0)
+        return fail(DSA_ERR_SHAPE, "%s: bad sizes (B=%d L=%d heads=%d d_nope=%d pos0=%d)", fn, B, L, heads,
+                    d_nope, pos0);
+    if (d_nope % 8 != 0 || d_rope % 8 != 0 || d_rope < 8 || d_rope > 128)
+        return fail(DSA_ERR_UNSUPPORTED, "%s: d_nope=%d and d_rope=%d must be multiples of 8, 8 <= d_rope <= 128",
+                    fn, d_nope, d_rope);
+    if (!(rope_base > 1.0) || !std::isfinite(rope_base))
+        return fail(DSA_ERR_SHAPE, "%s: rope_base must be finite and > 1", fn);
+    if ((int64_t)pos0 + L > ((int64_t)1 << 31) - 1)
+        return fail(DSA_ERR_SHAPE, "%s: positions exceed the int range", fn);
+    if ((int64_t)B * L > ((int64_t)1 << 31) - 1)
+        return fail(DSA_ERR_UNSUPPORTED, "%s: B*L=%lld too large", fn, (long long)B * L);
+    if ((int64_t)heads * (d_nope + d_rope) > ((int64_t)1 << 24))
+        return fail(DSA_ERR_UNSUPPORTED, "%s: heads * (d_nope + d_rope) too large", fn);
+    if (B == 0 || L == 0) return ok();
+    if (d_nope > 0) REQUIRE_PTR(nope);
+    REQUIRE_PTR(rope);
+    REQUIRE_PTR(out);
+    dsa::RopeLaunch a{};
+    a.nope = nope; a.rope = rope; a.out = out; a.B = B; a.L = L; a.heads = heads;
+    a.d_nope = d_nope; a.d_rope = d_rope; a.pos0 = pos0; a.base = rope_base;
+    return hip_status(fn, dsa::launch_rope_assemble(a, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -46,9 +46,29 @@ struct AttnLaunch {
     bool bf16;
 };
 
+struct QuantLaunch {
+    const void* x;          // [n_tok, tok_len] fp32 or bf16
+    uint8_t* codes;         // [n_tok, tok_len] e4m3
+    float* scales;          // [n_tok, repeat]
+    int64_t n_tok;
+    int tok_len, repeat;    // tok_len % 8 == 0, tok_len <= 16384
+    float margin;
+    bool bf16;
+};
+
+struct RopeLaunch {
+    const void* nope;       // [B, L, heads, d_nope] bf16
+    const void* rope;       // [B, L, heads, d_rope] bf16
+    void* out;              // [B, L, heads, d_nope + d_rope] bf16
+    int B, L, heads, d_nope, d_rope, pos0;
+    double base;
+};
+
 hipError_t launch_indexer(const IndexerLaunch& a, hipStream_t s);
 hipError_t launch_topk(const TopkLaunch& a, hipStream_t s);
 hipError_t launch_sparse_attn(const AttnLaunch& a, hipStream_t s);
+hipError_t launch_quantize_e4m3(const QuantLaunch& a, hipStream_t s);
+hipError_t launch_rope_assemble(const RopeLaunch& a, hipStream_t s);
 
 // Which (Dqk, Dv) pairs the bf16 attention kernel is instantiated for.
 bool sparse_attn_bf16_supported(int Dqk, int Dv);

@@ -133,3 +133,32 @@ def test_forward_workspace(L):
     assert fwd(A, need, T=-1) == SHAPE
     assert fwd(A, need, H=16) == UNSUP
     assert fwd(A, need, io=FP8) == DTYPE
+
+
+def test_quantize_validation(L):
+    def q(**kw):
+        a = dict(x=A, dt=F32, c=A, s=A, n=4, t=128, r=1, m=1.0)
+        a.update(kw)
+        return L.dsa_quantize_e4m3(a["x"], a["dt"], a["c"], a["s"], a["n"], a["t"], a["r"], a["m"], None)
+    assert q(x=None) == NULL and q(c=None) == NULL and q(s=None) == NULL
+    assert q(x=MIS) == ALIGN
+    assert q(dt=FP8) == DTYPE
+    assert q(t=12) == UNSUP and q(t=0) == UNSUP and q(t=16392) == UNSUP
+    assert q(r=0) == SHAPE and q(n=-1) == SHAPE
+    assert q(m=0.0) == SHAPE and q(m=float("inf")) == SHAPE and q(m=float("nan")) == SHAPE
+    assert q(n=0, x=None) == OK                     # empty: nothing to do
+
+
+def test_rope_assemble_validation(L):
+    def r(**kw):
+        a = dict(n=A, r=A, o=A, B=1, L=4, h=1, dn=512, dr=64, p0=0, base=10000.0)
+        a.update(kw)
+        return L.dsa_rope_assemble(a["n"], a["r"], a["o"], a["B"], a["L"], a["h"], a["dn"], a["dr"], a["p0"],
+                                   a["base"], None)
+    assert r(r=None) == NULL and r(o=None) == NULL and r(n=None) == NULL
+    assert r(n=None, dn=0, B=0) == OK               # no compressed part, empty problem
+    assert r(o=MIS) == ALIGN
+    assert r(dr=6) == UNSUP and r(dr=136) == UNSUP and r(dn=4) == UNSUP and r(dr=0) == UNSUP
+    assert r(base=1.0) == SHAPE and r(base=float("nan")) == SHAPE
+    assert r(h=0) == SHAPE and r(p0=-1) == SHAPE and r(B=-1) == SHAPE
+    assert r(B=0) == OK and r(L=0) == OK
