@@ -68,8 +68,19 @@ void indexer_fp8_kernel(const uint8_t* __restrict__ q8, const float* __restrict_
     const int t0 = t_begin + qb * kQB;
     const int rows_here = min(kQB, t_begin + t_count - t0);
     const int tpos_last = q_pos0 + t0 + rows_here - 1;
-    if (skip_upto_k > 0 && tpos_last + 1 <= skip_upto_k)
+    if (!write_masked && skip_upto_k > 0 && tpos_last + 1 <= skip_upto_k)
         return;
+
+    // The -inf upper triangle.  Block qb writes the masked tail of its mirror
+    // block nqb-1-qb: columns [mfrom, Lk) of the mirror's rows, where mfrom
+    // is the end of the groups the mirror computes itself.  The mirror's tail
+    // is about as long as this block's row range, so the longest-computing
+    // blocks (issued first) carry the longest tails, one 16-byte store per
+    // thread per key group, while the MFMA work runs; the short blocks at the
+    // end of the launch carry short tails.
+    const int t0_m = t_begin + (nqb - 1 - qb) * kQB;
+    const int rows_m = min(kQB, t_begin + t_count - t0_m);
+    const int mfrom = ((q_pos0 + t0_m + rows_m - 1) / kKG + 1) * kKG;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -214,6 +225,18 @@ void indexer_fp8_kernel(const uint8_t* __restrict__ q8, const float* __restrict_
             const v4f x = red[kb][ww][wave][lane];
             sum[0] += x[0]; sum[1] += x[1]; sum[2] += x[2]; sum[3] += x[3];
         }
+        if (write_masked) {
+            // mirror tail: row tid / 16 of the mirror block, 4 columns per thread
+            const int r = tid >> 4, s = mfrom + s0 + 4 * (tid & 15);
+            if (r < rows_m && s < Lk) {
+                float* dst = scores + (int64_t)b * sc_bstride + (int64_t)(t0_m + r - t_begin) * sc_rstride + s;
+                if (s + 3 < Lk && ((uintptr_t)dst & 15u) == 0) {
+                    *(v4f*)dst = v4f{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+                } else {
+                    for (int e = 0; e < 4 && s + e < Lk; ++e) dst[e] = -INFINITY;
+                }
+            }
+        }
         if (col < rows_here) {
             const int t = t0 + col;
             const int tpos = q_pos0 + t;
@@ -238,12 +261,12 @@ void indexer_fp8_kernel(const uint8_t* __restrict__ q8, const float* __restrict_
     }
 
     if (write_masked) {
-        // -inf beyond the last computed group for every row of the block
+        // what is left of the mirror tail after one 64-column slice per group
         // (16-byte stores where the row allows, the ragged end one by one)
-        const int s_from = ngroups * kKG;
+        const int s_from = mfrom + ngroups * kKG;
         const v4f ninf = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-        for (int r = 0; r < rows_here; ++r) {
-            float* dst = scores + (int64_t)b * sc_bstride + (int64_t)(t0 + r - t_begin) * sc_rstride;
+        for (int r = 0; r < rows_m; ++r) {
+            float* dst = scores + (int64_t)b * sc_bstride + (int64_t)(t0_m + r - t_begin) * sc_rstride;
             int s_vec = s_from, s_end = Lk;
             if (s_from < Lk && (((uintptr_t)(dst + s_from)) & 15u) == 0) {
                 const int nvec = (Lk - s_from) >> 2;
