@@ -187,11 +187,23 @@ void indexer_fp8_kernel(const uint8_t* __restrict__ q8, const float* __restrict_
         float ksc[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) ksc[r] = k_scale[(int64_t)b * Lk + min(sb + r, Lk - 1)];
+        // key fragments of tile i: the linear part's 8 bytes and the 32-byte
+        // MFMA operand; those of tile i + 1 are read while tile i computes
+        auto load_frag = [&](int i, u32x2& kk_, v8i& af_) {
+            const int kr = i * 16 + col;
+            kk_ = *(const u32x2*)(kt + ktile_off(kr, lin_chunk) + lin_byte);
+            af_ = as_i8(*(const u32x4*)(kt + ktile_off(kr, 2 * grp)),
+                        *(const u32x4*)(kt + ktile_off(kr, 2 * grp + 1)));
+        };
+        u32x2 kk;
+        v8i af;
+        load_frag(0, kk, af);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int kr = i * 16 + col;
+            u32x2 kk_next;
+            v8i af_next;
+            if (i + 1 < 4) load_frag(i + 1, kk_next, af_next);
             // linear part: this wave's 32 dims of c[col] . k[kr]
-            const u32x2 kk = *(const u32x2*)(kt + ktile_off(kr, lin_chunk) + lin_byte);
             u32x4 kbf;
             kbf[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kk[0], 1.0f, false));
             kbf[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kk[0], 1.0f, true));
@@ -202,8 +214,6 @@ void indexer_fp8_kernel(const uint8_t* __restrict__ q8, const float* __restrict_
             acc = mfma_bf16_16x16x32(ka, cb[1], acc);
             acc = mfma_bf16_16x16x32(ka, cb[0], acc);
             // absolute part over the wave's 16 heads
-            const v8i af = as_i8(*(const u32x4*)(kt + ktile_off(kr, 2 * grp)),
-                                 *(const u32x4*)(kt + ktile_off(kr, 2 * grp + 1)));
             // software-pipelined: the MFMA of head h + 1 is in flight while
             // the result of head h is folded in
             v4f d = mfma_fp8_16x16x128(af, qf[0], zero);
@@ -215,6 +225,10 @@ void indexer_fp8_kernel(const uint8_t* __restrict__ q8, const float* __restrict_
                 d = dn;
             }
             red[kb][wave][i][lane] = acc;
+            if (i + 1 < 4) {
+                kk = kk_next;
+                af = af_next;
+            }
         }
         wait_vmcnt0();
         __syncthreads();
