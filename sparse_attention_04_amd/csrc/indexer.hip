@@ -214,15 +214,19 @@ void indexer_fp8_kernel(const uint8_t* __restrict__ q8, const float* __restrict_
             acc = mfma_bf16_16x16x32(ka, cb[1], acc);
             acc = mfma_bf16_16x16x32(ka, cb[0], acc);
             // absolute part over the wave's 16 heads
-            // software-pipelined: the MFMA of head h + 1 is in flight while
-            // the result of head h is folded in
+            // software-pipelined: the MFMAs of heads h + 1 and h + 2 are in
+            // flight while the result of head h is folded in
             v4f d = mfma_fp8_16x16x128(af, qf[0], zero);
+            v4f d1 = mfma_fp8_16x16x128(af, qf[1], zero);
 #pragma unroll
             for (int h = 0; h < kHPW; ++h) {
-                const v4f dn = (h + 1 < kHPW) ? mfma_fp8_16x16x128(af, qf[(h + 1) % kHPW], zero) : d;
+                const v4f d2 = (h + 2 < kHPW) ? mfma_fp8_16x16x128(af, qf[(h + 2) % kHPW], zero) : d1;
+                __builtin_amdgcn_sched_barrier(0);           // keep the issue order written here
 #pragma unroll
                 for (int r = 0; r < 4; ++r) acc[r] = fmaf(wv[h], fabsf(d[r]), acc[r]);
-                d = dn;
+                __builtin_amdgcn_sched_barrier(0);
+                d = d1;
+                d1 = d2;
             }
             red[kb][wave][i][lane] = acc;
             if (i + 1 < 4) {
