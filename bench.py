@@ -176,7 +176,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    fwd = dsa.Forward(cfg.B, cfg.Lq, cfg.Lk, cfg.k, cfg.n_heads, cfg.d_v, inp["q"].dtype, dev,
+    fwd = dsa.Forward(cfg.B, cfg.Lq, cfg.Lk, cfg.k, cfg.n_heads, cfg.d_v, inp["q"].dtype, dev, d_qk=cfg.d_qk,
                       q_tile_rows=cfg.q_tile_rows)
     run = lambda: fwd(inp["q_idx"], inp["q_scale"], inp["k_idx"], inp["k_scale"], inp["w"], inp["q"],
                       inp["kv"], cfg.softmax_scale, q_pos0=cfg.q_pos0, stream=stream)

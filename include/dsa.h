@@ -127,20 +127,41 @@ dsa_status dsa_topk(const float* scores, int32_t* idx,
  * Supported: BF16 with n_heads % 16 == 0, n_heads <= 128, and
  *            (d_qk, d_v) in {(576,512), (128,128), (64,64)};
  *            F32 with d_qk <= 1024, d_v <= d_qk, n_heads <= 256.
+ *
+ * Few query rows (decode): when dsa_sparse_attn_workspace_size() is non-zero
+ * and `workspace` (256-byte aligned) holds that many bytes, each row's
+ * selected set is split over several workgroups whose normalised partial
+ * outputs and log-sum-exps are merged in fp32 (in a fixed order, so the
+ * result is deterministic).  With workspace NULL or too small the rows run
+ * unsplit; the two results agree within fp32 rounding before the bf16
+ * rounding of out.  The workspace's contents on entry do not matter.
  */
 dsa_status dsa_sparse_attn(const void* q, const void* kv, const int32_t* idx,
                            void* out, float* lse,
                            int B, int Lq, int Lk, int q_pos0,
                            int n_heads, int d_qk, int d_v, int k,
-                           float softmax_scale, dsa_dtype io_dtype, void* stream);
+                           float softmax_scale, dsa_dtype io_dtype,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Bytes of workspace with which dsa_sparse_attn splits the selected sets
+ * (0: these sizes run unsplit).  The split applies to the bf16 576/512 rows
+ * with 32, 64 or 128 heads, k <= 2048, and fewer than 128 query rows
+ * (B * Lq) in all.
+ */
+size_t dsa_sparse_attn_workspace_size(int B, int Lq, int n_heads, int d_qk, int d_v, int k,
+                                      dsa_dtype io_dtype);
 
 /*
  * Bytes of device workspace dsa_forward needs for these sizes.  q_tile_rows is
  * the number of query rows (per batch entry) whose scores are held at once;
- * 0 picks Lq, or fewer rows when Lq rows of scores would exceed 4 GiB.
- * Returns 0 for an empty problem.
+ * 0 picks Lq, or fewer rows when Lq rows of scores would exceed 4 GiB.  The
+ * workspace also holds the attention's split partials when
+ * dsa_sparse_attn_workspace_size(B, Lq, ...) is non-zero.  Returns 0 for an
+ * empty problem.
  */
-size_t dsa_forward_workspace_size(int B, int Lq, int Lk, int k, int q_tile_rows);
+size_t dsa_forward_workspace_size(int B, int Lq, int Lk, int k, int n_heads, int d_qk, int d_v,
+                                  dsa_dtype io_dtype, int q_tile_rows);
 
 /*
  * The whole forward: scores -> top-k -> sparse attention, processed in tiles of
@@ -148,11 +169,12 @@ size_t dsa_forward_workspace_size(int B, int Lq, int Lk, int k, int q_tile_rows)
  * once (the full Lq x Lk matrix is never held when q_tile_rows < Lq).
  *
  * Results are identical, bit for bit, to calling dsa_indexer_scores, dsa_topk
- * and dsa_sparse_attn in turn.  Rows with t_pos + 1 <= k select every
+ * and dsa_sparse_attn (with its workspace) in turn.  Rows with t_pos + 1 <= k select every
  * preceding token, so their scores are not computed.
  *
  * Arguments are those of the three calls; idx_out [B,Lq,k] and lse may be NULL.
- * workspace must hold dsa_forward_workspace_size(B, Lq, Lk, k, q_tile_rows)
+ * workspace must hold dsa_forward_workspace_size(B, Lq, Lk, k, n_heads, d_qk,
+ * d_v, io_dtype, q_tile_rows)
  * bytes, 256-byte aligned; its contents on entry do not matter.
  */
 dsa_status dsa_forward(const void* q_idx, const float* q_scale,

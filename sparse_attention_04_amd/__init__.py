@@ -5,7 +5,7 @@ kernels.  Tensors are torch CUDA (ROCm) tensors, used for device memory and the
 current stream.  The functions carry the C names:
 
     dsa_indexer_scores, dsa_topk, dsa_sparse_attn,
-    dsa_forward_workspace_size, dsa_forward,
+    dsa_sparse_attn_workspace_size, dsa_forward_workspace_size, dsa_forward,
     dsa_quantize_e4m3, dsa_rope_assemble         (input side)
 
 If the built library is missing the import fails loudly; there is no fallback.
@@ -23,7 +23,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdsa.so")
 
 DSA_F32, DSA_BF16, DSA_FP8_E4M3 = 0, 1, 2
-EXPORTS = ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_attn", "dsa_forward_workspace_size",
+EXPORTS = ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_attn", "dsa_sparse_attn_workspace_size",
+           "dsa_forward_workspace_size",
            "dsa_forward", "dsa_quantize_e4m3", "dsa_rope_assemble", "dsa_status_string", "dsa_last_error")
 
 
@@ -41,8 +42,10 @@ def _load() -> ctypes.CDLL:
     vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     L.dsa_indexer_scores.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp]
     L.dsa_topk.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp]
-    L.dsa_sparse_attn.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp]
-    L.dsa_forward_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+    L.dsa_sparse_attn.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp, sz, vp]
+    L.dsa_sparse_attn_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+    L.dsa_sparse_attn_workspace_size.restype = sz
+    L.dsa_forward_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i32]
     L.dsa_forward_workspace_size.restype = sz
     L.dsa_forward.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32,
                               vp, vp, i32, i32, i32, i32, f32,
@@ -122,10 +125,19 @@ def dsa_topk(scores, k: int, q_pos0: int = 0, idx: Optional[torch.Tensor] = None
     return idx
 
 
+def dsa_sparse_attn_workspace_size(B: int, Lq: int, n_heads: int, d_qk: int, d_v: int, k: int,
+                                   io_dtype: torch.dtype = torch.bfloat16) -> int:
+    dt = DSA_BF16 if io_dtype == torch.bfloat16 else DSA_F32
+    return int(lib.dsa_sparse_attn_workspace_size(B, Lq, n_heads, d_qk, d_v, k, dt))
+
+
 def dsa_sparse_attn(q, kv, idx, d_v: int, softmax_scale: float, q_pos0: int = 0,
                     out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                    want_lse: bool = True, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """(out [B,Lq,H,d_v] in q's dtype, lse [B,Lq,H] fp32 or None)."""
+                    want_lse: bool = True, workspace: Optional[torch.Tensor] = None, split: bool = True,
+                    stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """(out [B,Lq,H,d_v] in q's dtype, lse [B,Lq,H] fp32 or None).  With few
+    query rows the selected sets are split over workgroups; the workspace for
+    that is allocated here unless given (split=False runs unsplit)."""
     B, Lq, H, Dqk = q.shape
     Lk = kv.shape[1]
     k = idx.shape[2]
@@ -133,14 +145,21 @@ def dsa_sparse_attn(q, kv, idx, d_v: int, softmax_scale: float, q_pos0: int = 0,
         out = torch.empty((B, Lq, H, d_v), dtype=q.dtype, device=q.device)
     if lse is None and want_lse:
         lse = torch.empty((B, Lq, H), dtype=torch.float32, device=q.device)
+    if workspace is None and split:
+        nbytes = dsa_sparse_attn_workspace_size(B, Lq, H, Dqk, d_v, k, q.dtype)
+        if nbytes:
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
     _check("dsa_sparse_attn", lib.dsa_sparse_attn(
         _p(q), _p(kv), _p(idx), _p(out), _p(lse), B, Lq, Lk, q_pos0, H, Dqk, d_v, k,
-        float(softmax_scale), _io_dtype(q), _stream(stream)))
+        float(softmax_scale), _io_dtype(q), _p(workspace),
+        0 if workspace is None else workspace.numel(), _stream(stream)))
     return out, lse
 
 
-def dsa_forward_workspace_size(B: int, Lq: int, Lk: int, k: int, q_tile_rows: int = 0) -> int:
-    return int(lib.dsa_forward_workspace_size(B, Lq, Lk, k, q_tile_rows))
+def dsa_forward_workspace_size(B: int, Lq: int, Lk: int, k: int, n_heads: int, d_qk: int, d_v: int,
+                               io_dtype: torch.dtype = torch.bfloat16, q_tile_rows: int = 0) -> int:
+    dt = DSA_BF16 if io_dtype == torch.bfloat16 else DSA_F32
+    return int(lib.dsa_forward_workspace_size(B, Lq, Lk, k, n_heads, d_qk, d_v, dt, q_tile_rows))
 
 
 class Forward:
@@ -148,12 +167,12 @@ class Forward:
     then each call is one ``dsa_forward`` on the current stream."""
 
     def __init__(self, B, Lq, Lk, k, n_heads, d_v, io_dtype: torch.dtype, device,
-                 q_tile_rows: int = 0, want_idx: bool = True, want_lse: bool = True):
+                 q_tile_rows: int = 0, want_idx: bool = True, want_lse: bool = True, d_qk: int = 576):
         self.q_tile_rows = q_tile_rows
         self.out = torch.empty((B, Lq, n_heads, d_v), dtype=io_dtype, device=device)
         self.idx = torch.empty((B, Lq, k), dtype=torch.int32, device=device) if want_idx else None
         self.lse = torch.empty((B, Lq, n_heads), dtype=torch.float32, device=device) if want_lse else None
-        nbytes = dsa_forward_workspace_size(B, Lq, Lk, k, q_tile_rows)
+        nbytes = dsa_forward_workspace_size(B, Lq, Lk, k, n_heads, d_qk, d_v, io_dtype, q_tile_rows)
         self.workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
         self.k = k
 
@@ -180,7 +199,7 @@ def dsa_forward(q_idx, q_scale, k_idx, k_scale, w, q, kv, k: int = 2048,
         softmax_scale = 1.0 / math.sqrt(Dqk)
     if out is None:
         out = torch.empty((B, Lq, H, d_v), dtype=q.dtype, device=q.device)
-    nbytes = dsa_forward_workspace_size(B, Lq, Lk, k, q_tile_rows)
+    nbytes = dsa_forward_workspace_size(B, Lq, Lk, k, H, Dqk, d_v, q.dtype, q_tile_rows)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
     _check("dsa_forward", lib.dsa_forward(

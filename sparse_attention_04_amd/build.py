@@ -1,6 +1,6 @@
 """Build ``libdsa.so`` (the C-ABI library) for gfx950 with hipcc, in-tree.
 
-    python -m sparse_attention_04_amd.build      # or build() from Python
+    python sparse_attention_04_amd/build.py      # or build() from Python
 """
 from __future__ import annotations
 

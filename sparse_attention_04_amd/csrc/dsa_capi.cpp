@@ -198,9 +198,19 @@ dsa_status dsa_topk(const float* scores, int32_t* idx, int B, int Lq, int Lk, in
     return hip_status(fn, dsa::launch_topk(a, (hipStream_t)stream));
 }
 
+size_t dsa_sparse_attn_workspace_size(int B, int Lq, int n_heads, int d_qk, int d_v, int k, dsa_dtype io_dtype)
+{
+    if (B <= 0 || Lq <= 0 || n_heads <= 0 || d_v <= 0 || k <= 0) return 0;
+    const int64_t rows = (int64_t)B * Lq;
+    const int ns = dsa::sparse_attn_split(rows, n_heads, d_qk, d_v, k, io_dtype == DSA_BF16);
+    const size_t bytes = dsa::sparse_attn_split_bytes(rows, n_heads, d_v, ns);
+    return bytes ? round256(bytes) : 0;
+}
+
 dsa_status dsa_sparse_attn(const void* q, const void* kv, const int32_t* idx, void* out, float* lse,
                            int B, int Lq, int Lk, int q_pos0, int n_heads, int d_qk, int d_v, int k,
-                           float softmax_scale, dsa_dtype io_dtype, void* stream)
+                           float softmax_scale, dsa_dtype io_dtype, void* workspace, size_t workspace_bytes,
+                           void* stream)
 {
     const char* fn = "dsa_sparse_attn";
     bool empty = false;
@@ -215,16 +225,29 @@ dsa_status dsa_sparse_attn(const void* q, const void* kv, const int32_t* idx, vo
     a.B = B; a.Lq = Lq; a.Lk = Lk; a.t_begin = 0; a.t_count = Lq; a.idx_bstride = (int64_t)Lq * k;
     a.H = n_heads; a.Dqk = d_qk; a.Dv = d_v; a.k = k; a.scale = softmax_scale;
     a.bf16 = (io_dtype == DSA_BF16);
+    // the split over the selected set runs only with a large enough workspace
+    const size_t need = dsa_sparse_attn_workspace_size(B, Lq, n_heads, d_qk, d_v, k, io_dtype);
+    if (need > 0 && workspace != nullptr && workspace_bytes >= need) {
+        if (((uintptr_t)workspace & 255u) != 0)
+            return fail(DSA_ERR_ALIGN, "%s: workspace must be 256-byte aligned", fn);
+        a.nsplit = dsa::sparse_attn_split((int64_t)B * Lq, n_heads, d_qk, d_v, k, a.bf16);
+        a.part = (float*)workspace;
+    }
     return hip_status(fn, dsa::launch_sparse_attn(a, (hipStream_t)stream));
 }
 
-size_t dsa_forward_workspace_size(int B, int Lq, int Lk, int k, int q_tile_rows)
+size_t dsa_forward_workspace_size(int B, int Lq, int Lk, int k, int n_heads, int d_qk, int d_v,
+                                  dsa_dtype io_dtype, int q_tile_rows)
 {
     if (B <= 0 || Lq <= 0 || Lk <= 0 || k <= 0 || q_tile_rows < 0) return 0;
     const int T = q_tile_rows > 0 ? (q_tile_rows < Lq ? q_tile_rows : Lq) : auto_tile_rows(B, Lq, Lk);
     const size_t scores = round256((size_t)B * (size_t)T * (size_t)Lk * sizeof(float));
     const size_t idx = round256((size_t)B * (size_t)T * (size_t)k * sizeof(int32_t));
-    return scores + idx;
+    // the attention's split partials: decided by the whole problem's rows
+    // (as dsa_sparse_attn decides), sized for one tile
+    const int ns = dsa::sparse_attn_split((int64_t)B * Lq, n_heads, d_qk, d_v, k, io_dtype == DSA_BF16);
+    const size_t part = round256(dsa::sparse_attn_split_bytes((int64_t)B * T, n_heads, d_v, ns));
+    return scores + idx + part;
 }
 
 dsa_status dsa_forward(const void* q_idx, const float* q_scale, const void* k_idx,
@@ -247,13 +270,15 @@ dsa_status dsa_forward(const void* q_idx, const float* q_scale, const void* k_id
     OPTIONAL_PTR(idx_out);
     if (q_tile_rows < 0) return fail(DSA_ERR_SHAPE, "%s: q_tile_rows=%d must be >= 0", fn, q_tile_rows);
     const int T = q_tile_rows > 0 ? (q_tile_rows < Lq ? q_tile_rows : Lq) : auto_tile_rows(B, Lq, Lk);
-    const size_t need = dsa_forward_workspace_size(B, Lq, Lk, k, q_tile_rows);
+    const size_t need = dsa_forward_workspace_size(B, Lq, Lk, k, n_heads, d_qk, d_v, io_dtype, q_tile_rows);
     if (workspace == nullptr || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0)
         return fail(DSA_ERR_WORKSPACE, "%s: workspace needs %zu bytes, 256-byte aligned (got %zu at %p)",
                     fn, need, workspace_bytes, workspace);
 
     float* ws_scores = (float*)workspace;
     int32_t* ws_idx = (int32_t*)((char*)workspace + round256((size_t)B * T * (size_t)Lk * sizeof(float)));
+    float* ws_part = (float*)((char*)ws_idx + round256((size_t)B * T * (size_t)k * sizeof(int32_t)));
+    const int nsplit = dsa::sparse_attn_split((int64_t)B * Lq, n_heads, d_qk, d_v, k, io_dtype == DSA_BF16);
     hipStream_t s = (hipStream_t)stream;
 
     for (int t0 = 0; t0 < Lq; t0 += T) {
@@ -281,6 +306,8 @@ dsa_status dsa_forward(const void* q_idx, const float* q_scale, const void* k_id
         aa.B = B; aa.Lq = Lq; aa.Lk = Lk; aa.t_begin = t0; aa.t_count = tc; aa.idx_bstride = idx_bstride;
         aa.H = n_heads; aa.Dqk = d_qk; aa.Dv = d_v; aa.k = k; aa.scale = softmax_scale;
         aa.bf16 = (io_dtype == DSA_BF16);
+        aa.nsplit = nsplit;
+        aa.part = nsplit > 1 ? ws_part : nullptr;
         e = dsa::launch_sparse_attn(aa, s);
         if (e != hipSuccess) return hip_status(fn, e);
     }

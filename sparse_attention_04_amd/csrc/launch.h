@@ -44,6 +44,8 @@ struct AttnLaunch {
     int H, Dqk, Dv, k;
     float scale;
     bool bf16;
+    int nsplit;             // > 1: split each row's selected set (32-head kernel only)
+    float* part;            // split partials, sparse_attn_split_bytes(B * t_count, H, Dv, nsplit) bytes
 };
 
 struct QuantLaunch {
@@ -69,6 +71,11 @@ hipError_t launch_topk(const TopkLaunch& a, hipStream_t s);
 hipError_t launch_sparse_attn(const AttnLaunch& a, hipStream_t s);
 hipError_t launch_quantize_e4m3(const QuantLaunch& a, hipStream_t s);
 hipError_t launch_rope_assemble(const RopeLaunch& a, hipStream_t s);
+
+// Split factor for the selected set when few query rows are attended (1 = no
+// split), and the bytes of partial results it needs.
+int sparse_attn_split(int64_t rows, int H, int Dqk, int Dv, int k, bool bf16);
+size_t sparse_attn_split_bytes(int64_t rows, int H, int Dv, int nsplit);
 
 // Which (Dqk, Dv) pairs the bf16 attention kernel is instantiated for.
 bool sparse_attn_bf16_supported(int Dqk, int Dv);

@@ -226,7 +226,8 @@ __global__ __launch_bounds__(64 * NW)
 void sparse_attn_bf16_w32_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
                                  const int32_t* __restrict__ idx, uint16_t* __restrict__ out,
                                  float* __restrict__ lse, int Lq, int Lk, int t_begin, int H, int k,
-                                 int64_t idx_bstride, float scale_log2)
+                                 int64_t idx_bstride, float scale_log2, int cps,
+                                 float* __restrict__ part_o, float* __restrict__ part_lse)
 {
     using S = W32Shape<DQK, DV, NW>;
     constexpr int NC = S::NC;
@@ -270,7 +271,11 @@ void sparse_attn_bf16_w32_kernel(const uint16_t* __restrict__ q, const uint16_t*
     __syncthreads();
 #pragma unroll
     for (int w = 0; w < NW; ++w) last = max(last, wlast[w]);
-    const int nchunks = (last + NC) / NC;                   // last = -1: nothing to attend
+    // Split over the selected set (gridDim.z > 1): this workgroup takes chunks
+    // [c0, c0 + cps) of the list and leaves a normalised partial output and
+    // its log-sum-exp for the merge kernel.
+    const int c0 = (int)blockIdx.z * cps;
+    const int nchunks = max(0, min((last + NC) / NC - c0, cps));   // last = -1: nothing to attend
     // bit r set when entry r of chunk c is a real row
     auto valid_mask = [&](int c) -> uint32_t {
         return (uint32_t)__ballot(lane < NC && sel[c * NC + (lane & 31)] >= 0);
@@ -317,7 +322,7 @@ void sparse_attn_bf16_w32_kernel(const uint16_t* __restrict__ q, const uint16_t*
         for (int it = -1; it < nchunks; ++it) {
             wait_vmcnt0();                                   // this wave's copies of chunk it landed
             __syncthreads();                                 // all of chunk it visible; chunk it-1 consumed
-            const int c = it < 0 ? 0 : it;
+            const int c = c0 + (it < 0 ? 0 : it);
             const uint32_t vmask = valid_mask(c);
             const uint8_t* cur = ring[c % S::NBUF];
 
@@ -349,7 +354,7 @@ void sparse_attn_bf16_w32_kernel(const uint16_t* __restrict__ q, const uint16_t*
                 }
             }
             // queue the next chunk (while the last QK MFMAs drain)
-            if (it + 1 < nchunks) issue_chunk(it + 1);
+            if (it + 1 < nchunks) issue_chunk(c0 + it + 1);
             if (it < 0) continue;
 
             // Softmax of head h over the chunk's rows.  Probabilities only
@@ -430,6 +435,22 @@ void sparse_attn_bf16_w32_kernel(const uint16_t* __restrict__ q, const uint16_t*
     }
 
     const float inv = (l > 0.f) ? 1.f / l : 0.f;
+    const float lse_row = (l > 0.f) ? (m + log2f(l)) * 0.69314718055994531f : -INFINITY;
+    if (gridDim.z > 1) {
+        // partial (b, row, split z, head h): fp32, normalised by its own sum
+        const int64_t pr = ((int64_t)b * gridDim.x + row) * gridDim.z + blockIdx.z;
+        float* prow = part_o + (pr * H + h) * DV;
+#pragma unroll
+        for (int dt = 0; dt < S::DT; ++dt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int d0 = dt * 32 + 8 * g + 4 * hi;
+                *(v4f*)(prow + d0) = v4f{o[dt][4 * g] * inv, o[dt][4 * g + 1] * inv, o[dt][4 * g + 2] * inv,
+                                         o[dt][4 * g + 3] * inv};
+            }
+        if (hi == 0) part_lse[pr * H + h] = lse_row;
+        return;
+    }
     uint16_t* orow = out + (((int64_t)b * Lq + t) * H + h) * DV;
 #pragma unroll
     for (int dt = 0; dt < S::DT; ++dt)
@@ -441,7 +462,50 @@ void sparse_attn_bf16_w32_kernel(const uint16_t* __restrict__ q, const uint16_t*
             *(u32x2*)(orow + d0) = u32x2{w0, w1};
         }
     if (lse != nullptr && hi == 0)
-        lse[((int64_t)b * Lq + t) * H + h] = (l > 0.f) ? (m + log2f(l)) * 0.69314718055994531f : -INFINITY;
+        lse[((int64_t)b * Lq + t) * H + h] = lse_row;
+}
+
+// Merge of the split partials: per (b, row, head), the log-sum-exp of the
+// parts and the parts' outputs weighted by exp(lse_z - lse), in fp32, then
+// rounded to bf16.  One thread per 4 output values; the parts are summed in
+// split order, so the result is deterministic.
+constexpr int kMergeThreads = 256;
+
+__global__ __launch_bounds__(kMergeThreads)
+void attn_merge_kernel(const float* __restrict__ part_o, const float* __restrict__ part_lse,
+                       uint16_t* __restrict__ out, float* __restrict__ lse, int64_t n_items, int rows, int Lq,
+                       int t_begin, int nsplit, int H, int DV)
+{
+    const int64_t i = (int64_t)blockIdx.x * kMergeThreads + threadIdx.x;
+    if (i >= n_items) return;
+    const int q4 = DV / 4;
+    const int d4 = (int)(i % q4);
+    int64_t rest = i / q4;
+    const int h = (int)(rest % H);
+    rest /= H;
+    const int row = (int)(rest % rows);
+    const int b = (int)(rest / rows);
+    const int64_t pr0 = ((int64_t)b * rows + row) * nsplit;
+    float mx = -INFINITY;
+    for (int z = 0; z < nsplit; ++z) mx = fmaxf(mx, part_lse[(pr0 + z) * H + h]);
+    v4f acc = {0.f, 0.f, 0.f, 0.f};
+    float den = 0.f;
+    if (mx != -INFINITY) {
+        for (int z = 0; z < nsplit; ++z) {
+            const float wz = expf(part_lse[(pr0 + z) * H + h] - mx);
+            const v4f x = *(const v4f*)(part_o + ((pr0 + z) * H + h) * DV + 4 * d4);
+            den += wz;
+            acc[0] = fmaf(wz, x[0], acc[0]);
+            acc[1] = fmaf(wz, x[1], acc[1]);
+            acc[2] = fmaf(wz, x[2], acc[2]);
+            acc[3] = fmaf(wz, x[3], acc[3]);
+        }
+        const float inv = 1.f / den;
+        acc[0] *= inv; acc[1] *= inv; acc[2] *= inv; acc[3] *= inv;
+    }
+    const int64_t orow = ((int64_t)b * Lq + t_begin + row) * H + h;
+    *(u32x2*)(out + orow * DV + 4 * d4) = u32x2{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+    if (lse != nullptr && d4 == 0) lse[orow] = (mx != -INFINITY) ? mx + logf(den) : -INFINITY;
 }
 
 // fp32 kernel for small problems: one workgroup per query row; heads in turn.
@@ -531,6 +595,26 @@ hipError_t launch_bf16(const AttnLaunch& a, hipStream_t s)
 
 }  // namespace
 
+int sparse_attn_split(int64_t rows, int H, int Dqk, int Dv, int k, bool bf16)
+{
+    // the 32-head kernel over few query rows: split each row's selected set
+    // so that about 256 workgroups run, at least 4 chunks of 32 rows each
+    if (!bf16 || (H != 32 && H != 64 && H != 128) || Dqk != 576 || Dv != 512 || k > 2048 || rows <= 0 ||
+        rows >= 128)
+        return 1;
+    const int nch = (k + 31) / 32;
+    int ns = (int)((256 + rows - 1) / rows);
+    ns = ns < 8 ? ns : 8;
+    ns = ns < nch / 4 ? ns : nch / 4;
+    return ns > 1 ? ns : 1;
+}
+
+size_t sparse_attn_split_bytes(int64_t rows, int H, int Dv, int nsplit)
+{
+    if (nsplit <= 1) return 0;
+    return (size_t)rows * nsplit * H * (Dv + 1) * sizeof(float);
+}
+
 bool sparse_attn_bf16_supported(int Dqk, int Dv)
 {
     return (Dqk == 576 && Dv == 512) || (Dqk == 128 && Dv == 128) || (Dqk == 64 && Dv == 64);
@@ -540,9 +624,21 @@ template <int DQK, int DV, int NW>
 hipError_t launch_bf16_w32(const AttnLaunch& a, hipStream_t s)
 {
     const float scale_log2 = a.scale * 1.4426950408889634f;
-    hipLaunchKernelGGL((sparse_attn_bf16_w32_kernel<DQK, DV, NW>), dim3(a.t_count, a.B), dim3(64 * NW), 0, s,
+    const int ns = (a.nsplit > 1 && a.part != nullptr) ? a.nsplit : 1;
+    const int nch = (a.k + 31) / 32;
+    const int cps = (nch + ns - 1) / ns;
+    float* part_o = a.part;
+    float* part_lse = ns > 1 ? a.part + (size_t)a.B * a.t_count * ns * a.H * DV : nullptr;
+    hipLaunchKernelGGL((sparse_attn_bf16_w32_kernel<DQK, DV, NW>), dim3(a.t_count, a.B, ns), dim3(64 * NW), 0, s,
                        (const uint16_t*)a.q, (const uint16_t*)a.kv, a.idx, (uint16_t*)a.out, a.lse,
-                       a.Lq, a.Lk, a.t_begin, a.H, a.k, a.idx_bstride, scale_log2);
+                       a.Lq, a.Lk, a.t_begin, a.H, a.k, a.idx_bstride, scale_log2, cps, part_o, part_lse);
+    if (ns == 1) return hipGetLastError();
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t n_items = (int64_t)a.B * a.t_count * a.H * (DV / 4);
+    hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)((n_items + kMergeThreads - 1) / kMergeThreads)),
+                       dim3(kMergeThreads), 0, s, part_o, part_lse, (uint16_t*)a.out, a.lse, n_items, a.t_count,
+                       a.Lq, a.t_begin, ns, a.H, DV);
     return hipGetLastError();
 }
 

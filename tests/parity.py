@@ -116,6 +116,7 @@ def check_attention(gpu_out: np.ndarray, ref_out: np.ndarray, gpu_lse, ref_lse, 
     if gpu_lse is not None:
         gl = gpu_lse.astype(np.float64)
         both_inf = np.isneginf(gl) & np.isneginf(ref_lse)
-        le = np.where(both_inf, 0.0, np.abs(gl - ref_lse))
+        with np.errstate(invalid="ignore"):
+            le = np.where(both_inf, 0.0, np.abs(gl - ref_lse))
         assert np.all(le <= 2e-3), f"lse max err {le.max():.4g}"
     return float(err.max()) if err.size else 0.0

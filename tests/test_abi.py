@@ -90,7 +90,7 @@ def attn(L, **kw):
              k=4, scale=0.1, dt=BF16)
     a.update(kw)
     return L.dsa_sparse_attn(a["q"], a["kv"], a["idx"], a["out"], a["lse"], a["B"], a["Lq"], a["Lk"],
-                             a["q0"], a["H"], a["dqk"], a["dv"], a["k"], a["scale"], a["dt"], None)
+                             a["q0"], a["H"], a["dqk"], a["dv"], a["k"], a["scale"], a["dt"], None, 0, None)
 
 
 def test_attention_validation(L):
@@ -109,13 +109,30 @@ def test_attention_validation(L):
     assert attn(L, B=0) == OK
 
 
+def test_attention_split_workspace(L):
+    ws = L.dsa_sparse_attn_workspace_size
+    part = lambda rows, ns, H=128, dv=512: rows * ns * H * (dv + 1) * 4
+    assert ws(64, 1, 128, 576, 512, 2048, BF16) == part(64, 4)        # decode batch: 4 splits
+    assert ws(1, 8, 128, 576, 512, 2048, BF16) == part(8, 8)          # at most 8 splits
+    assert ws(1, 8, 32, 576, 512, 2048, BF16) == part(8, 8, H=32)
+    assert ws(1, 8, 128, 576, 512, 256, BF16) == part(8, 2)           # at least 4 chunks of 32 per split
+    assert ws(1, 128, 128, 576, 512, 2048, BF16) == 0                 # enough rows: no split
+    assert ws(1, 8, 128, 576, 512, 64, BF16) == 0
+    assert ws(1, 8, 128, 576, 512, 2048, F32) == 0
+    assert ws(1, 8, 16, 576, 512, 2048, BF16) == 0
+    assert ws(1, 8, 96, 576, 512, 2048, BF16) == 0
+    assert ws(1, 8, 128, 128, 128, 2048, BF16) == 0
+    assert ws(0, 8, 128, 576, 512, 2048, BF16) == 0
+
+
 def test_forward_workspace(L):
-    ws = L.dsa_forward_workspace_size
+    ws = lambda B, Lq, Lk, k, T: L.dsa_forward_workspace_size(B, Lq, Lk, k, 128, 576, 512, BF16, T)
     assert ws(1, 32768, 32768, 2048, 0) == 32768 * 32768 * 4 + 32768 * 2048 * 4
     assert ws(1, 131072, 131072, 2048, 4096) == 4096 * 131072 * 4 + 4096 * 2048 * 4
     # auto tile caps the score tile at 4 GiB
     assert ws(1, 131072, 131072, 2048, 0) == 8192 * 131072 * 4 + 8192 * 2048 * 4
-    assert ws(64, 1, 65536, 2048, 0) == 64 * 65536 * 4 + 64 * 2048 * 4
+    # decode batch: scores, indices and the attention's split partials (4 splits)
+    assert ws(64, 1, 65536, 2048, 0) == 64 * 65536 * 4 + 64 * 2048 * 4 + 64 * 4 * 128 * 513 * 4
     assert ws(0, 1, 1, 1, 0) == 0
     need = ws(1, 8, 8, 4, 0)
 

@@ -337,6 +337,35 @@ def test_attention_crafted_sets(dsa, H, dqk, dv, k):
     assert torch.equal(single, row.expand_as(single)), "a one-row set must return that row exactly"
 
 
+def test_attention_split_matches_unsplit_and_oracle(dsa):
+    """Few query rows (decode): the selected set split over workgroups and
+    merged by log-sum-exp gives the unsplit result to within fp32 rounding
+    (before the bf16 rounding of out), and the oracle's to the usual bar.
+    Short and empty sets leave some splits without rows."""
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(13)
+    B, Lq, Lk, H, k = 4, 3, 5000, 128, 2048
+    assert dsa.dsa_sparse_attn_workspace_size(B, Lq, H, 576, 512, k) > 0
+    q = torch.randn(B, Lq, H, 576, device=dev, generator=g).to(torch.bfloat16)
+    kv = torch.randn(B, Lk, 576, device=dev, generator=g).to(torch.bfloat16)
+    idx = torch.randint(0, Lk, (B, Lq, k), device=dev, generator=g, dtype=torch.int32)
+    idx[0, 0, 100:] = -1                       # one chunk of rows: the other splits are empty
+    idx[1, 2, :] = -1                          # empty set
+    idx[2, 1, 1500:] = -1                      # the last split partly empty
+    out_s, lse_s = dsa.dsa_sparse_attn(q, kv, idx, 512, 192 ** -0.5, q_pos0=Lk - Lq)
+    out_u, lse_u = dsa.dsa_sparse_attn(q, kv, idx, 512, 192 ** -0.5, q_pos0=Lk - Lq, split=False)
+    torch.cuda.synchronize()
+    du = (out_s.float() - out_u.float()).abs()
+    assert float(du.max()) <= 2.0 ** -7 * float(out_u.float().abs().max()), "split and unsplit outputs differ"
+    fin = torch.isfinite(lse_u)
+    assert torch.equal(fin, torch.isfinite(lse_s))
+    assert float((lse_s[fin] - lse_u[fin]).abs().max()) <= 1e-5
+    assert torch.all(out_s[1, 2] == 0) and torch.all(torch.isneginf(lse_s[1, 2]))
+    for b in range(B):
+        o_ref, l_ref = oracle.sparse_attn(q[b].cpu(), kv[b].cpu(), idx[b].cpu().numpy(), 512, 192 ** -0.5, BF16)
+        check_attention(out_s[b].float().cpu().numpy(), o_ref, lse_s[b].cpu().numpy(), l_ref, True)
+
+
 def test_attention_fp32_crafted(dsa):
     dev = torch.device("cuda:0")
     g = torch.Generator(device=dev).manual_seed(5)
