@@ -57,6 +57,10 @@ def lib():
         L.orc_quantize_e4m3.restype = i32
         L.orc_rope_rows.argtypes = [vp, vp, i64, i32, i32, i32, vp, dp, vp]
         L.orc_rope_rows.restype = i32
+        L.orc_kv_pack_fp8.argtypes = [vp, i64, vp]
+        L.orc_kv_pack_fp8.restype = i32
+        L.orc_kv_unpack_fp8.argtypes = [vp, i64, vp]
+        L.orc_kv_unpack_fp8.restype = i32
         L.orc_num_threads.argtypes = []
         L.orc_num_threads.restype = i32
         _lib = L
@@ -226,6 +230,39 @@ def rope_rows(nope, rope, pos, base: float = 10000.0) -> np.ndarray:
     if rc != 0:
         raise ValueError("orc_rope_rows: bad arguments")
     return out
+
+
+KV_FP8_ROW_BYTES = 656
+
+
+def kv_pack_fp8(kv) -> np.ndarray:
+    """Packed FP8 rows [..., 656] uint8 of bf16 latent rows [..., 576]."""
+    a = _np(kv).view(np.uint16)
+    assert a.shape[-1] == 576
+    n = int(a.size // 576)
+    out = np.empty(a.shape[:-1] + (KV_FP8_ROW_BYTES,), dtype=np.uint8)
+    if lib().orc_kv_pack_fp8(_ptr(a), n, _ptr(out)) != 0:
+        raise ValueError("orc_kv_pack_fp8: bad arguments")
+    return out
+
+
+def kv_unpack_fp8(packed) -> np.ndarray:
+    """The fp32 values [..., 576] that packed FP8 rows [..., 656] stand for."""
+    a = _np(packed).view(np.uint8)
+    assert a.shape[-1] == KV_FP8_ROW_BYTES
+    n = int(a.size // KV_FP8_ROW_BYTES)
+    out = np.empty(a.shape[:-1] + (576,), dtype=np.float32)
+    if lib().orc_kv_unpack_fp8(_ptr(a), n, _ptr(out)) != 0:
+        raise ValueError("orc_kv_unpack_fp8: bad arguments")
+    return out
+
+
+def sparse_attn_fp8kv(q, packed, idx, d_v: int, scale: float) -> Tuple[np.ndarray, np.ndarray]:
+    """Attention over packed FP8 latent rows: the rows' fp32 values (exact)
+    and the bf16 queries widened to fp32 (exact), then ``sparse_attn``."""
+    kvf = kv_unpack_fp8(packed)
+    qf = _np(q).view(np.uint16).astype(np.uint32) << 16
+    return sparse_attn(qf.view(np.float32), kvf, idx, d_v, scale, F32)
 
 
 def forward_rows(inp: dict, cfg, rows, with_scores: bool = False):

@@ -20,7 +20,9 @@
  *  - on the input side, per-token FP8 e4m3 quantisation (nearest code by
  *    exhaustive search, scale and division in fp32, the precision the codes
  *    are decided in) and the assembly of a row from its compressed part and
- *    its rotary part (section 1.1 of the same page).
+ *    its rotary part (section 1.1 of the same page);
+ *  - the 656-byte FP8 form of a latent row (per-128-column power-of-two block
+ *    scales) and the exact values it stands for.
  *
  * Inputs are the same bytes the GPU consumes.  FP8 e4m3fn codes are decoded
  * with a table built here from the OCP E4M3 definition (1 sign bit, 4 exponent
@@ -387,6 +389,82 @@ int orc_rope_rows(const uint16_t* nope, const uint16_t* rope, int64_t n_tok, int
                 o[d_nope + 2 * p] = x0 * cos(a) - x1 * sin(a);
                 o[d_nope + 2 * p + 1] = x0 * sin(a) + x1 * cos(a);
             }
+        }
+    }
+    return 0;
+}
+
+/*
+ * FP8 latent rows (NEXT row of the path: the cache at half the bytes;
+ * "DeepSeek模型架构创新解析" section 2.3 gives FP8 storage with a scale
+ * calibrated per block).  A 576-wide bf16 row becomes 656 bytes:
+ *   [0, 512)    e4m3 codes of dims 0..511
+ *   [512, 528)  four fp32 block scales, dims 128g .. 128g + 127
+ *   [528, 656)  dims 512..575 (the rotary part) as the original bf16
+ * Block scale: t = fp32(amax / 448); scale = the smallest power of two >= t
+ * (1 when amax == 0); code = e4m3(clamp(fp32(x / scale), -448, 448)).  With a
+ * power-of-two scale, code * scale is exact in bf16 and fp32.
+ */
+static float pow2_ceil(float t)
+{
+    int e;
+    float f = frexpf(t, &e);                         /* t = f * 2^e, f in [0.5, 1) */
+    return (f == 0.5f) ? t : ldexpf(1.0f, e);
+}
+
+int orc_kv_pack_fp8(const uint16_t* kv, int64_t n_tok, uint8_t* out)
+{
+    if (n_tok < 0)
+        return -1;
+    e4m3_table_init();
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n_tok; ++i) {
+        const uint16_t* row = kv + i * 576;
+        uint8_t* o = out + i * 656;
+        for (int g = 0; g < 4; ++g) {
+            float amax = 0.0f;
+            for (int d = 128 * g; d < 128 * g + 128; ++d) {
+                float a = fabsf(bf16_to_float(row[d]));
+                if (a > amax) amax = a;
+            }
+            float scale = 1.0f;
+            if (amax > 0.0f) {
+                float t = amax / 448.0f;
+                scale = pow2_ceil(t);
+            }
+            memcpy(o + 512 + 4 * g, &scale, 4);
+            for (int d = 128 * g; d < 128 * g + 128; ++d) {
+                float y = bf16_to_float(row[d]) / scale;
+                if (y > 448.0f) y = 448.0f;
+                if (y < -448.0f) y = -448.0f;
+                o[d] = (uint8_t)orc_e4m3_encode(y);
+            }
+        }
+        memcpy(o + 528, row + 512, 128);
+    }
+    return 0;
+}
+
+/* The 576 fp32 values a packed row stands for: code * scale, then the bf16 tail. */
+int orc_kv_unpack_fp8(const uint8_t* packed, int64_t n_tok, float* out)
+{
+    if (n_tok < 0)
+        return -1;
+    e4m3_table_init();
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n_tok; ++i) {
+        const uint8_t* p = packed + i * 656;
+        float* o = out + i * 576;
+        for (int g = 0; g < 4; ++g) {
+            float scale;
+            memcpy(&scale, p + 512 + 4 * g, 4);
+            for (int d = 128 * g; d < 128 * g + 128; ++d)
+                o[d] = g_e4m3[p[d]] * scale;
+        }
+        for (int d = 0; d < 64; ++d) {
+            uint16_t h;
+            memcpy(&h, p + 528 + 2 * d, 2);
+            o[512 + d] = bf16_to_float(h);
         }
     }
     return 0;

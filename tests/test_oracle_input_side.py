@@ -175,3 +175,69 @@ def test_rope_rows_angles_add():
     ph = np.exp(1j * s[:, None] * theta[None, :])[:, None, :]
     c = (first[..., 0] + 1j * first[..., 1]) * ph
     np.testing.assert_allclose(np.stack([c.real, c.imag], -1).reshape(3, 2, 8), both, rtol=0, atol=1e-10)
+
+
+# ---------------------------------------------------------------- FP8 latent rows (656-byte packed form)
+
+def _blocks(packed):
+    codes = packed[..., :512].reshape(*packed.shape[:-1], 4, 128)
+    scales = np.ascontiguousarray(packed[..., 512:528]).view(np.float32)
+    return codes, scales
+
+
+def test_kv_pack_scales_are_powers_of_two_covering_amax():
+    kv = torch.from_numpy((rng.standard_normal((40, 576)) * np.exp(rng.standard_normal((40, 1)) * 3))
+                          .astype(np.float32)).to(torch.bfloat16)
+    packed = oracle.kv_pack_fp8(kv)
+    codes, scales = _blocks(packed)
+    amax = kv.float().numpy()[:, :512].reshape(40, 4, 128).__abs__().max(axis=2)
+    mant, _ = np.frexp(scales)
+    assert np.all(mant == 0.5), "block scales must be powers of two"
+    t = (amax.astype(np.float32) / np.float32(448.0))
+    assert np.all(scales >= t) and np.all(scales < 2 * t)
+    # codes are torch's e4m3 cast of x / scale, block by block
+    x = kv.float().numpy()[:, :512].reshape(40, 4, 128)
+    ref = _torch_e4m3(np.clip(x / scales[:, :, None], -448, 448))
+    assert np.array_equal(codes, ref)
+    # the rotary part is the original bf16, bit for bit
+    assert np.array_equal(packed[:, 528:].view(np.uint16), kv.view(torch.int16).numpy()[:, 512:].view(np.uint16))
+
+
+def test_kv_pack_round_trip_bounds_and_exact_cases():
+    kv = torch.from_numpy(rng.standard_normal((30, 576)).astype(np.float32)).to(torch.bfloat16)
+    kv[3, 128:256] = 0                                     # an all-zero block
+    packed = oracle.kv_pack_fp8(kv)
+    codes, scales = _blocks(packed)
+    assert scales[3, 1] == 1.0 and np.all(codes[3, 1] == 0)
+    u = oracle.kv_unpack_fp8(packed)
+    x = kv.float().numpy()
+    step = np.repeat(scales, 128, axis=1)
+    err = np.abs(u[:, :512] - x[:, :512])
+    assert np.all(err <= np.abs(x[:, :512]) * 2.0 ** -4 + step * 2.0 ** -10)
+    assert np.array_equal(u[:, 512:], x[:, 512:])
+    # rows that are already e4m3 codes times a power of two (with the block
+    # maximum 448 present) come back exactly
+    c = rng.integers(0, 0x7F, (5, 512)).astype(np.uint8)
+    c[:, ::128] = 0x7E
+    vals = oracle.e4m3_table()[c] * np.float32(2.0 ** -3)
+    tail = _bf16(rng.standard_normal((5, 64))).float().numpy()
+    row = np.concatenate([vals, tail], axis=1)
+    rb = torch.from_numpy(row).to(torch.bfloat16)
+    assert np.array_equal(rb.float().numpy(), row)          # exact in bf16
+    pk = oracle.kv_pack_fp8(rb)
+    assert np.all(_blocks(pk)[1] == 0.125)
+    assert np.array_equal(oracle.kv_unpack_fp8(pk), row)
+
+
+def test_fp8kv_attention_equals_bf16_attention_on_representable_rows():
+    c = rng.integers(0, 0xFF, (60, 512)).astype(np.uint8)
+    c[(c & 0x7F) == 0x7F] = 0x10
+    c[:, ::128] = 0x7E
+    vals = oracle.e4m3_table()[c] * np.float32(2.0 ** -6)
+    rows = np.concatenate([vals, rng.standard_normal((60, 64)).astype(np.float32)], axis=1)
+    kv = torch.from_numpy(rows).to(torch.bfloat16)
+    q = torch.from_numpy(rng.standard_normal((4, 8, 576)).astype(np.float32)).to(torch.bfloat16)
+    idx = rng.integers(-1, 60, (4, 20)).astype(np.int32)
+    o1, l1 = oracle.sparse_attn_fp8kv(q, oracle.kv_pack_fp8(kv), idx, 512, 192 ** -0.5)
+    o2, l2 = oracle.sparse_attn(q, kv, idx, 512, 192 ** -0.5, oracle.BF16)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
