@@ -153,6 +153,39 @@ size_t dsa_sparse_attn_workspace_size(int B, int Lq, int n_heads, int d_qk, int 
                                       dsa_dtype io_dtype);
 
 /*
+ * FP8 latent rows (the cache at 656 instead of 1152 bytes per token;
+ * "DeepSeek模型架构创新解析" section 2.3: FP8 storage with a scale calibrated
+ * per block).  Row layout, per token:
+ *   bytes [0, 512)    e4m3 codes of dims 0..511
+ *   bytes [512, 528)  four fp32 scales, scale g for dims 128g .. 128g+127
+ *   bytes [528, 656)  dims 512..575 (the rotary part) as bf16, unchanged
+ * Scale of a block: t = (amax / 448) in fp32, rounded up to a power of two (1
+ * for an all-zero block); codes = e4m3(clamp(x / scale, -448, 448)), round to
+ * nearest even.  Because the scale is a power of two, code * scale is exact in
+ * bf16.
+ *
+ *   kv     [n_tok, 576] bf16 (input)
+ *   kv_fp8 [n_tok, 656] bytes (output)
+ */
+dsa_status dsa_kv_pack_fp8(const void* kv, void* kv_fp8, int64_t n_tok, void* stream);
+
+/*
+ * dsa_sparse_attn over FP8 latent rows: the same computation with key row
+ * [code * scale ; rotary part] (576 wide) and value its first 512 dims, taken
+ * exactly (the kernel widens code * scale to bf16 without rounding).
+ *   q      [B,Lq,n_heads,576] bf16
+ *   kv_fp8 [B,Lk,656] packed rows (dsa_kv_pack_fp8)
+ *   idx, out [B,Lq,n_heads,512] bf16, lse: as for dsa_sparse_attn
+ * Supported: n_heads in {32, 64, 128}, k <= 2048.  The workspace rule is that
+ * of dsa_sparse_attn with d_qk = 576, d_v = 512 (dsa_sparse_attn_workspace_size).
+ */
+dsa_status dsa_sparse_attn_fp8kv(const void* q, const void* kv_fp8, const int32_t* idx,
+                                 void* out, float* lse,
+                                 int B, int Lq, int Lk, int q_pos0, int n_heads, int k,
+                                 float softmax_scale, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
+/*
  * Bytes of device workspace dsa_forward needs for these sizes.  q_tile_rows is
  * the number of query rows (per batch entry) whose scores are held at once;
  * 0 picks Lq, or fewer rows when Lq rows of scores would exceed 4 GiB.  The

@@ -7,6 +7,7 @@ current stream.  The functions carry the C names:
     dsa_indexer_scores, dsa_topk, dsa_sparse_attn,
     dsa_sparse_attn_workspace_size, dsa_forward_workspace_size, dsa_forward,
     dsa_quantize_e4m3, dsa_rope_assemble         (input side)
+    dsa_kv_pack_fp8, dsa_sparse_attn_fp8kv       (FP8 latent rows)
 
 If the built library is missing the import fails loudly; there is no fallback.
 """
@@ -25,7 +26,7 @@ LIB_PATH = os.path.join(_HERE, "libdsa.so")
 DSA_F32, DSA_BF16, DSA_FP8_E4M3 = 0, 1, 2
 EXPORTS = ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_attn", "dsa_sparse_attn_workspace_size",
            "dsa_forward_workspace_size",
-           "dsa_forward", "dsa_quantize_e4m3", "dsa_rope_assemble", "dsa_status_string", "dsa_last_error")
+           "dsa_forward", "dsa_quantize_e4m3", "dsa_rope_assemble", "dsa_kv_pack_fp8", "dsa_sparse_attn_fp8kv", "dsa_status_string", "dsa_last_error")
 
 
 class DSAError(RuntimeError):
@@ -54,8 +55,10 @@ def _load() -> ctypes.CDLL:
     i64, f64 = ctypes.c_int64, ctypes.c_double
     L.dsa_quantize_e4m3.argtypes = [vp, i32, vp, vp, i64, i32, i32, f32, vp]
     L.dsa_rope_assemble.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, f64, vp]
+    L.dsa_kv_pack_fp8.argtypes = [vp, vp, i64, vp]
+    L.dsa_sparse_attn_fp8kv.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, vp, sz, vp]
     for fn in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_attn", "dsa_forward", "dsa_quantize_e4m3",
-               "dsa_rope_assemble"):
+               "dsa_rope_assemble", "dsa_kv_pack_fp8", "dsa_sparse_attn_fp8kv"):
         getattr(L, fn).restype = i32
     L.dsa_status_string.argtypes = [i32]
     L.dsa_status_string.restype = ctypes.c_char_p
@@ -252,3 +255,40 @@ def dsa_rope_assemble(nope: Optional[torch.Tensor], rope: torch.Tensor, pos0: in
     _check("dsa_rope_assemble", lib.dsa_rope_assemble(
         _p(nope), _p(rope), _p(out), B, L, heads, d_nope, d_rope, pos0, float(rope_base), _stream(stream)))
     return out
+
+
+KV_FP8_ROW_BYTES = 656
+
+
+def dsa_kv_pack_fp8(kv: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Packed FP8 latent rows [..., 656] uint8 of bf16 rows kv [..., 576]."""
+    if kv.dtype != torch.bfloat16 or kv.shape[-1] != 576:
+        raise TypeError("kv must be bf16 [..., 576]")
+    n_tok = kv.numel() // 576
+    if out is None:
+        out = torch.empty(tuple(kv.shape[:-1]) + (KV_FP8_ROW_BYTES,), dtype=torch.uint8, device=kv.device)
+    _check("dsa_kv_pack_fp8", lib.dsa_kv_pack_fp8(_p(kv), _p(out), n_tok, _stream(stream)))
+    return out
+
+
+def dsa_sparse_attn_fp8kv(q, kv_fp8, idx, softmax_scale: float, q_pos0: int = 0,
+                          out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                          want_lse: bool = True, workspace: Optional[torch.Tensor] = None, split: bool = True,
+                          stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Attention over packed FP8 latent rows kv_fp8 [B,Lk,656]; q bf16
+    [B,Lq,H,576].  Returns (out [B,Lq,H,512] bf16, lse [B,Lq,H] or None)."""
+    B, Lq, H, _ = q.shape
+    Lk = kv_fp8.shape[1]
+    k = idx.shape[2]
+    if out is None:
+        out = torch.empty((B, Lq, H, 512), dtype=torch.bfloat16, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Lq, H), dtype=torch.float32, device=q.device)
+    if workspace is None and split:
+        nbytes = dsa_sparse_attn_workspace_size(B, Lq, H, 576, 512, k)
+        if nbytes:
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    _check("dsa_sparse_attn_fp8kv", lib.dsa_sparse_attn_fp8kv(
+        _p(q), _p(kv_fp8), _p(idx), _p(out), _p(lse), B, Lq, Lk, q_pos0, H, k, float(softmax_scale),
+        _p(workspace), 0 if workspace is None else workspace.numel(), _stream(stream)))
+    return out, lse

@@ -236,6 +236,49 @@ dsa_status dsa_sparse_attn(const void* q, const void* kv, const int32_t* idx, vo
     return hip_status(fn, dsa::launch_sparse_attn(a, (hipStream_t)stream));
 }
 
+dsa_status dsa_sparse_attn_fp8kv(const void* q, const void* kv_fp8, const int32_t* idx, void* out, float* lse,
+                                 int B, int Lq, int Lk, int q_pos0, int n_heads, int k, float softmax_scale,
+                                 void* workspace, size_t workspace_bytes, void* stream)
+{
+    const char* fn = "dsa_sparse_attn_fp8kv";
+    bool empty = false;
+    dsa_status st = check_positions(fn, B, Lq, Lk, q_pos0, &empty);
+    if (st != DSA_OK || empty) return st == DSA_OK ? ok() : st;
+    REQUIRE_PTR(idx);
+    if (k < 1) return fail(DSA_ERR_SHAPE, "%s: k=%d must be >= 1", fn, k);
+    st = check_attn(fn, q, kv_fp8, out, lse, n_heads, 576, 512, k, softmax_scale, DSA_BF16);
+    if (st != DSA_OK) return st;
+    if (n_heads != 32 && n_heads != 64 && n_heads != 128)
+        return fail(DSA_ERR_UNSUPPORTED, "%s: n_heads must be 32, 64 or 128 (got %d)", fn, n_heads);
+    if (k > 2048) return fail(DSA_ERR_UNSUPPORTED, "%s: k=%d exceeds 2048", fn, k);
+    dsa::AttnLaunch a{};
+    a.q = q; a.kv = kv_fp8; a.idx = idx; a.out = out; a.lse = lse;
+    a.B = B; a.Lq = Lq; a.Lk = Lk; a.t_begin = 0; a.t_count = Lq; a.idx_bstride = (int64_t)Lq * k;
+    a.H = n_heads; a.Dqk = 576; a.Dv = 512; a.k = k; a.scale = softmax_scale;
+    a.bf16 = true; a.kv_fp8 = true;
+    const size_t need = dsa_sparse_attn_workspace_size(B, Lq, n_heads, 576, 512, k, DSA_BF16);
+    if (need > 0 && workspace != nullptr && workspace_bytes >= need) {
+        if (((uintptr_t)workspace & 255u) != 0)
+            return fail(DSA_ERR_ALIGN, "%s: workspace must be 256-byte aligned", fn);
+        a.nsplit = dsa::sparse_attn_split((int64_t)B * Lq, n_heads, 576, 512, k, true);
+        a.part = (float*)workspace;
+    }
+    return hip_status(fn, dsa::launch_sparse_attn(a, (hipStream_t)stream));
+}
+
+dsa_status dsa_kv_pack_fp8(const void* kv, void* kv_fp8, int64_t n_tok, void* stream)
+{
+    const char* fn = "dsa_kv_pack_fp8";
+    if (n_tok < 0) return fail(DSA_ERR_SHAPE, "%s: negative n_tok (%lld)", fn, (long long)n_tok);
+    if (n_tok == 0) return ok();
+    if (n_tok > ((int64_t)1 << 33)) return fail(DSA_ERR_UNSUPPORTED, "%s: n_tok too large", fn);
+    REQUIRE_PTR(kv);
+    REQUIRE_PTR(kv_fp8);
+    dsa::KvPackLaunch a{};
+    a.kv = kv; a.out = kv_fp8; a.n_tok = n_tok;
+    return hip_status(fn, dsa::launch_kv_pack_fp8(a, (hipStream_t)stream));
+}
+
 size_t dsa_forward_workspace_size(int B, int Lq, int Lk, int k, int n_heads, int d_qk, int d_v,
                                   dsa_dtype io_dtype, int q_tile_rows)
 {

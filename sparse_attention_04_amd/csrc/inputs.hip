@@ -1,8 +1,9 @@
 // Input side of the DSA path on gfx950: per-token FP8 e4m3 quantisation of
 // the indexer vectors ("DeepseekV3.2 拆解", section 核心组件: the indexer runs
 // in FP8; "DeepSeek模型架构创新解析" section 4.3: a safety margin on the FP8
-// scale) and the assembly of latent / query rows from their compressed part
-// and their decoupled rotary part (same page, section 1.1).
+// scale), the assembly of latent / query rows from their compressed part and
+// their decoupled rotary part (same page, section 1.1), and the FP8 form of
+// the latent rows with a scale per 128-column block (same page, section 2.3).
 //
 // Both kernels are HBM-bound streaming passes: every input byte is read once
 // and every output byte written once, with 16- or 32-byte accesses per lane.
@@ -146,7 +147,56 @@ void rope_assemble_kernel(const uint16_t* __restrict__ nope, const uint16_t* __r
     }
 }
 
+// FP8 latent rows: one wave per token.  Lane l converts dims 8l..8l+7 of the
+// 512 latent dims; the 16 lanes of each 128-dim block share its amax, whose
+// scale t = amax / 448 (fp32) is rounded up to a power of two, so the codes
+// x / scale come from an exact division.  Lanes 0..7 copy the bf16 rotary
+// part (dims 512..575).
+constexpr int kPackRow = 656;
+
+__global__ __launch_bounds__(256)
+void kv_pack_fp8_kernel(const uint16_t* __restrict__ kv, uint8_t* __restrict__ out, int64_t n_tok)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t tok = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (tok >= n_tok) return;                         // whole waves leave together
+    const uint16_t* row = kv + tok * 576;
+    uint8_t* o = out + tok * kPackRow;
+    const u32x4 u = *(const u32x4*)(row + 8 * lane);
+    float v[8];
+    float amax = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        v[2 * e] = __uint_as_float(u[e] << 16);
+        v[2 * e + 1] = __uint_as_float(u[e] & 0xFFFF0000u);
+        amax = fmaxf(amax, fmaxf(fabsf(v[2 * e]), fabsf(v[2 * e + 1])));
+    }
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, kWave));
+    float scale = 1.f;
+    if (amax > 0.f) {
+        int ex;
+        const float t = amax / kE4m3Max;
+        const float f = frexpf(t, &ex);
+        scale = (f == 0.5f) ? t : ldexpf(1.f, ex);
+    }
+    float y[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = fminf(fmaxf(v[e] / scale, -kE4m3Max), kE4m3Max);
+    *(u32x2*)(o + 8 * lane) = u32x2{cvt_e4m3x4(y[0], y[1], y[2], y[3]), cvt_e4m3x4(y[4], y[5], y[6], y[7])};
+    if ((lane & 15) == 0) *(float*)(o + 512 + 4 * (lane >> 4)) = scale;
+    if (lane < 8) *(u32x4*)(o + 528 + 16 * lane) = *(const u32x4*)(row + 512 + 8 * lane);
+}
+
 }  // namespace
+
+hipError_t launch_kv_pack_fp8(const KvPackLaunch& a, hipStream_t s)
+{
+    if (a.n_tok == 0) return hipSuccess;
+    hipLaunchKernelGGL(kv_pack_fp8_kernel, dim3((unsigned)((a.n_tok + 3) / 4)), dim3(256), 0, s,
+                       (const uint16_t*)a.kv, (uint8_t*)a.out, a.n_tok);
+    return hipGetLastError();
+}
 
 hipError_t launch_quantize_e4m3(const QuantLaunch& a, hipStream_t s)
 {

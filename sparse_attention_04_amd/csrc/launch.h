@@ -44,6 +44,7 @@ struct AttnLaunch {
     int H, Dqk, Dv, k;
     float scale;
     bool bf16;
+    bool kv_fp8;            // kv holds 656-byte FP8 rows (576/512 rows, 32-head kernel only)
     int nsplit;             // > 1: split each row's selected set (32-head kernel only)
     float* part;            // split partials, sparse_attn_split_bytes(B * t_count, H, Dv, nsplit) bytes
 };
@@ -56,6 +57,12 @@ struct QuantLaunch {
     int tok_len, repeat;    // tok_len % 8 == 0, tok_len <= 16384
     float margin;
     bool bf16;
+};
+
+struct KvPackLaunch {
+    const void* kv;         // [n_tok, 576] bf16
+    void* out;              // [n_tok, 656] packed FP8 rows
+    int64_t n_tok;
 };
 
 struct RopeLaunch {
@@ -71,6 +78,7 @@ hipError_t launch_topk(const TopkLaunch& a, hipStream_t s);
 hipError_t launch_sparse_attn(const AttnLaunch& a, hipStream_t s);
 hipError_t launch_quantize_e4m3(const QuantLaunch& a, hipStream_t s);
 hipError_t launch_rope_assemble(const RopeLaunch& a, hipStream_t s);
+hipError_t launch_kv_pack_fp8(const KvPackLaunch& a, hipStream_t s);
 
 // Split factor for the selected set when few query rows are attended (1 = no
 // split), and the bytes of partial results it needs.

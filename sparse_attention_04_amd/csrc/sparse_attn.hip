@@ -221,9 +221,20 @@ __device__ __forceinline__ constexpr int slot_row(int m)
     return (m & 16) | (((m >> 3) & 1) << 1) | ((m >> 2) & 1) | ((m & 3) << 2);
 }
 
-template <int DQK, int DV, int NW>
+// FP8 latent rows (F8 = true): 656 bytes per token -- e4m3 codes of dims
+// 0..511, four fp32 power-of-two scales (one per 128 dims), and dims 512..575
+// in bf16.  The copies land in a staging area (codes, scales, rotary part),
+// and at the top of each chunk the workgroup writes the chunk into the ring
+// in the bf16 layout above: code * scale is exact in bf16 because the scale
+// is a power of two, so the MFMA work that follows is unchanged.
+constexpr int kF8Row = 656;                 // bytes per packed row
+constexpr int kF8Codes = 32 * 512;          // staging: codes of the chunk's 32 rows
+constexpr int kF8Scales = 1024;             // staging: 16 bytes of scales per row (one copy instruction)
+constexpr int kF8Stage = kF8Codes + kF8Scales + 32 * 128;
+
+template <int DQK, int DV, int NW, bool F8, bool SPLIT>
 __global__ __launch_bounds__(64 * NW)
-void sparse_attn_bf16_w32_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
+void sparse_attn_bf16_w32_kernel(const uint16_t* __restrict__ q, const void* __restrict__ kv,
                                  const int32_t* __restrict__ idx, uint16_t* __restrict__ out,
                                  float* __restrict__ lse, int Lq, int Lk, int t_begin, int H, int k,
                                  int64_t idx_bstride, float scale_log2, int cps,
@@ -234,6 +245,7 @@ void sparse_attn_bf16_w32_kernel(const uint16_t* __restrict__ q, const uint16_t*
     __shared__ __attribute__((aligned(16))) uint8_t ring[S::NBUF][S::BUF_BYTES];
     __shared__ __attribute__((aligned(16))) int32_t sel[S::KMAX];   // the query's index list (-1 padded)
     __shared__ int wlast[NW];                                       // per wave: last valid list position
+    __shared__ __attribute__((aligned(16))) uint8_t stg[F8 ? 2 : 1][F8 ? kF8Stage : 16];
 
     const int row = blockIdx.x, b = blockIdx.y;
     const int t = t_begin + row;
@@ -255,7 +267,8 @@ void sparse_attn_bf16_w32_kernel(const uint16_t* __restrict__ q, const uint16_t*
     float m = -INFINITY, l = 0.f;
 
     const int32_t* irow = idx + (int64_t)b * idx_bstride + (int64_t)row * k;
-    const uint16_t* kvb = kv + (int64_t)b * Lk * DQK;
+    const uint16_t* kvb = (const uint16_t*)kv + (F8 ? 0 : (int64_t)b * Lk * DQK);
+    const uint8_t* kv8b = (const uint8_t*)kv + (F8 ? (int64_t)b * Lk * kF8Row : 0);
     // Stage the index list; entries that cannot be read become -1.  Chunks
     // past the last valid entry (a short row's -1 padding) are not visited.
     int last = -1;
@@ -271,6 +284,7 @@ void sparse_attn_bf16_w32_kernel(const uint16_t* __restrict__ q, const uint16_t*
     __syncthreads();
 #pragma unroll
     for (int w = 0; w < NW; ++w) last = max(last, wlast[w]);
+    last = __builtin_amdgcn_readfirstlane(last);                   // workgroup-uniform
     // Split over the selected set (gridDim.z > 1): this workgroup takes chunks
     // [c0, c0 + cps) of the list and leaves a normalised partial output and
     // its log-sum-exp for the merge kernel.
@@ -283,6 +297,30 @@ void sparse_attn_bf16_w32_kernel(const uint16_t* __restrict__ q, const uint16_t*
     // this wave's copies of chunk c: RPW value parts, then its share of tails.
     // Padding entries copy row 0; they are masked in the softmax.
     auto issue_chunk = [&](int c) {
+        if constexpr (F8) {
+            // 21 copy instructions per chunk, instruction i on wave i % NW:
+            // 16 of codes (2 rows each), 1 of scales (rows 0..31, the upper
+            // half of the wave repeats them), 4 of rotary parts (8 rows each)
+            const uint32_t sbase = lds_byte_address(stg[c & 1]);
+#pragma unroll 1
+            for (int i = wave; i < 21; i += NW) {
+                int r, off;
+                if (i < 16) {
+                    r = 2 * i + (lane >> 5);
+                    off = (lane & 31) * 16;
+                } else if (i == 16) {
+                    r = lane & 31;
+                    off = 512;
+                } else {
+                    r = 8 * (i - 17) + (lane >> 3);
+                    off = 528 + (lane & 7) * 16;
+                }
+                const int sr = max(sel[c * NC + r], 0);
+                global_to_lds16_async(kv8b + (int64_t)sr * kF8Row + off,
+                                      __builtin_amdgcn_readfirstlane(sbase + (uint32_t)i * 1024));
+            }
+            return;
+        }
         const int32_t* rr_ = &sel[c * NC];
         int vr[S::RPW];
 #pragma unroll
@@ -325,6 +363,38 @@ void sparse_attn_bf16_w32_kernel(const uint16_t* __restrict__ q, const uint16_t*
             const int c = c0 + (it < 0 ? 0 : it);
             const uint32_t vmask = valid_mask(c);
             const uint8_t* cur = ring[c % S::NBUF];
+            if constexpr (F8) {
+                if (it >= 0) {
+                    // staging -> ring: 8 codes per unit (dims 8j..8j+7 of row r)
+                    const uint8_t* sg = stg[c & 1];
+                    uint8_t* rg = ring[c % S::NBUF];
+#pragma unroll 1
+                    for (int u = tid; u < 32 * 64; u += 64 * NW) {
+                        const int r = u >> 6, j = u & 63;
+                        const u32x2 cw = *(const u32x2*)(sg + r * 512 + 8 * j);
+                        const float sc = *(const float*)(sg + kF8Codes + r * 16 + 4 * (j >> 4));
+                        u32x4 o4;
+#pragma unroll
+                        for (int e = 0; e < 2; ++e) {
+                            const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)cw[e], false);
+                            const f32x2_t hi2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)cw[e], true);
+                            // code * scale is exact with few significant bits: keep the top half
+                            o4[2 * e] = (__float_as_uint(lo[0] * sc) >> 16) | (__float_as_uint(lo[1] * sc) & 0xFFFF0000u);
+                            o4[2 * e + 1] = (__float_as_uint(hi2[0] * sc) >> 16) |
+                                            (__float_as_uint(hi2[1] * sc) & 0xFFFF0000u);
+                        }
+                        *(u32x4*)(rg + r * S::VPITCH + 16 * j) = o4;
+                    }
+                    // rotary parts: piece p of row r to its swizzled tail position
+#pragma unroll 1
+                    for (int u = tid; u < 32 * 8; u += 64 * NW) {
+                        const int r = u >> 3, pc = u & 7;
+                        const u32x4 x = *(const u32x4*)(sg + kF8Codes + kF8Scales + r * 128 + pc * 16);
+                        *(u32x4*)(rg + S::VBYTES + (r >> 3) * 1024 + ((r & 7) * 8 + (pc ^ (r & 7))) * 16) = x;
+                    }
+                    __syncthreads();
+                }
+            }
 
             // S^T (32 rows x 32 heads); key fragments read kPre steps ahead.
             // Step c2 < DV/16 reads value-part piece 2*c2 + hi of row
@@ -436,7 +506,7 @@ void sparse_attn_bf16_w32_kernel(const uint16_t* __restrict__ q, const uint16_t*
 
     const float inv = (l > 0.f) ? 1.f / l : 0.f;
     const float lse_row = (l > 0.f) ? (m + log2f(l)) * 0.69314718055994531f : -INFINITY;
-    if (gridDim.z > 1) {
+    if constexpr (SPLIT) {
         // partial (b, row, split z, head h): fp32, normalised by its own sum
         const int64_t pr = ((int64_t)b * gridDim.x + row) * gridDim.z + blockIdx.z;
         float* prow = part_o + (pr * H + h) * DV;
@@ -449,20 +519,20 @@ void sparse_attn_bf16_w32_kernel(const uint16_t* __restrict__ q, const uint16_t*
                                          o[dt][4 * g + 3] * inv};
             }
         if (hi == 0) part_lse[pr * H + h] = lse_row;
-        return;
+    } else {
+        uint16_t* orow = out + (((int64_t)b * Lq + t) * H + h) * DV;
+#pragma unroll
+        for (int dt = 0; dt < S::DT; ++dt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int d0 = dt * 32 + 8 * g + 4 * hi;
+                const uint32_t w0 = pack_bf16x2(o[dt][4 * g] * inv, o[dt][4 * g + 1] * inv);
+                const uint32_t w1 = pack_bf16x2(o[dt][4 * g + 2] * inv, o[dt][4 * g + 3] * inv);
+                *(u32x2*)(orow + d0) = u32x2{w0, w1};
+            }
+        if (lse != nullptr && hi == 0)
+            lse[((int64_t)b * Lq + t) * H + h] = lse_row;
     }
-    uint16_t* orow = out + (((int64_t)b * Lq + t) * H + h) * DV;
-#pragma unroll
-    for (int dt = 0; dt < S::DT; ++dt)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int d0 = dt * 32 + 8 * g + 4 * hi;
-            const uint32_t w0 = pack_bf16x2(o[dt][4 * g] * inv, o[dt][4 * g + 1] * inv);
-            const uint32_t w1 = pack_bf16x2(o[dt][4 * g + 2] * inv, o[dt][4 * g + 3] * inv);
-            *(u32x2*)(orow + d0) = u32x2{w0, w1};
-        }
-    if (lse != nullptr && hi == 0)
-        lse[((int64_t)b * Lq + t) * H + h] = lse_row;
 }
 
 // Merge of the split partials: per (b, row, head), the log-sum-exp of the
@@ -620,7 +690,7 @@ bool sparse_attn_bf16_supported(int Dqk, int Dv)
     return (Dqk == 576 && Dv == 512) || (Dqk == 128 && Dv == 128) || (Dqk == 64 && Dv == 64);
 }
 
-template <int DQK, int DV, int NW>
+template <int DQK, int DV, int NW, bool F8>
 hipError_t launch_bf16_w32(const AttnLaunch& a, hipStream_t s)
 {
     const float scale_log2 = a.scale * 1.4426950408889634f;
@@ -629,10 +699,15 @@ hipError_t launch_bf16_w32(const AttnLaunch& a, hipStream_t s)
     const int cps = (nch + ns - 1) / ns;
     float* part_o = a.part;
     float* part_lse = ns > 1 ? a.part + (size_t)a.B * a.t_count * ns * a.H * DV : nullptr;
-    hipLaunchKernelGGL((sparse_attn_bf16_w32_kernel<DQK, DV, NW>), dim3(a.t_count, a.B, ns), dim3(64 * NW), 0, s,
-                       (const uint16_t*)a.q, (const uint16_t*)a.kv, a.idx, (uint16_t*)a.out, a.lse,
+    if (ns == 1) {
+        hipLaunchKernelGGL((sparse_attn_bf16_w32_kernel<DQK, DV, NW, F8, false>), dim3(a.t_count, a.B, 1),
+                           dim3(64 * NW), 0, s, (const uint16_t*)a.q, a.kv, a.idx, (uint16_t*)a.out, a.lse,
+                           a.Lq, a.Lk, a.t_begin, a.H, a.k, a.idx_bstride, scale_log2, cps, part_o, part_lse);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL((sparse_attn_bf16_w32_kernel<DQK, DV, NW, F8, true>), dim3(a.t_count, a.B, ns), dim3(64 * NW),
+                       0, s, (const uint16_t*)a.q, a.kv, a.idx, (uint16_t*)a.out, a.lse,
                        a.Lq, a.Lk, a.t_begin, a.H, a.k, a.idx_bstride, scale_log2, cps, part_o, part_lse);
-    if (ns == 1) return hipGetLastError();
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t n_items = (int64_t)a.B * a.t_count * a.H * (DV / 4);
@@ -646,10 +721,18 @@ template <int DQK, int DV>
 hipError_t launch_bf16_w32_any(const AttnLaunch& a, hipStream_t s, bool* handled)
 {
     *handled = true;
-    switch (a.H / 32) {
-    case 1: return launch_bf16_w32<DQK, DV, 1>(a, s);
-    case 2: return launch_bf16_w32<DQK, DV, 2>(a, s);
-    case 4: return launch_bf16_w32<DQK, DV, 4>(a, s);
+    if (a.kv_fp8) {
+        switch (a.H / 32) {
+        case 1: return launch_bf16_w32<DQK, DV, 1, true>(a, s);
+        case 2: return launch_bf16_w32<DQK, DV, 2, true>(a, s);
+        case 4: return launch_bf16_w32<DQK, DV, 4, true>(a, s);
+        }
+    } else {
+        switch (a.H / 32) {
+        case 1: return launch_bf16_w32<DQK, DV, 1, false>(a, s);
+        case 2: return launch_bf16_w32<DQK, DV, 2, false>(a, s);
+        case 4: return launch_bf16_w32<DQK, DV, 4, false>(a, s);
+        }
     }
     *handled = false;
     return hipSuccess;
@@ -658,6 +741,14 @@ hipError_t launch_bf16_w32_any(const AttnLaunch& a, hipStream_t s, bool* handled
 hipError_t launch_sparse_attn(const AttnLaunch& a, hipStream_t s)
 {
     if (a.B == 0 || a.t_count == 0) return hipSuccess;
+    if (a.kv_fp8) {
+        // FP8 latent rows: the 32-head kernel only (checked by the caller)
+        bool handled = false;
+        hipError_t e = hipErrorInvalidValue;
+        if (a.bf16 && a.H % 32 == 0 && a.k <= 2048 && a.Dqk == 576 && a.Dv == 512)
+            e = launch_bf16_w32_any<576, 512>(a, s, &handled);
+        return handled ? e : hipErrorInvalidValue;
+    }
     if (a.bf16 && a.H % 32 == 0 && a.k <= 2048) {
         bool handled = false;
         hipError_t e = hipSuccess;

@@ -154,3 +154,78 @@ def test_assembled_rows_feed_the_attention(dsa):
     from tests.parity import check_attention
     o_ref, l_ref = oracle.sparse_attn(q[0].cpu(), kv[0].cpu(), idx[0].cpu().numpy(), 512, 192 ** -0.5, oracle.BF16)
     check_attention(out[0].float().cpu().numpy(), o_ref, lse[0].cpu().numpy(), l_ref, True)
+
+
+# ---------------------------------------------------------------- FP8 latent rows
+
+def test_kv_pack_fp8_matches_oracle(dsa):
+    """Packed rows byte for byte: codes, power-of-two block scales, the bf16
+    rotary part; wide value ranges, an all-zero block, odd row counts."""
+    g = torch.Generator(device=DEV).manual_seed(31)
+    kv = (torch.randn(3, 1001, 576, device=DEV, generator=g) *
+          torch.randn(3, 1001, 1, device=DEV, generator=g).mul(3).exp()).to(torch.bfloat16)
+    kv[0, 5, 128:256] = 0
+    packed = dsa.dsa_kv_pack_fp8(kv)
+    torch.cuda.synchronize()
+    ref = oracle.kv_pack_fp8(kv.cpu())
+    got = packed.cpu().numpy()
+    bad = np.argwhere(got != ref)
+    assert bad.size == 0, f"{len(bad)} bytes differ; first at {bad[0].tolist()}"
+
+
+def _fp8kv_case(dsa, B, Lq, Lk, H, k, seed, short=True):
+    g = torch.Generator(device=DEV).manual_seed(seed)
+    q = torch.randn(B, Lq, H, 576, device=DEV, generator=g).to(torch.bfloat16)
+    kv = torch.randn(B, Lk, 576, device=DEV, generator=g).to(torch.bfloat16)
+    packed = dsa.dsa_kv_pack_fp8(kv)
+    idx = torch.randint(0, Lk, (B, Lq, k), device=DEV, generator=g, dtype=torch.int32)
+    if short:
+        idx[0, 0, k // 3:] = -1                   # short set
+        if Lq > 1:
+            idx[0, 1, :] = -1                     # empty set
+    return q, packed, idx
+
+
+@pytest.mark.parametrize("B,Lq,Lk,H,k", [(2, 3, 3000, 128, 2048), (1, 40, 700, 64, 300), (2, 200, 5000, 32, 512)])
+def test_fp8kv_attention_matches_oracle(dsa, B, Lq, Lk, H, k):
+    """Attention over the packed rows, split (few rows) and unsplit, against
+    the oracle on the same rows' exact values."""
+    from tests.parity import check_attention
+    q, packed, idx = _fp8kv_case(dsa, B, Lq, Lk, H, k, seed=B * 100 + Lq)
+    scale = 192 ** -0.5
+    out, lse = dsa.dsa_sparse_attn_fp8kv(q, packed, idx, scale, q_pos0=Lk - Lq)
+    out_u, lse_u = dsa.dsa_sparse_attn_fp8kv(q, packed, idx, scale, q_pos0=Lk - Lq, split=False)
+    torch.cuda.synchronize()
+    for b in range(B):
+        o_ref, l_ref = oracle.sparse_attn_fp8kv(q[b].cpu(), packed[b].cpu(), idx[b].cpu().numpy(), 512, scale)
+        check_attention(out[b].float().cpu().numpy(), o_ref, lse[b].cpu().numpy(), l_ref, True)
+        check_attention(out_u[b].float().cpu().numpy(), o_ref, lse_u[b].cpu().numpy(), l_ref, True)
+
+
+def test_fp8kv_attention_equals_bf16_attention_on_the_same_values(dsa):
+    """The FP8 path widens code * scale to bf16 exactly: over the unpacked rows
+    (as bf16) the bf16 attention kernel gives the same bits."""
+    q, packed, idx = _fp8kv_case(dsa, 2, 300, 4000, 128, 2048, seed=5, short=False)
+    kv_vals = torch.from_numpy(oracle.kv_unpack_fp8(packed.cpu())).to(torch.bfloat16).to(DEV)
+    out8, lse8 = dsa.dsa_sparse_attn_fp8kv(q, packed, idx, 192 ** -0.5, q_pos0=4000 - 300)
+    out16, lse16 = dsa.dsa_sparse_attn(q, kv_vals, idx, 512, 192 ** -0.5, q_pos0=4000 - 300)
+    torch.cuda.synchronize()
+    assert torch.equal(out8.view(torch.int16), out16.view(torch.int16)) and torch.equal(lse8, lse16)
+
+
+def test_fp8kv_decode_batch_full_size(dsa):
+    """The decode shape (B = 64, cache of 65536, k = 2048) on packed rows, with
+    the split; sampled sequences against the oracle."""
+    from tests.parity import check_attention
+    g = torch.Generator(device=DEV).manual_seed(8)
+    B, Lk, H, k = 64, 65536, 128, 2048
+    kv = torch.randn(B, Lk, 576, device=DEV, generator=g).to(torch.bfloat16)
+    packed = dsa.dsa_kv_pack_fp8(kv)
+    del kv
+    q = torch.randn(B, 1, H, 576, device=DEV, generator=g).to(torch.bfloat16)
+    idx = torch.sort(torch.randint(0, Lk, (B, 1, k), device=DEV, generator=g, dtype=torch.int32), dim=2).values
+    out, lse = dsa.dsa_sparse_attn_fp8kv(q, packed, idx, 192 ** -0.5, q_pos0=Lk - 1)
+    torch.cuda.synchronize()
+    for b in (0, 17, 63):
+        o_ref, l_ref = oracle.sparse_attn_fp8kv(q[b].cpu(), packed[b].cpu(), idx[b].cpu().numpy(), 512, 192 ** -0.5)
+        check_attention(out[b].float().cpu().numpy(), o_ref, lse[b].cpu().numpy(), l_ref, True)
