@@ -61,6 +61,8 @@ def lib():
         L.orc_kv_pack_fp8.restype = i32
         L.orc_kv_unpack_fp8.argtypes = [vp, i64, vp]
         L.orc_kv_unpack_fp8.restype = i32
+        L.orc_indexer_kl.argtypes = [vp, vp, i32, vp, vp, i32, i32, i32, i32, dp, vp]
+        L.orc_indexer_kl.restype = i32
         L.orc_num_threads.argtypes = []
         L.orc_num_threads.restype = i32
         _lib = L
@@ -263,6 +265,30 @@ def sparse_attn_fp8kv(q, packed, idx, d_v: int, scale: float) -> Tuple[np.ndarra
     kvf = kv_unpack_fp8(packed)
     qf = _np(q).view(np.uint16).astype(np.uint32) << 16
     return sparse_attn(qf.view(np.float32), kvf, idx, d_v, scale, F32)
+
+
+def indexer_kl(q, kv, scores, t_pos, scale: float, dtype: int) -> np.ndarray:
+    """KL(p_t || Softmax(I_t)) per row, float64 [n_rows]: p_t = the mean over
+    heads of the dense attention distributions of q [n_rows,H,d_qk] over
+    kv [Lk,d_qk] (rows s <= t_pos), I = scores [n_rows,Lk]."""
+    qq = _np(q)
+    kk = _np(kv)
+    if dtype == BF16:
+        qq = qq.view(np.uint16)
+        kk = kk.view(np.uint16)
+    else:
+        qq = _np(qq, np.float32)
+        kk = _np(kk, np.float32)
+    n_rows, H, d_qk = qq.shape
+    Lk = kk.shape[0]
+    sc = _np(scores, np.float64)
+    assert sc.shape == (n_rows, Lk)
+    tp = _np(t_pos, np.int64)
+    out = np.empty(n_rows, dtype=np.float64)
+    if lib().orc_indexer_kl(_ptr(qq), _ptr(kk), dtype, _ptr(sc), _ptr(tp), n_rows, Lk, H, d_qk, float(scale),
+                            _ptr(out)) != 0:
+        raise ValueError("orc_indexer_kl: bad arguments")
+    return out
 
 
 def forward_rows(inp: dict, cfg, rows, with_scores: bool = False):

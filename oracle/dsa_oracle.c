@@ -22,7 +22,9 @@
  *    are decided in) and the assembly of a row from its compressed part and
  *    its rotary part (section 1.1 of the same page);
  *  - the 656-byte FP8 form of a latent row (per-128-column power-of-two block
- *    scales) and the exact values it stands for.
+ *    scales) and the exact values it stands for;
+ *  - the indexer's distillation loss, KL(dense attention distribution ||
+ *    softmax of the indexer scores) per query row.
  *
  * Inputs are the same bytes the GPU consumes.  FP8 e4m3fn codes are decoded
  * with a table built here from the OCP E4M3 definition (1 sign bit, 4 exponent
@@ -468,6 +470,65 @@ int orc_kv_unpack_fp8(const uint8_t* packed, int64_t n_tok, float* out)
         }
     }
     return 0;
+}
+
+/*
+ * Indexer distillation loss of the dense warm-up ("DeepseekV3.2 拆解", section
+ * 预训练策略, dense warm-up stage): per query row r, KL(p || Softmax(I[r,:]))
+ * over the keys s <= t_pos[r], where p is the dense attention distribution of
+ * the main attention over the same rows, taken as the mean over the H heads
+ * of each head's softmax (the pages leave the head aggregation open):
+ *   z[h][s] = scale * q[r][h][:] . kv[s][0:d_qk]
+ *   p[s]    = (1/H) sum_h exp(z[h][s] - LSE_h(z[h][:]))
+ *   KL[r]   = sum_s p[s] (log p[s] - (I[r][s] - LSE(I[r][:])))   (0 log 0 = 0)
+ * q [n_rows][H][d_qk] and kv [Lk][d_qk] are F32 or BF16 (dtype); scores
+ * [n_rows][Lk] float64.  Returns 0, or -1 on bad arguments.
+ */
+int orc_indexer_kl(const void* q, const void* kv, int dtype, const double* scores,
+                   const int64_t* t_pos, int n_rows, int Lk, int H, int d_qk, double scale,
+                   double* kl)
+{
+    if ((dtype != ORC_F32 && dtype != ORC_BF16) || H < 1 || d_qk < 1)
+        return -1;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(|: bad)
+    for (int r = 0; r < n_rows; ++r) {
+        const int64_t n = t_pos[r] + 1;
+        if (n < 1 || n > Lk) {
+            bad = 1;
+            continue;
+        }
+        double* z = (double*)malloc(sizeof(double) * (size_t)n);
+        double* p = (double*)calloc((size_t)n, sizeof(double));
+        for (int h = 0; h < H; ++h) {
+            const int64_t qoff = ((int64_t)r * H + h) * d_qk;
+            double zmax = -INFINITY;
+            for (int64_t s = 0; s < n; ++s) {
+                double dot = 0.0;
+                for (int d = 0; d < d_qk; ++d)
+                    dot += (double)load_elem(q, dtype, qoff + d) * (double)load_elem(kv, dtype, s * d_qk + d);
+                z[s] = scale * dot;
+                if (z[s] > zmax) zmax = z[s];
+            }
+            double sum = 0.0;
+            for (int64_t s = 0; s < n; ++s) sum += exp(z[s] - zmax);
+            const double lse = zmax + log(sum);
+            for (int64_t s = 0; s < n; ++s) p[s] += exp(z[s] - lse) / (double)H;
+        }
+        const double* I = scores + (int64_t)r * Lk;
+        double imax = -INFINITY;
+        for (int64_t s = 0; s < n; ++s) if (I[s] > imax) imax = I[s];
+        double isum = 0.0;
+        for (int64_t s = 0; s < n; ++s) isum += exp(I[s] - imax);
+        const double lse_i = imax + log(isum);
+        double acc = 0.0;
+        for (int64_t s = 0; s < n; ++s)
+            if (p[s] > 0.0) acc += p[s] * (log(p[s]) - (I[s] - lse_i));
+        kl[r] = acc;
+        free(z);
+        free(p);
+    }
+    return bad ? -1 : 0;
 }
 
 /* Number of threads OpenMP would use for the loops above. */
