@@ -186,6 +186,26 @@ dsa_status dsa_sparse_attn_fp8kv(const void* q, const void* kv_fp8, const int32_
                                  void* stream);
 
 /*
+ * Indexer distillation loss of the dense warm-up ("DeepseekV3.2 拆解", section
+ * 预训练策略: L^I = sum_t KL(p_t || Softmax(I_t))), one value per query row:
+ *
+ *   z[h,s]     = softmax_scale * q[b,t,h,:] . kv[b,s,0:d_qk]
+ *   p[s]       = (1/n_heads) sum_h exp(z[h,s] - LSE_s' z[h,s'])      (dense, s <= t_pos)
+ *   kl[b,t]    = sum_{s <= t_pos} p[s] (log p[s] - (scores[b,t,s] - LSE_s' scores[b,t,s']))
+ *
+ * p is the mean over heads of the main attention's dense distributions (the
+ * pages leave the head aggregation open).  L^I is the sum of kl over rows.
+ *   q      [B,Lq,n_heads,d_qk] bf16;  kv [B,Lk,d_qk] bf16
+ *   scores [B,Lq,Lk] fp32 (as dsa_indexer_scores writes them; s <= t_pos read)
+ *   kl     [B,Lq] fp32 (output)
+ * Accumulation is fp32.  Supported: d_qk = 576, n_heads in {32, 64, 128}.
+ * The work is two dense QK^T products per query row.
+ */
+dsa_status dsa_indexer_kl(const void* q, const void* kv, const float* scores, float* kl,
+                          int B, int Lq, int Lk, int q_pos0, int n_heads, int d_qk,
+                          float softmax_scale, void* stream);
+
+/*
  * Bytes of device workspace dsa_forward needs for these sizes.  q_tile_rows is
  * the number of query rows (per batch entry) whose scores are held at once;
  * 0 picks Lq, or fewer rows when Lq rows of scores would exceed 4 GiB.  The

@@ -8,6 +8,7 @@ current stream.  The functions carry the C names:
     dsa_sparse_attn_workspace_size, dsa_forward_workspace_size, dsa_forward,
     dsa_quantize_e4m3, dsa_rope_assemble         (input side)
     dsa_kv_pack_fp8, dsa_sparse_attn_fp8kv       (FP8 latent rows)
+    dsa_indexer_kl                               (indexer distillation loss)
 
 If the built library is missing the import fails loudly; there is no fallback.
 """
@@ -26,7 +27,8 @@ LIB_PATH = os.path.join(_HERE, "libdsa.so")
 DSA_F32, DSA_BF16, DSA_FP8_E4M3 = 0, 1, 2
 EXPORTS = ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_attn", "dsa_sparse_attn_workspace_size",
            "dsa_forward_workspace_size",
-           "dsa_forward", "dsa_quantize_e4m3", "dsa_rope_assemble", "dsa_kv_pack_fp8", "dsa_sparse_attn_fp8kv", "dsa_status_string", "dsa_last_error")
+           "dsa_forward", "dsa_quantize_e4m3", "dsa_rope_assemble", "dsa_kv_pack_fp8", "dsa_sparse_attn_fp8kv",
+           "dsa_indexer_kl", "dsa_status_string", "dsa_last_error")
 
 
 class DSAError(RuntimeError):
@@ -56,9 +58,10 @@ def _load() -> ctypes.CDLL:
     L.dsa_quantize_e4m3.argtypes = [vp, i32, vp, vp, i64, i32, i32, f32, vp]
     L.dsa_rope_assemble.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, f64, vp]
     L.dsa_kv_pack_fp8.argtypes = [vp, vp, i64, vp]
+    L.dsa_indexer_kl.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, vp]
     L.dsa_sparse_attn_fp8kv.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, vp, sz, vp]
     for fn in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_attn", "dsa_forward", "dsa_quantize_e4m3",
-               "dsa_rope_assemble", "dsa_kv_pack_fp8", "dsa_sparse_attn_fp8kv"):
+               "dsa_rope_assemble", "dsa_kv_pack_fp8", "dsa_sparse_attn_fp8kv", "dsa_indexer_kl"):
         getattr(L, fn).restype = i32
     L.dsa_status_string.argtypes = [i32]
     L.dsa_status_string.restype = ctypes.c_char_p
@@ -292,3 +295,17 @@ def dsa_sparse_attn_fp8kv(q, kv_fp8, idx, softmax_scale: float, q_pos0: int = 0,
         _p(q), _p(kv_fp8), _p(idx), _p(out), _p(lse), B, Lq, Lk, q_pos0, H, k, float(softmax_scale),
         _p(workspace), 0 if workspace is None else workspace.numel(), _stream(stream)))
     return out, lse
+
+
+def dsa_indexer_kl(q, kv, scores, softmax_scale: float, q_pos0: int = 0, kl: Optional[torch.Tensor] = None,
+                   stream=None) -> torch.Tensor:
+    """KL(p_t || Softmax(I_t)) per query row [B,Lq] fp32: p_t the mean over
+    heads of the dense attention distributions of q [B,Lq,H,576] over kv
+    [B,Lk,576] (bf16), I = scores [B,Lq,Lk].  The loss is kl.sum()."""
+    B, Lq, H, Dqk = q.shape
+    Lk = kv.shape[1]
+    if kl is None:
+        kl = torch.empty((B, Lq), dtype=torch.float32, device=q.device)
+    _check("dsa_indexer_kl", lib.dsa_indexer_kl(_p(q), _p(kv), _p(scores), _p(kl), B, Lq, Lk, q_pos0, H, Dqk,
+                                                float(softmax_scale), _stream(stream)))
+    return kl

@@ -24,6 +24,7 @@ SOURCES = [
     ("topk.hip", []),
     ("sparse_attn.hip", []),
     ("inputs.hip", []),
+    ("kl.hip", []),
 ]
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

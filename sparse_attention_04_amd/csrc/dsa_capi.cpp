@@ -266,6 +266,28 @@ dsa_status dsa_sparse_attn_fp8kv(const void* q, const void* kv_fp8, const int32_
     return hip_status(fn, dsa::launch_sparse_attn(a, (hipStream_t)stream));
 }
 
+dsa_status dsa_indexer_kl(const void* q, const void* kv, const float* scores, float* kl, int B, int Lq, int Lk,
+                          int q_pos0, int n_heads, int d_qk, float softmax_scale, void* stream)
+{
+    const char* fn = "dsa_indexer_kl";
+    bool empty = false;
+    dsa_status st = check_positions(fn, B, Lq, Lk, q_pos0, &empty);
+    if (st != DSA_OK || empty) return st == DSA_OK ? ok() : st;
+    REQUIRE_PTR(q);
+    REQUIRE_PTR(kv);
+    REQUIRE_PTR(scores);
+    REQUIRE_PTR(kl);
+    if (d_qk != 576) return fail(DSA_ERR_UNSUPPORTED, "%s: d_qk must be 576 (got %d)", fn, d_qk);
+    if (n_heads != 32 && n_heads != 64 && n_heads != 128)
+        return fail(DSA_ERR_UNSUPPORTED, "%s: n_heads must be 32, 64 or 128 (got %d)", fn, n_heads);
+    if (!(std::isfinite(softmax_scale) && softmax_scale > 0.f))
+        return fail(DSA_ERR_SHAPE, "%s: softmax_scale must be finite and > 0", fn);
+    dsa::KlLaunch a{};
+    a.q = q; a.kv = kv; a.scores = scores; a.kl = kl; a.B = B; a.Lq = Lq; a.Lk = Lk; a.q_pos0 = q_pos0;
+    a.H = n_heads; a.scale = softmax_scale;
+    return hip_status(fn, dsa::launch_indexer_kl(a, (hipStream_t)stream));
+}
+
 dsa_status dsa_kv_pack_fp8(const void* kv, void* kv_fp8, int64_t n_tok, void* stream)
 {
     const char* fn = "dsa_kv_pack_fp8";

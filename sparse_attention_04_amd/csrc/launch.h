@@ -59,6 +59,15 @@ struct QuantLaunch {
     bool bf16;
 };
 
+struct KlLaunch {
+    const void* q;          // [B, Lq, H, 576] bf16
+    const void* kv;         // [B, Lk, 576] bf16
+    const float* scores;    // [B, Lq, Lk] indexer scores (s <= t_pos read)
+    float* kl;              // [B, Lq]
+    int B, Lq, Lk, q_pos0, H;
+    float scale;
+};
+
 struct KvPackLaunch {
     const void* kv;         // [n_tok, 576] bf16
     void* out;              // [n_tok, 656] packed FP8 rows
@@ -79,6 +88,7 @@ hipError_t launch_sparse_attn(const AttnLaunch& a, hipStream_t s);
 hipError_t launch_quantize_e4m3(const QuantLaunch& a, hipStream_t s);
 hipError_t launch_rope_assemble(const RopeLaunch& a, hipStream_t s);
 hipError_t launch_kv_pack_fp8(const KvPackLaunch& a, hipStream_t s);
+hipError_t launch_indexer_kl(const KlLaunch& a, hipStream_t s);
 
 // Split factor for the selected set when few query rows are attended (1 = no
 // split), and the bytes of partial results it needs.
