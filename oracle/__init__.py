@@ -63,6 +63,8 @@ def lib():
         L.orc_kv_unpack_fp8.restype = i32
         L.orc_indexer_kl.argtypes = [vp, vp, i32, vp, vp, i32, i32, i32, i32, dp, vp]
         L.orc_indexer_kl.restype = i32
+        L.orc_sparse_attn_bwd.argtypes = [vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32, dp, vp, vp]
+        L.orc_sparse_attn_bwd.restype = i32
         L.orc_num_threads.argtypes = []
         L.orc_num_threads.restype = i32
         _lib = L
@@ -289,6 +291,26 @@ def indexer_kl(q, kv, scores, t_pos, scale: float, dtype: int) -> np.ndarray:
                             _ptr(out)) != 0:
         raise ValueError("orc_indexer_kl: bad arguments")
     return out
+
+
+def sparse_attn_bwd(q, kv, dout, idx, d_v: int, scale: float, dtype: int) -> Tuple[np.ndarray, np.ndarray]:
+    """(dq [n_rows,H,d_qk], dkv [Lk,d_qk]) float64: gradients of sum(out * dout)
+    for out = sparse_attn(q, kv, idx, d_v, scale) (fp32 or bf16 inputs)."""
+    def prep(x):
+        a = _np(x)
+        return a.view(np.uint16) if dtype == BF16 else _np(a, np.float32)
+    qq, kk, gg = prep(q), prep(kv), prep(dout)
+    ii = _np(idx, np.int32)
+    n_rows, H, d_qk = qq.shape
+    Lk = kk.shape[0]
+    k = ii.shape[1]
+    assert gg.shape == (n_rows, H, d_v)
+    dq = np.empty((n_rows, H, d_qk), dtype=np.float64)
+    dkv = np.empty((Lk, d_qk), dtype=np.float64)
+    if lib().orc_sparse_attn_bwd(_ptr(qq), _ptr(kk), _ptr(gg), dtype, _ptr(ii), n_rows, k, Lk, H, d_qk, int(d_v),
+                                 float(scale), _ptr(dq), _ptr(dkv)) != 0:
+        raise ValueError("orc_sparse_attn_bwd: bad arguments")
+    return dq, dkv
 
 
 def forward_rows(inp: dict, cfg, rows, with_scores: bool = False):

@@ -24,7 +24,9 @@
  *  - the 656-byte FP8 form of a latent row (per-128-column power-of-two block
  *    scales) and the exact values it stands for;
  *  - the indexer's distillation loss, KL(dense attention distribution ||
- *    softmax of the indexer scores) per query row.
+ *    softmax of the indexer scores) per query row;
+ *  - the backward of the sparse attention (gradients of q and of the latent
+ *    rows through the selected sets).
  *
  * Inputs are the same bytes the GPU consumes.  FP8 e4m3fn codes are decoded
  * with a table built here from the OCP E4M3 definition (1 sign bit, 4 exponent
@@ -527,6 +529,85 @@ int orc_indexer_kl(const void* q, const void* kv, int dtype, const double* score
         kl[r] = acc;
         free(z);
         free(p);
+    }
+    return bad ? -1 : 0;
+}
+
+/*
+ * Backward of the sparse attention (the sparse training stage of "DeepseekV3.2
+ * 拆解", section 预训练策略, trains the main model through the selected sets):
+ * for each row r and head h, over the selected entries i (s_i = idx[r][i]
+ * valid, counted once per occurrence),
+ *   z_i  = scale * q[r][h] . kv[s_i][0:d_qk],   p = softmax(z)
+ *   dp_i = dout[r][h] . kv[s_i][0:d_v],         D = sum_i p_i dp_i
+ *   dz_i = p_i (dp_i - D)
+ *   dq[r][h]            = scale * sum_i dz_i kv[s_i][0:d_qk]
+ *   dkv[s_i][0:d_qk]   += scale * dz_i q[r][h]
+ *   dkv[s_i][0:d_v]    += p_i dout[r][h]
+ * q [n_rows][H][d_qk], kv [Lk][d_qk], dout [n_rows][H][d_v] (F32 or BF16);
+ * dq [n_rows][H][d_qk] and dkv [Lk][d_qk] float64 (dkv overwritten).
+ * Rows run in parallel with a private dkv per thread, summed at the end.
+ */
+int orc_sparse_attn_bwd(const void* q, const void* kv, const void* dout, int dtype, const int32_t* idx,
+                        int n_rows, int k, int Lk, int H, int d_qk, int d_v, double scale,
+                        double* dq, double* dkv)
+{
+    if ((dtype != ORC_F32 && dtype != ORC_BF16) || d_v > d_qk)
+        return -1;
+    memset(dkv, 0, sizeof(double) * (size_t)Lk * (size_t)d_qk);
+    int bad = 0;
+#pragma omp parallel reduction(|: bad)
+    {
+        double* my = (double*)calloc((size_t)Lk * (size_t)d_qk, sizeof(double));
+        double* z = (double*)malloc(sizeof(double) * (size_t)(k > 0 ? k : 1));
+        double* dp = (double*)malloc(sizeof(double) * (size_t)(k > 0 ? k : 1));
+        int32_t* rows = (int32_t*)malloc(sizeof(int32_t) * (size_t)(k > 0 ? k : 1));
+#pragma omp for schedule(dynamic, 1)
+        for (int r = 0; r < n_rows; ++r) {
+            int n = 0;
+            for (int i = 0; i < k; ++i) {
+                const int32_t s = idx[(int64_t)r * k + i];
+                if (s >= Lk) bad = 1;
+                if (s >= 0 && s < Lk) rows[n++] = s;
+            }
+            for (int h = 0; h < H; ++h) {
+                const int64_t qo = ((int64_t)r * H + h) * d_qk, go = ((int64_t)r * H + h) * d_v;
+                double* dqh = dq + qo;
+                for (int d = 0; d < d_qk; ++d) dqh[d] = 0.0;
+                if (n == 0) continue;
+                double zmax = -INFINITY;
+                for (int i = 0; i < n; ++i) {
+                    double a = 0.0, g = 0.0;
+                    for (int d = 0; d < d_qk; ++d)
+                        a += (double)load_elem(q, dtype, qo + d) * (double)load_elem(kv, dtype, (int64_t)rows[i] * d_qk + d);
+                    for (int d = 0; d < d_v; ++d)
+                        g += (double)load_elem(dout, dtype, go + d) * (double)load_elem(kv, dtype, (int64_t)rows[i] * d_qk + d);
+                    z[i] = scale * a;
+                    dp[i] = g;
+                    if (z[i] > zmax) zmax = z[i];
+                }
+                double sum = 0.0;
+                for (int i = 0; i < n; ++i) { z[i] = exp(z[i] - zmax); sum += z[i]; }
+                double D = 0.0;
+                for (int i = 0; i < n; ++i) { z[i] /= sum; D += z[i] * dp[i]; }      /* z now holds p */
+                for (int i = 0; i < n; ++i) {
+                    const double dz = z[i] * (dp[i] - D);
+                    const int64_t ko = (int64_t)rows[i] * d_qk;
+                    for (int d = 0; d < d_qk; ++d) {
+                        dqh[d] += scale * dz * (double)load_elem(kv, dtype, ko + d);
+                        my[ko + d] += scale * dz * (double)load_elem(q, dtype, qo + d);
+                    }
+                    for (int d = 0; d < d_v; ++d)
+                        my[ko + d] += z[i] * (double)load_elem(dout, dtype, go + d);
+                }
+            }
+        }
+#pragma omp critical
+        for (int64_t e = 0; e < (int64_t)Lk * d_qk; ++e) dkv[e] += my[e];
+        free(my);
+        free(z);
+        free(dp);
+        free(rows);
     }
     return bad ? -1 : 0;
 }
