@@ -206,6 +206,31 @@ dsa_status dsa_indexer_kl(const void* q, const void* kv, const float* scores, fl
                           float softmax_scale, void* stream);
 
 /*
+ * Backward of dsa_sparse_attn (the sparse training stage of "DeepseekV3.2
+ * 拆解", section 预训练策略, trains the main model through the selected
+ * sets).  Given dout = dL/dout, for each row and head over the selected
+ * entries i (rows s_i, once per occurrence):
+ *   P_i = exp(z_i - lse),  dP_i = dout . kv[s_i][0:d_v],  D = dout . out
+ *   dZ_i = P_i (dP_i - D)
+ *   dq          = softmax_scale * sum_i dZ_i kv[s_i][0:d_qk]
+ *   dkv[s_i]   += softmax_scale * dZ_i q   (all d_qk columns)
+ *   dkv[s_i]   += P_i dout                 (first d_v columns)
+ * out and lse are the forward's outputs for the same inputs.
+ *   q [B,Lq,n_heads,576] bf16; kv [B,Lk,576] bf16; idx [B,Lq,k] int32
+ *   out, dout [B,Lq,n_heads,512] bf16; lse [B,Lq,n_heads] fp32
+ *   dq [B,Lq,n_heads,576] fp32 (output); dkv [B,Lk,576] fp32 (output, overwritten)
+ * P and dZ pass through the workspace in bf16 (the MFMA operand precision);
+ * dkv is accumulated with fp32 atomics, so its last bits vary between runs.
+ * Supported: (d_qk, d_v) = (576, 512), n_heads in {16, 32, 64, 128}, k <= 2048.
+ */
+size_t dsa_sparse_attn_bwd_workspace_size(int B, int Lq, int n_heads, int k);
+
+dsa_status dsa_sparse_attn_bwd(const void* q, const void* kv, const int32_t* idx, const void* out,
+                               const float* lse, const void* dout, float* dq, float* dkv,
+                               int B, int Lq, int Lk, int q_pos0, int n_heads, int d_qk, int d_v, int k,
+                               float softmax_scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Bytes of device workspace dsa_forward needs for these sizes.  q_tile_rows is
  * the number of query rows (per batch entry) whose scores are held at once;
  * 0 picks Lq, or fewer rows when Lq rows of scores would exceed 4 GiB.  The

@@ -9,6 +9,7 @@ current stream.  The functions carry the C names:
     dsa_quantize_e4m3, dsa_rope_assemble         (input side)
     dsa_kv_pack_fp8, dsa_sparse_attn_fp8kv       (FP8 latent rows)
     dsa_indexer_kl                               (indexer distillation loss)
+    dsa_sparse_attn_bwd_workspace_size, dsa_sparse_attn_bwd   (attention backward)
 
 If the built library is missing the import fails loudly; there is no fallback.
 """
@@ -28,7 +29,7 @@ DSA_F32, DSA_BF16, DSA_FP8_E4M3 = 0, 1, 2
 EXPORTS = ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_attn", "dsa_sparse_attn_workspace_size",
            "dsa_forward_workspace_size",
            "dsa_forward", "dsa_quantize_e4m3", "dsa_rope_assemble", "dsa_kv_pack_fp8", "dsa_sparse_attn_fp8kv",
-           "dsa_indexer_kl", "dsa_status_string", "dsa_last_error")
+           "dsa_indexer_kl", "dsa_sparse_attn_bwd_workspace_size", "dsa_sparse_attn_bwd", "dsa_status_string", "dsa_last_error")
 
 
 class DSAError(RuntimeError):
@@ -59,9 +60,14 @@ def _load() -> ctypes.CDLL:
     L.dsa_rope_assemble.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, f64, vp]
     L.dsa_kv_pack_fp8.argtypes = [vp, vp, i64, vp]
     L.dsa_indexer_kl.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, vp]
+    L.dsa_sparse_attn_bwd_workspace_size.argtypes = [i32, i32, i32, i32]
+    L.dsa_sparse_attn_bwd_workspace_size.restype = sz
+    L.dsa_sparse_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, f32,
+                                      vp, sz, vp]
     L.dsa_sparse_attn_fp8kv.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, vp, sz, vp]
     for fn in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_attn", "dsa_forward", "dsa_quantize_e4m3",
-               "dsa_rope_assemble", "dsa_kv_pack_fp8", "dsa_sparse_attn_fp8kv", "dsa_indexer_kl"):
+               "dsa_rope_assemble", "dsa_kv_pack_fp8", "dsa_sparse_attn_fp8kv", "dsa_indexer_kl",
+               "dsa_sparse_attn_bwd"):
         getattr(L, fn).restype = i32
     L.dsa_status_string.argtypes = [i32]
     L.dsa_status_string.restype = ctypes.c_char_p
@@ -309,3 +315,25 @@ def dsa_indexer_kl(q, kv, scores, softmax_scale: float, q_pos0: int = 0, kl: Opt
     _check("dsa_indexer_kl", lib.dsa_indexer_kl(_p(q), _p(kv), _p(scores), _p(kl), B, Lq, Lk, q_pos0, H, Dqk,
                                                 float(softmax_scale), _stream(stream)))
     return kl
+
+
+def dsa_sparse_attn_bwd(q, kv, idx, out, lse, dout, softmax_scale: float, q_pos0: int = 0,
+                        dq: Optional[torch.Tensor] = None, dkv: Optional[torch.Tensor] = None,
+                        workspace: Optional[torch.Tensor] = None, stream=None):
+    """Gradients (dq [B,Lq,H,576] fp32, dkv [B,Lk,576] fp32) of the sparse
+    attention for upstream gradient dout, given the forward's out and lse."""
+    B, Lq, H, Dqk = q.shape
+    Lk = kv.shape[1]
+    k = idx.shape[2]
+    Dv = out.shape[-1]
+    if dq is None:
+        dq = torch.empty((B, Lq, H, Dqk), dtype=torch.float32, device=q.device)
+    if dkv is None:
+        dkv = torch.empty((B, Lk, Dqk), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        n = int(lib.dsa_sparse_attn_bwd_workspace_size(B, Lq, H, k))
+        workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=q.device)
+    _check("dsa_sparse_attn_bwd", lib.dsa_sparse_attn_bwd(
+        _p(q), _p(kv), _p(idx), _p(out), _p(lse), _p(dout), _p(dq), _p(dkv), B, Lq, Lk, q_pos0, H, Dqk, Dv, k,
+        float(softmax_scale), _p(workspace), workspace.numel(), _stream(stream)))
+    return dq, dkv

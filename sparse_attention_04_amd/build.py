@@ -25,6 +25,7 @@ SOURCES = [
     ("sparse_attn.hip", []),
     ("inputs.hip", []),
     ("kl.hip", []),
+    ("attn_bwd.hip", []),
 ]
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

@@ -288,6 +288,46 @@ dsa_status dsa_indexer_kl(const void* q, const void* kv, const float* scores, fl
     return hip_status(fn, dsa::launch_indexer_kl(a, (hipStream_t)stream));
 }
 
+size_t dsa_sparse_attn_bwd_workspace_size(int B, int Lq, int n_heads, int k)
+{
+    if (B <= 0 || Lq <= 0 || n_heads <= 0 || k <= 0) return 0;
+    return round256(dsa::attn_bwd_workspace_bytes(B, Lq, n_heads, k));
+}
+
+dsa_status dsa_sparse_attn_bwd(const void* q, const void* kv, const int32_t* idx, const void* out,
+                               const float* lse, const void* dout, float* dq, float* dkv, int B, int Lq, int Lk,
+                               int q_pos0, int n_heads, int d_qk, int d_v, int k, float softmax_scale,
+                               void* workspace, size_t workspace_bytes, void* stream)
+{
+    const char* fn = "dsa_sparse_attn_bwd";
+    bool empty = false;
+    dsa_status st = check_positions(fn, B, Lq, Lk, q_pos0, &empty);
+    if (st != DSA_OK || empty) return st == DSA_OK ? ok() : st;
+    REQUIRE_PTR(q);
+    REQUIRE_PTR(kv);
+    REQUIRE_PTR(idx);
+    REQUIRE_PTR(out);
+    REQUIRE_PTR(lse);
+    REQUIRE_PTR(dout);
+    REQUIRE_PTR(dq);
+    REQUIRE_PTR(dkv);
+    if (d_qk != 576 || d_v != 512)
+        return fail(DSA_ERR_UNSUPPORTED, "%s: built for (d_qk, d_v) = (576, 512), got (%d, %d)", fn, d_qk, d_v);
+    if (n_heads != 16 && n_heads != 32 && n_heads != 64 && n_heads != 128)
+        return fail(DSA_ERR_UNSUPPORTED, "%s: n_heads must be 16, 32, 64 or 128 (got %d)", fn, n_heads);
+    if (k < 1 || k > 2048) return fail(DSA_ERR_UNSUPPORTED, "%s: k=%d outside [1, 2048]", fn, k);
+    if (!(std::isfinite(softmax_scale) && softmax_scale > 0.f))
+        return fail(DSA_ERR_SHAPE, "%s: softmax_scale must be finite and > 0", fn);
+    const size_t need = dsa_sparse_attn_bwd_workspace_size(B, Lq, n_heads, k);
+    if (workspace == nullptr || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0)
+        return fail(DSA_ERR_WORKSPACE, "%s: workspace needs %zu bytes, 256-byte aligned (got %zu at %p)", fn, need,
+                    workspace_bytes, workspace);
+    dsa::AttnBwdLaunch a{};
+    a.q = q; a.kv = kv; a.idx = idx; a.out = out; a.lse = lse; a.dout = dout; a.dq = dq; a.dkv = dkv;
+    a.workspace = workspace; a.B = B; a.Lq = Lq; a.Lk = Lk; a.H = n_heads; a.k = k; a.scale = softmax_scale;
+    return hip_status(fn, dsa::launch_attn_bwd(a, (hipStream_t)stream));
+}
+
 dsa_status dsa_kv_pack_fp8(const void* kv, void* kv_fp8, int64_t n_tok, void* stream)
 {
     const char* fn = "dsa_kv_pack_fp8";

@@ -59,6 +59,20 @@ struct QuantLaunch {
     bool bf16;
 };
 
+struct AttnBwdLaunch {
+    const void* q;          // [B, Lq, H, 576] bf16
+    const void* kv;         // [B, Lk, 576] bf16
+    const int32_t* idx;     // [B, Lq, k]
+    const void* out;        // [B, Lq, H, 512] bf16 (forward output)
+    const float* lse;       // [B, Lq, H] (forward log-sum-exp, natural log)
+    const void* dout;       // [B, Lq, H, 512] bf16
+    float* dq;              // [B, Lq, H, 576]
+    float* dkv;             // [B, Lk, 576]
+    void* workspace;        // attn_bwd_workspace_bytes(B, Lq, H, k)
+    int B, Lq, Lk, H, k;
+    float scale;
+};
+
 struct KlLaunch {
     const void* q;          // [B, Lq, H, 576] bf16
     const void* kv;         // [B, Lk, 576] bf16
@@ -89,6 +103,8 @@ hipError_t launch_quantize_e4m3(const QuantLaunch& a, hipStream_t s);
 hipError_t launch_rope_assemble(const RopeLaunch& a, hipStream_t s);
 hipError_t launch_kv_pack_fp8(const KvPackLaunch& a, hipStream_t s);
 hipError_t launch_indexer_kl(const KlLaunch& a, hipStream_t s);
+hipError_t launch_attn_bwd(const AttnBwdLaunch& a, hipStream_t s);
+size_t attn_bwd_workspace_bytes(int B, int Lq, int H, int k);
 
 // Split factor for the selected set when few query rows are attended (1 = no
 // split), and the bytes of partial results it needs.
