@@ -10,11 +10,16 @@
 //
 // One workgroup per query row, one wave per 32 heads, the query held in
 // registers as 36 bf16 MFMA operands (v_mfma_f32_32x32x16_bf16, keys as the A
-// operand).  Two sweeps over the row's keys in chunks of 32 rows staged in
-// LDS: the first keeps each head's running maximum and sum (LSE_h), the second
-// recomputes the scores, turns them into per-head probabilities, sums them
-// over the heads through LDS and folds p log p, p I and p into three sums.
-// The work is two QK^T products per query row (no value product).
+// operand).  Two sweeps over the row's keys in chunks of 32 rows: the first
+// keeps each head's running maximum and sum (LSE_h), the second recomputes the
+// scores, turns them into per-head probabilities, sums them over the heads
+// through LDS and folds p log p, p I and p into three sums.  The rows stream
+// through a two-slot LDS ring with asynchronous global -> LDS copies issued one
+// chunk ahead: each row's first 512 columns at a 1040-byte pitch (one copy
+// instruction per row; 16 consecutive rows read at one column cover all banks
+// once), its last 64 columns packed 8 rows per 1 KB with piece p of row r at
+// position p ^ (r % 8).  The work is two QK^T products per query row (no value
+// product).
 #include "hw.h"
 #include "launch.h"
 
@@ -25,7 +30,11 @@ namespace {
 constexpr int kKC = 32;                 // keys per chunk
 constexpr int kQK = 576;                // latent row width (key)
 constexpr int kSteps = kQK / 16;        // MFMA K steps
-constexpr int kKPitch = kQK * 2 + 16;   // staged key row pitch in bytes (conflict-free b128 reads)
+constexpr int kVPitch = 1040;           // bytes per staged row head (first 512 columns + one skew piece)
+constexpr int kVBytes = kKC * kVPitch;
+constexpr int kScoreOff = kVBytes + kKC * 128;  // after the 64-column tails: the chunk's 32 indexer scores
+constexpr int kSlot = kScoreOff + 256;
+constexpr int kRing = 3;                        // slots: copies run two chunks ahead
 
 __device__ __forceinline__ float block_sum(float v, float* red, int nwaves)
 {
@@ -59,11 +68,11 @@ void indexer_kl_kernel(const uint16_t* __restrict__ q, const uint16_t* __restric
 {
     constexpr int H = 32 * NW;
     constexpr int NT = 64 * NW;
-    __shared__ __attribute__((aligned(16))) uint8_t krow[kKC * kKPitch];
+    __shared__ __attribute__((aligned(16))) uint8_t ring[kRing][kSlot];
     __shared__ float E[kKC][H + 1];                  // per key: each head's probability
     __shared__ float red[NW];
 
-    const int t = blockIdx.x, b = blockIdx.y;
+    const int t = Lq - 1 - (int)blockIdx.x, b = blockIdx.y;     // longest rows first
     const int tpos = q_pos0 + t, n = tpos + 1;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -86,33 +95,74 @@ void indexer_kl_kernel(const uint16_t* __restrict__ q, const uint16_t* __restric
     const float lse_i = mi + logf(block_sum(si, red, NW));
 
     const uint16_t* kvb = kv + (int64_t)b * Lk * kQK;
-    // stage keys c0 .. c0+31 (rows past the row's last key repeat it; masked below)
-    auto stage = [&](int c0) {
-        __syncthreads();                                       // previous chunk fully consumed
-        for (int pc = tid; pc < kKC * (kQK / 8); pc += NT) {
-            const int r = pc / (kQK / 8), c = pc - r * (kQK / 8);
-            const int s = min(c0 + r, n - 1);
-            *(u32x4*)(krow + r * kKPitch + c * 16) = *(const u32x4*)(kvb + (int64_t)s * kQK + c * 8);
+    const int nch = (n + kKC - 1) / kKC;
+    // copies of keys c0 .. c0+31 into ring slot `slot` (rows past the row's
+    // last key repeat it; masked below): row e on wave e % NW, tail group ti
+    // (rows 8 ti .. 8 ti + 7) on wave ti % NW
+    auto issue = [&](int c0, int slot) {
+        const uint32_t base = lds_byte_address(ring[slot]);
+        for (int e = wave; e < kKC; e += NW) {
+            const int sr = min(c0 + e, n - 1);
+            global_to_lds16_async(kvb + (int64_t)sr * kQK + lane * 8,
+                                  __builtin_amdgcn_readfirstlane(base + (uint32_t)e * kVPitch));
         }
-        __syncthreads();
+        for (int ti = wave; ti < kKC / 8; ti += NW) {
+            const int r = 8 * ti + (lane >> 3);
+            const int sr = min(c0 + r, n - 1);
+            const int pc = (lane & 7) ^ (r & 7);
+            global_to_lds16_async(kvb + (int64_t)sr * kQK + 512 + pc * 8,
+                                  __builtin_amdgcn_readfirstlane(base + (uint32_t)(kVBytes + ti * 1024)));
+        }
+        // the chunk's indexer scores (wave 0; lanes 32..63 repeat the last)
+        if (wave == 0)
+            global_to_lds4_async(I + min(c0 + lane, n - 1), __builtin_amdgcn_readfirstlane(base + (uint32_t)kScoreOff));
     };
-    // S^T of the chunk for this wave's heads: element v is key c0 + 8 (v / 4) + 4 hi + v % 4
-    auto scores_T = [&]() -> v16f {
+    // copy instructions one wave issues per chunk (vmcnt counts them)
+    // top of chunk ch: its copies landed everywhere (those of ch + 1 may still
+    // be in flight), the slot of ch - 1 is free; then ch + 2 is queued into it
+    auto next_chunk = [&](int ch) {
+        constexpr int kPer = kKC / NW + (kKC / 8 + NW - 1) / NW;
+        if (ch + 1 >= nch) wait_vmcnt0();
+        else if (wave == 0) wait_vmcnt<kPer + 1>();
+        else wait_vmcnt<kPer>();
+        __syncthreads();
+        if (ch + 2 < nch) issue((ch + 2) * kKC, (ch + 2) % kRing);
+    };
+    // S^T of the chunk in slot `slot` for this wave's heads: element v is key
+    // c0 + 8 (v / 4) + 4 hi + v % 4 (the A operand's row is the lane's key)
+    auto scores_T = [&](int slot) -> v16f {
         v16f acc;
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[v] = 0.f;
-        const uint8_t* kr = krow + col * kKPitch + hi * 16;
+        const uint8_t* vr = ring[slot] + col * kVPitch + hi * 16;
+        const uint8_t* tr = ring[slot] + kVBytes + (col >> 3) * 1024 + (col & 7) * 128;
+        auto frag = [&](int c) -> u32x4 {
+            return c < 32 ? *(const u32x4*)(vr + 32 * c) : *(const u32x4*)(tr + (((2 * (c - 32) + hi) ^ (col & 7)) << 4));
+        };
+        // fragments read kPre steps ahead of their MFMA (order pinned: the
+        // compiler would otherwise move each read next to its use)
+        constexpr int kPre = 7;
+        u32x4 kf[kPre + 1];
 #pragma unroll
-        for (int c = 0; c < kSteps; ++c)
-            acc = mfma_bf16_32x32x16(as_bf8(*(const u32x4*)(kr + c * 32)), qf[c], acc);
+        for (int i = 0; i < kPre; ++i) kf[i] = frag(i);
+#pragma unroll
+        for (int c = 0; c < kSteps; ++c) {
+            if (c + kPre < kSteps) kf[(c + kPre) % (kPre + 1)] = frag(c + kPre);
+            acc = mfma_bf16_32x32x16(as_bf8(kf[c % (kPre + 1)]), qf[c], acc);
+            __builtin_amdgcn_sched_barrier(0);
+        }
         return acc;
     };
 
     // pass 1: per-head maximum and sum (log2 domain)
     float m = -INFINITY, l = 0.f;
-    for (int c0 = 0; c0 < n; c0 += kKC) {
-        stage(c0);
-        const v16f st = scores_T();
+    __syncthreads();
+    issue(0, 0);
+    if (nch > 1) issue(kKC, 1);
+    for (int ch = 0; ch < nch; ++ch) {
+        const int c0 = ch * kKC;
+        next_chunk(ch);
+        const v16f st = scores_T(ch % kRing);
         float z[16], cm = -INFINITY;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
@@ -134,9 +184,13 @@ void indexer_kl_kernel(const uint16_t* __restrict__ q, const uint16_t* __restric
     // pass 2: p per key, then the three sums
     float a_plogp = 0.f, a_pI = 0.f, a_p = 0.f;
     constexpr int TPK = NT / kKC;                              // threads per key in the head sum
-    for (int c0 = 0; c0 < n; c0 += kKC) {
-        stage(c0);
-        const v16f st = scores_T();
+    __syncthreads();                                           // pass 1 done with the ring
+    issue(0, 0);
+    if (nch > 1) issue(kKC, 1);
+    for (int ch = 0; ch < nch; ++ch) {
+        const int c0 = ch * kKC;
+        next_chunk(ch);
+        const v16f st = scores_T(ch % kRing);
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
             const int kk = 8 * (v >> 2) + 4 * hi + (v & 3);
@@ -152,7 +206,7 @@ void indexer_kl_kernel(const uint16_t* __restrict__ q, const uint16_t* __restric
         if (part == 0 && s < n) {
             const float p = ph * (1.f / H);
             if (p > 0.f) a_plogp += p * logf(p);
-            a_pI += p * I[s];
+            a_pI += p * *(const float*)(ring[ch % kRing] + kScoreOff + 4 * kk);
             a_p += p;
         }
     }
