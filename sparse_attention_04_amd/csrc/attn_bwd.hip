@@ -12,12 +12,14 @@
 //     of 32 selected rows (staged in LDS, plus a transposed copy) it forms
 //     S^T and dP^T, then P and dZ, and accumulates dq^T = K^T dZ^T in 36
 //     register tiles.  P and dZ are also written (bf16, keys-major) for 2.
-//  2. dkv: one workgroup per (row, 16 of the 34 column tiles of 32: 18 of the
-//     key part, 16 of the value part), one wave per 4 tiles.  The B operands
-//     (q or dO, heads along K) stay in registers for the whole row; per chunk
-//     the 32 x H weights (dZ or P) come through LDS and each 32 x 32 tile is
-//     added to the selected rows with fp32 atomics (so dkv's summation order
-//     varies between runs).
+//  2. dkv: one workgroup per (row, 8 of the 18 column tiles of 32), one wave
+//     per 2 tiles.  A tile of the first 512 columns takes both products,
+//     scale dZ q and P dO, into one accumulator (one atomic per element, not
+//     two); the last 2 tiles take scale dZ q only.  The B operands (q and dO,
+//     heads along K) stay in registers for the whole row; per chunk the 32 x H
+//     weights (P and scale dZ) come through LDS and each 32 x 32 tile is added
+//     to the selected rows with fp32 atomics (so dkv's summation order varies
+//     between runs).
 #include "hw.h"
 #include "launch.h"
 
@@ -141,7 +143,7 @@ void attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
                 const bool ok = rows[16 * j + 4 * g + i] >= 0;
                 const float p = ok ? exp2f(fmaf(st[j][i], scale_log2, -lse2)) : 0.f;
                 pv[4 * j + i] = p;
-                zv[4 * j + i] = p * (dpt[j][i] - Dh);
+                zv[4 * j + i] = p * (dpt[j][i] - Dh) * scale;          // scale dZ, used by dq and dkv
             }
         // dq^T tiles: A = dZ (head col, key slots 8g..8g+7 = keys 4g..4g+3, 16+4g..16+4g+3),
         // B = K^T (same key slots, dim 16 m + col) from the transposed copy
@@ -189,14 +191,14 @@ void attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
     for (int m = 0; m < kBQK / 16; ++m)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            dq[(qrow * H + hb + 4 * g + i) * kBQK + 16 * m + col] = scale * dqa[m][i];
+            dq[(qrow * H + hb + 4 * g + i) * kBQK + 16 * m + col] = dqa[m][i];
 }
 
 // ---------------------------------------------------------------- 2. dkv
 
-constexpr int kTilesPerWave = 4;
-constexpr int kDkvTiles = kBQK / 32 + kBV / 32;                         // 34
-constexpr int kTilesPerGroup = 4 * kTilesPerWave;                       // 16 per workgroup
+constexpr int kTilesPerWave = 2;
+constexpr int kDkvTiles = kBQK / 32;                                    // 18 (16 with a value part)
+constexpr int kTilesPerGroup = 4 * kTilesPerWave;                       // 8 per workgroup
 
 template <int KS>                                                       // K steps of 16 heads (H = 16 KS)
 __global__ __launch_bounds__(256)
@@ -216,27 +218,28 @@ void attn_bwd_dkv_kernel(const uint16_t* __restrict__ q, const int32_t* __restri
     const int tile0 = blockIdx.z * kTilesPerGroup + wave * kTilesPerWave;
     const int ntl = max(0, min(kTilesPerWave, kDkvTiles - tile0));
 
-    // B operands: tile T < 18 is q over dims 32 T..; tile T >= 18 is dO over
-    // dims 32 (T - 18)..; heads 16 st + 8 hs + e along K, dim 32 T' + n along N
-    v8bf bf[kTilesPerWave][KS];
+    // B operands of tile T (dims 32 T + n): q, and for T < 16 also dO; heads
+    // 16 st + 8 hs + e along K
+    v8bf bq[kTilesPerWave][KS], bo[kTilesPerWave][KS];
 #pragma unroll
     for (int j = 0; j < kTilesPerWave; ++j) {
         const int T = tile0 + j;
-        const bool isq = T < kBQK / 32;
-        const uint16_t* base = isq ? q + qrow * H * kBQK + 32 * T + n : dout + qrow * H * kBV + 32 * (T - kBQK / 32) + n;
-        const int pitch = isq ? kBQK : kBV;
+        const bool hasv = T < kBV / 32;
 #pragma unroll
         for (int st = 0; st < KS; ++st) {
-            uint32_t u[4] = {0u, 0u, 0u, 0u};
+            uint32_t uq[4] = {0u, 0u, 0u, 0u}, uo[4] = {0u, 0u, 0u, 0u};
             if (j < ntl) {
 #pragma unroll
                 for (int e = 0; e < 8; e += 2) {
-                    const uint32_t lo = base[(int64_t)(16 * st + 8 * hs + e) * pitch];
-                    const uint32_t hi2 = base[(int64_t)(16 * st + 8 * hs + e + 1) * pitch];
-                    u[e / 2] = lo | (hi2 << 16);
+                    const int64_t h0 = qrow * H + 16 * st + 8 * hs + e;
+                    uq[e / 2] = (uint32_t)q[h0 * kBQK + 32 * T + n] | ((uint32_t)q[(h0 + 1) * kBQK + 32 * T + n] << 16);
+                    if (hasv)
+                        uo[e / 2] = (uint32_t)dout[h0 * kBV + 32 * T + n] |
+                                    ((uint32_t)dout[(h0 + 1) * kBV + 32 * T + n] << 16);
                 }
             }
-            bf[j][st] = as_bf8(u32x4{u[0], u[1], u[2], u[3]});
+            bq[j][st] = as_bf8(u32x4{uq[0], uq[1], uq[2], uq[3]});
+            bo[j][st] = as_bf8(u32x4{uo[0], uo[1], uo[2], uo[3]});
         }
     }
 
@@ -266,20 +269,24 @@ void attn_bwd_dkv_kernel(const uint16_t* __restrict__ q, const int32_t* __restri
         for (int j = 0; j < kTilesPerWave; ++j) {
             if (j >= ntl) break;                                        // wave-uniform
             const int T = tile0 + j;
-            const bool isq = T < kBQK / 32;
-            const uint16_t* wt = W[isq ? 1 : 0] + n * (H + 8) + 8 * hs;
+            const uint16_t* wz = W[1] + n * (H + 8) + 8 * hs;           // scale dZ
+            const uint16_t* wp = W[0] + n * (H + 8) + 8 * hs;           // P
             v16f acc;
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[v] = 0.f;
 #pragma unroll
             for (int st = 0; st < KS; ++st)
-                acc = mfma_bf16_32x32x16(as_bf8(*(const u32x4*)(wt + 16 * st)), bf[j][st], acc);
-            const float mul = isq ? scale : 1.f;
-            const int d = (isq ? 32 * T : 32 * (T - kBQK / 32)) + n;
+                acc = mfma_bf16_32x32x16(as_bf8(*(const u32x4*)(wz + 16 * st)), bq[j][st], acc);
+            if (T < kBV / 32) {
+#pragma unroll
+                for (int st = 0; st < KS; ++st)
+                    acc = mfma_bf16_32x32x16(as_bf8(*(const u32x4*)(wp + 16 * st)), bo[j][st], acc);
+            }
+            const int d = 32 * T + n;
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int s = rows[8 * (v >> 2) + 4 * hs + (v & 3)];
-                if (s >= 0) unsafeAtomicAdd(dkvb + (int64_t)s * kBQK + d, mul * acc[v]);
+                if (s >= 0) unsafeAtomicAdd(dkvb + (int64_t)s * kBQK + d, acc[v]);
             }
         }
     }
