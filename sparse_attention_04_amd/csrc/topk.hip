@@ -12,16 +12,22 @@
 //
 // A first-digit histogram of 1024 evenly spaced sample keys gives a lower bound
 // L that about 2k keys of the row exceed; the keys >= L are copied to an LDS
-// list, and when that list holds at least k and at most kCand keys the radix
-// select runs on the list alone (the k largest keys of the row are all in it);
-// otherwise it runs over the whole row.  Rows of up to 32768 scores are read
-// from memory once (each thread keeps the keys of positions 4096 v + 4 tid + e
-// in registers); longer rows are read again in each pass.  Selected positions are assembled in LDS and
-// written out in one coalesced pass.  The histogram is kept in four copies
-// (lane % 4 picks one) so that lanes hitting the same bin in one atomic
-// instruction mostly hit different LDS words.
+// list, and when that list holds at least k and at most kCand keys the
+// threshold is found on the list alone (the k largest keys of the row are all
+// in it): one histogram over the list's range, then a brute-force rank inside
+// the threshold bin; otherwise the radix select runs over the whole row.  Rows
+// of up to 32768 scores are read from memory once (each thread keeps the keys
+// of positions 4096 v + 4 tid + e in registers, in a kernel instance of its
+// own); longer rows are read again in each pass.  Selected positions are
+// assembled in LDS and written out in one coalesced pass.  The histogram is
+// kept in four copies (lane % 4 picks one) so that lanes hitting the same bin
+// in one atomic instruction mostly hit different LDS words; its bins are
+// scanned by all threads at once.  Stores that only some lanes need go to a
+// per-lane trash word instead of being branched around.
 #include "hw.h"
 #include "launch.h"
+
+#include <algorithm>
 
 namespace dsa {
 
@@ -37,62 +43,64 @@ constexpr int kBins = 2048;
 constexpr int kCand = 6144;        // LDS list of candidate keys
 constexpr int kSelCap = 2048;      // k up to this is assembled in LDS
 
-// Bin totals are stored with one pad word per 32 bins, so lanes reading 32
-// consecutive bins each hit distinct banks.
-__device__ __forceinline__ uint32_t tot_slot(uint32_t bin) { return bin + (bin >> 5); }
-
 struct TopkShared {
     uint32_t hist[kBins * kCopies];   // [bin][copy]
-    uint32_t tot[kBins + kBins / 32];
+    uint32_t wsum[kWaves];            // per-wave totals of a scan
     uint32_t wtot[kNV][kWaves];
     uint32_t cand[kCand];
     int32_t sel[kSelCap];
-    uint32_t bin, above, ncand;
-    uint32_t cmax, nsmall, tkey, tgt;
+    uint32_t trash[kWave];            // target of the stores of lanes with nothing to store
+    uint32_t bin, above, bincnt, ncand;
+    uint32_t cmax, nsmall, tkey, tgt, teq;
 };
 
 // Histogram over nb = 2^kWidth bins of the bins `for_each_bin` yields
 // (fn(bin), bin < nb; larger bins ordered higher); leaves in sh.bin the bin
-// holding the need-th largest entry and in sh.above the number of entries in
-// higher bins.  Requires at least `need` entries.  Every thread calls it; it
-// ends with a barrier.
+// holding the need-th largest entry, in sh.above the number of entries in
+// higher bins and in sh.bincnt the entries in that bin.  Requires at least
+// `need` entries and sh.hist zero on entry (zeroed once at the start of the
+// kernel; the copies are cleared again as they are summed).  Every thread
+// calls it; the callers' writes it depends on must be published by a barrier
+// before; it ends with a barrier.
+//
+// The bins are scanned from the largest down by all threads at once: thread
+// tid owns nb / kT consecutive bins below nb - 1 - (nb / kT) tid, a wave scan
+// orders the threads of a wave, and every wave scans the kWaves wave totals.
 template <int kWidth, typename ForEachBin>
 __device__ __forceinline__ void bin_step(TopkShared& sh, uint32_t need, ForEachBin for_each_bin)
 {
     constexpr uint32_t nb = 1u << kWidth;
-    constexpr uint32_t per = nb / kWave;           // bins per lane in the scan
+    constexpr uint32_t per = nb / kT;              // bins per thread
+    static_assert(per >= 1 && per * kT == nb, "whole bins per thread");
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    for (uint32_t i = tid; i < nb * kCopies; i += kT) sh.hist[i] = 0;
-    __syncthreads();
     const uint32_t copy = (uint32_t)lane & (kCopies - 1);
     for_each_bin([&](uint32_t bin) { atomicAdd(&sh.hist[bin * kCopies + copy], 1u); });
     __syncthreads();
-    for (uint32_t i = tid; i < nb; i += kT) {
-        const u32x4 c = *(const u32x4*)&sh.hist[i * kCopies];
-        sh.tot[tot_slot(i)] = c[0] + c[1] + c[2] + c[3];
+    const uint32_t top = nb - 1 - per * (uint32_t)tid;
+    uint32_t c[per], local = 0;
+#pragma unroll
+    for (uint32_t j = 0; j < per; ++j) {
+        u32x4* h = (u32x4*)&sh.hist[(top - j) * kCopies];
+        const u32x4 x = *h;
+        c[j] = x[0] + x[1] + x[2] + x[3];
+        local += c[j];
+        *h = u32x4{0u, 0u, 0u, 0u};
     }
+    const uint32_t incl = wave_incl_scan(local, lane);
+    if (lane == 63) sh.wsum[wave] = incl;
     __syncthreads();
-    if (wave == 0) {
-        // lane L owns bins [nb - (L+1)*per, nb - L*per): lane 0 the largest
-        const uint32_t lo = nb - (uint32_t)(lane + 1) * per;
-        uint32_t local = 0;
-#pragma unroll 8
-        for (uint32_t i = 0; i < per; ++i) local += sh.tot[tot_slot(lo + i)];
-        const uint32_t incl = wave_incl_scan(local, lane);
-        const uint32_t excl = incl - local;
-        // the lane whose range holds the need-th largest key
-        const uint64_t hit = __ballot(excl < need && need <= incl);
-        const int lt = __ffsll((unsigned long long)hit) - 1;
-        const uint32_t base = __builtin_amdgcn_readlane(excl, lt);
-        const uint32_t lo_t = nb - (uint32_t)(lt + 1) * per;
-        // lanes 0..per-1 take that range's bins from the largest down
-        const uint32_t c = (uint32_t)lane < per ? sh.tot[tot_slot(lo_t + per - 1 - lane)] : 0u;
-        const uint32_t ci = wave_incl_scan(c, lane);
-        const uint64_t hit2 = __ballot((uint32_t)lane < per && base + ci >= need);
-        const int it = __ffsll((unsigned long long)hit2) - 1;
-        if (lane == it) {
-            sh.bin = lo_t + per - 1 - (uint32_t)it;
-            sh.above = base + ci - c;
+    const uint32_t wincl = wave_incl_scan((lane < kWaves) ? sh.wsum[lane] : 0u, lane);
+    const uint32_t wbase = (wave == 0) ? 0u : (uint32_t)__shfl((int)wincl, wave - 1, kWave);
+    uint32_t a = wbase + incl - local;             // entries in the bins above this thread's
+    if (a < need && need <= a + local) {           // exactly one thread
+#pragma unroll
+        for (uint32_t j = 0; j < per; ++j) {
+            if (a < need && need <= a + c[j]) {
+                sh.bin = top - j;
+                sh.above = a;
+                sh.bincnt = c[j];
+            }
+            a += c[j];
         }
     }
     __syncthreads();
@@ -113,7 +121,8 @@ __device__ __forceinline__ void radix_step(TopkShared& sh, int shift, uint32_t p
 
 // Three radix steps (11, 11, 10 bits) over the keys `each` enumerates; returns
 // the need-th largest of them (need = k on entry; on return, the number of
-// keys equal to the result that belong to the top set).
+// keys equal to the result that belong to the top set).  sh.bincnt is left
+// holding the number of keys equal to the result.
 template <typename ForEachKey>
 __device__ __forceinline__ uint32_t radix_select(TopkShared& sh, uint32_t& need, ForEachKey each)
 {
@@ -133,15 +142,20 @@ __device__ __forceinline__ uint32_t radix_select(TopkShared& sh, uint32_t& need,
     return prefix;
 }
 
-// two rows per CU: 8 waves per SIMD (64 VGPRs) and under 80 KB of LDS each
+// Two rows per CU: 8 waves per SIMD (64 VGPRs) and under 80 KB of LDS each.
+// IN_REGS: every row of the launch has 4 <= n <= kRegRow, starts 16-byte
+// aligned and is held in registers (a separate instance, so that the
+// registers of the streaming path do not crowd the 32 register-resident
+// keys).  Block x handles row row0 + x.
+template <bool IN_REGS>
 __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(8)))
 void topk_radix_kernel(const float* __restrict__ scores, int32_t* __restrict__ idx,
-                       int q_pos0, int t_begin, int64_t sc_bstride, int64_t sc_rstride,
+                       int q_pos0, int t_begin, int row0, int64_t sc_bstride, int64_t sc_rstride,
                        int64_t idx_bstride, int k)
 {
     __shared__ TopkShared sh;
 
-    const int row = blockIdx.x, b = blockIdx.y;
+    const int row = row0 + (int)blockIdx.x, b = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int t = t_begin + row;
     const int n = q_pos0 + t + 1;                  // candidates s = 0 .. t_pos
@@ -151,12 +165,28 @@ void topk_radix_kernel(const float* __restrict__ scores, int32_t* __restrict__ i
         return;
     }
     const float* src = scores + (int64_t)b * sc_bstride + (int64_t)row * sc_rstride;
-    const bool in_regs = n <= kRegRow;
-    const bool vec = ((uintptr_t)src & 15u) == 0;
+    constexpr bool in_regs = IN_REGS;
+    const bool vec = IN_REGS || ((uintptr_t)src & 15u) == 0;
     if (tid == 0) {                                // published by the first barrier below
         sh.ncand = 0;
         sh.cmax = 0;
         sh.nsmall = 0;
+    }
+    for (int i = tid; i < kBins * kCopies / 4; i += kT) ((u32x4*)sh.hist)[i] = u32x4{0u, 0u, 0u, 0u};
+
+    // 1. Lower bound from evenly spaced sample keys: about 2k row keys are
+    //    expected at or above the sample's j-th largest key.  A row held in
+    //    registers takes that key's first digit (11 bits) from 1024 samples;
+    //    a longer row, where one first-digit bin holds too many keys for the
+    //    list, takes its first two digits (22 bits) from 2048 samples.
+    const int64_t target = 2 * (int64_t)k;
+    const bool sampled = target < n;
+    const int ns = in_regs ? kT : 2 * kT;
+    uint32_t sraw[2] = {0u, 0u};                   // sample scores, raw bits
+    if (sampled) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+            if (e == 0 || !in_regs) sraw[e] = __float_as_uint(src[(int)(((int64_t)(tid + e * kT) * n) / ns)]);
     }
 
     // keys of positions s0..s0+3 (0 past the row)
@@ -171,12 +201,42 @@ void topk_radix_kernel(const float* __restrict__ scores, int32_t* __restrict__ i
         }
     };
     // Register copy of a row of up to kRegRow: step v holds positions
-    // 4096 v + 4 tid + e.  Steps past the row are skipped (workgroup-uniform).
+    // 4096 v + 4 tid + e (0 past the row; steps past the row are skipped,
+    // workgroup-uniform).  The row is read in aligned groups of 4 without
+    // branches: a group running past the row reads the row's last whole
+    // aligned group instead (its keys are set to 0 when converted), and the
+    // one partial group (n % 4 != 0) is read with scalar loads and patched in.
+    // All loads are issued before the first conversion, so they are in flight
+    // together.
     uint32_t key[kNV][4];
     if (in_regs) {
+        const int last4 = (n - 4) & ~3;            // start of the last whole aligned group
 #pragma unroll
-        for (int v = 0; v < kNV; ++v)
-            if (v * kTile < n) load4(v * kTile + tid * 4, key[v]);
+        for (int v = 0; v < kNV; ++v) {
+            if (v * kTile >= n) break;
+            const u32x4 x = *(const u32x4*)(src + min(v * kTile + tid * 4, last4));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) key[v][e] = x[e];
+        }
+#pragma unroll
+        for (int v = 0; v < kNV; ++v) {
+            if (v * kTile >= n) break;
+            const uint32_t keep = (v * kTile + tid * 4 <= last4) ? ~0u : 0u;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) key[v][e] = score_key(__uint_as_float(key[v][e])) & keep;
+        }
+        const int sp = last4 + 4;                  // the partial group, if any (workgroup-uniform)
+        if (sp < n) {
+            uint32_t px[3];
+#pragma unroll
+            for (int e = 0; e < 3; ++e) px[e] = (sp + e < n) ? score_key(src[sp + e]) : 0u;
+            const bool own = tid == (sp % kTile) / 4;
+#pragma unroll
+            for (int v = 0; v < kNV; ++v)
+                if (v == sp / kTile)
+#pragma unroll
+                    for (int e = 0; e < 3; ++e) key[v][e] = own ? px[e] : key[v][e];
+        }
     }
     // fn(step start s0, keys of s0..s0+3) over the whole row, in ascending steps
     auto for_each_step = [&](auto&& fn) {
@@ -192,21 +252,20 @@ void topk_radix_kernel(const float* __restrict__ scores, int32_t* __restrict__ i
             }
         }
     };
+    __syncthreads();                               // zero histogram and counters published
 
-    // 1. Lower bound from evenly spaced sample keys: about 2k row keys are
-    //    expected at or above the sample's j-th largest key.  A row held in
-    //    registers takes that key's first digit (11 bits) from 1024 samples;
-    //    a longer row, where one first-digit bin holds too many keys for the
-    //    list, takes its first two digits (22 bits) from 2048 samples.
     uint32_t lbound = 0;
-    const int64_t target = 2 * (int64_t)k;
-    if (target < n) {
-        const int ns = in_regs ? kT : 2 * kT;
+    if (sampled) {
         const uint32_t j = (uint32_t)((target * ns + n - 1) / n);      // 1 <= j <= ns
         uint32_t sample[2];
 #pragma unroll
-        for (int e = 0; e < 2; ++e)
-            sample[e] = (e == 0 || !in_regs) ? score_key(src[(int)(((int64_t)(tid + e * kT) * n) / ns)]) : 0u;
+        for (int e = 0; e < 2; ++e) sample[e] = score_key(__uint_as_float(sraw[e]));
+        // the largest sample: the top of the candidate list's histogram range
+        // (published by the barriers below)
+        uint32_t smax = in_regs ? sample[0] : max(sample[0], sample[1]);
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) smax = max(smax, (uint32_t)__shfl_xor((int)smax, o, kWave));
+        if (lane == 0) atomicMax(&sh.cmax, smax);
         auto each_sample = [&](auto&& fn) {
             fn(sample[0]);
             if (!in_regs) fn(sample[1]);
@@ -220,30 +279,81 @@ void topk_radix_kernel(const float* __restrict__ scores, int32_t* __restrict__ i
             radix_step<11>(sh, 10, b1 << 21, 0x7FFu << 21, j - above, each_sample);
             lbound |= sh.bin << 10;
         }
-    } else {
-        __syncthreads();                           // publishes sh.ncand = 0
     }
 
-    // 2. Copy the keys >= lbound to the LDS list: per step one wave scan and one
-    //    atomic per wave.
+    // 2. Copy the keys >= lbound to the LDS list (in any order): one wave scan
+    //    of the per-thread counts and one atomic per wave reserve the wave's
+    //    range (per step, for a row streamed from memory).
     uint32_t cmax = 0;                             // largest key in the list (this thread's part)
-    for_each_step([&](int s0, const uint32_t (&kk)[4]) {
-        uint32_t c = 0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) c += (s0 + e < n) && kk[e] >= lbound;
+    auto append = [&](auto&& each_key, uint32_t c) {
         const uint32_t incl = wave_incl_scan(c, lane);
         uint32_t base = 0;
         if (lane == 63) base = atomicAdd(&sh.ncand, incl);
         base = __builtin_amdgcn_readlane(base, 63) + incl - c;
+        each_key([&](uint32_t key) {
+            if (base < (uint32_t)kCand) sh.cand[base] = key;
+            ++base;
+            cmax = max(cmax, key);
+        });
+    };
+    if (in_regs) {
+        // Positions past the row hold key 0, kept out by lb1 = max(lbound, 1).
+        // A real key 0 (score bits 0xFFFFFFFF, the smallest key) is then left
+        // out too when lbound = 0; it belongs to the top k only if fewer than
+        // k keys are >= 1, i.e. the list is short, which sends the row to the
+        // radix select over the whole row.  Lanes with nothing to store write
+        // to their own trash word, so the stores need no branches.
+        const uint32_t lb1 = max(lbound, 1u);
+        uint32_t c = 0, rmax = 0;
+        if (sampled) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            if ((s0 + e < n) && kk[e] >= lbound) {
-                if (base < (uint32_t)kCand) sh.cand[base] = kk[e];
-                ++base;
-                cmax = max(cmax, kk[e]);
-            }
+            for (int v = 0; v < kNV; ++v)
+                if (v * kTile < n)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) c += key[v][e] >= lb1;
+        } else {
+            // no samples: the list's range ends at the row's largest key
+#pragma unroll
+            for (int v = 0; v < kNV; ++v)
+                if (v * kTile < n)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        c += key[v][e] >= lb1;
+                        rmax = max(rmax, key[v][e]);
+                    }
         }
-    });
+        const uint32_t incl = wave_incl_scan(c, lane);
+        uint32_t base = 0;
+        if (lane == 63) base = atomicAdd(&sh.ncand, incl);
+        const uint32_t wbase = __builtin_amdgcn_readlane(base, 63);
+        base = wbase + incl - c;
+        uint32_t* trash = &sh.trash[lane];
+        auto store = [&](bool guard) {
+#pragma unroll
+            for (int v = 0; v < kNV; ++v)
+                if (v * kTile < n)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const bool pass = key[v][e] >= lb1 && (!guard || base < (uint32_t)kCand);
+                        *(pass ? &sh.cand[base] : trash) = key[v][e];
+                        base += key[v][e] >= lb1;
+                    }
+        };
+        if (wbase + __builtin_amdgcn_readlane(incl, 63) <= (uint32_t)kCand) store(false);   // the wave's range fits
+        else store(true);
+        cmax = rmax;
+    } else {
+        for_each_step([&](int s0, const uint32_t (&kk)[4]) {
+            uint32_t c = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) c += (s0 + e < n) && kk[e] >= lbound;
+            append([&](auto&& put) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if ((s0 + e < n) && kk[e] >= lbound) put(kk[e]);
+            }, c);
+        });
+    }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) cmax = max(cmax, (uint32_t)__shfl_xor((int)cmax, o, kWave));
     if (lane == 0) atomicMax(&sh.cmax, cmax);
@@ -251,30 +361,35 @@ void topk_radix_kernel(const float* __restrict__ scores, int32_t* __restrict__ i
     const uint32_t nc = sh.ncand;
 
     // 3. The k-th largest key T: from the list when it holds the top k (at least
-    //    k keys >= lbound) and fits; otherwise from the whole row.
+    //    k keys >= lbound) and fits; otherwise from the whole row.  Also the
+    //    number eqT of the row's keys equal to T.
     uint32_t need = (uint32_t)k;
-    uint32_t T;
+    uint32_t T, eqT;
     bool done = false;
     if (nc >= (uint32_t)k && nc <= (uint32_t)kCand) {
-        // One histogram of (key - lbound) >> sft, sft chosen so the list's
-        // range [lbound, cmax] spans at most 2048 bins; the threshold bin then
-        // holds few keys, ranked by brute force.
+        // One histogram of (key - lbound) >> sft, sft chosen so that
+        // [lbound, cmax] spans at most 2048 bins (cmax: the largest sample
+        // key, or the row's largest key; keys above cmax share the top bin);
+        // the threshold bin then holds few keys, ranked by brute force.
         const uint32_t lb = lbound, range = sh.cmax - lb;
         const int sft = max(0, (range ? 32 - __clz(range) : 0) - 11);
+        auto lbin = [&](uint32_t key) { return min((key - lb) >> sft, (uint32_t)kBins - 1u); };
         bin_step<11>(sh, need, [&](auto&& fn) {
-            for (uint32_t i = tid; i < nc; i += kT) fn((sh.cand[i] - lb) >> sft);
+            for (uint32_t i = tid; i < nc; i += kT) fn(lbin(sh.cand[i]));
         });
         const uint32_t bstar = sh.bin, above = sh.above;
-        if (sft == 0) {
-            T = lb + bstar;                        // one key value per bin
+        if (sft == 0 && bstar + 1 < (uint32_t)kBins) {
+            T = lb + bstar;                        // one key value per bin (below the top bin)
+            eqT = sh.bincnt;
             need -= above;
             done = true;
         } else {
-            // the threshold bin's keys, in the (now free) histogram storage
-            uint32_t* small = sh.hist;
+            // the threshold bin's keys, in the (still unused) output storage
+            static_assert(kSelCap >= kT, "room for kT keys");
+            uint32_t* small = (uint32_t*)sh.sel;
             for (uint32_t i = tid; i < nc; i += kT) {
                 const uint32_t key = sh.cand[i];
-                if (((key - lb) >> sft) == bstar) {
+                if (lbin(key) == bstar) {
                     const uint32_t pos = atomicAdd(&sh.nsmall, 1u);
                     if (pos < (uint32_t)kT) small[pos] = key;
                 }
@@ -294,10 +409,12 @@ void topk_radix_kernel(const float* __restrict__ scores, int32_t* __restrict__ i
                     if (gt < nb_ && nb_ <= gt + eq) {   // every copy of the key writes the same
                         sh.tkey = x;
                         sh.tgt = gt;
+                        sh.teq = eq;
                     }
                 }
                 __syncthreads();
                 T = sh.tkey;
+                eqT = sh.teq;                      // the bin holds every key equal to T
                 need = nb_ - sh.tgt;
                 done = true;
             }
@@ -306,6 +423,7 @@ void topk_radix_kernel(const float* __restrict__ scores, int32_t* __restrict__ i
             T = radix_select(sh, need, [&](auto&& fn) {
                 for (uint32_t i = tid; i < nc; i += kT) fn(sh.cand[i]);
             });
+            eqT = sh.bincnt;                       // the list's keys == T
             done = true;
         }
     } else {
@@ -318,12 +436,13 @@ void topk_radix_kernel(const float* __restrict__ scores, int32_t* __restrict__ i
                     if (s0 + e < n) fn(kk[e]);
             }
         });
+        eqT = sh.bincnt;                           // the row's keys == T
     }
 
     // 4. Compaction in ascending s: position = (#keys > T before s) + min(#keys == T before s, need).
-    //    Counts of (> T, == T) are packed as (gt << 16) | eq (a step of 4096
-    //    positions holds at most 4096 of either).  Positions are assembled in
-    //    LDS when k fits.
+    //    In the general case counts of (> T, == T) are packed as
+    //    (gt << 16) | eq (a step of 4096 positions holds at most 4096 of
+    //    either).  Positions are assembled in LDS when k fits.
     const bool to_lds = k <= kSelCap;
     int32_t* dst = to_lds ? sh.sel : out;
     auto counts = [&](int s0, const uint32_t (&kk)[4]) {
@@ -354,29 +473,80 @@ void topk_radix_kernel(const float* __restrict__ scores, int32_t* __restrict__ i
         }
     };
     if (in_regs) {
-        // All steps at once.  Per-step wave scans give positions within a wave;
-        // the (step, wave) totals, in ascending-s order (step-major), get one
-        // exclusive scan that every wave evaluates (two totals per lane), and
-        // each wave reads its own prefixes with uniform lane reads.  The
-        // per-step scans are recomputed after the barrier rather than kept.
-        static_assert(kNV * kWaves == 2 * kWave, "two (step, wave) totals per lane");
+        // All steps at once.  Usually every key equal to T is taken (eqT ==
+        // need) and T >= 1, so the selection is simply key >= T (positions
+        // past the row hold key 0).  Per lane, the counts of selected keys of
+        // the 8 steps (at most 4 each) are packed three to a word in 10-bit
+        // fields, so three wave scans give every in-wave prefix (at most 256)
+        // and the wave totals; the (step, wave) totals in ascending-s order
+        // (step-major), two per lane, get one exclusive scan that every wave
+        // evaluates, and each wave reads its own prefixes with uniform lane
+        // reads.  Lanes write unselected positions to their own trash word.
+        static_assert(kNV == 8 && kNV * kWaves == 2 * kWave, "three packed scans; two (step, wave) totals per lane");
+        if (eqT == need && T > 0u && to_lds) {
+            uint32_t cw[3] = {0u, 0u, 0u};
 #pragma unroll
-        for (int v = 0; v < kNV; ++v) {
-            const uint32_t incl = (v * kTile < n) ? wave_incl_scan(counts(v * kTile + tid * 4, key[v]), lane) : 0u;
-            if (lane == 63) sh.wtot[v][wave] = incl;
-        }
-        __syncthreads();
-        const uint32_t* flat = &sh.wtot[0][0];
-        const uint32_t x0 = flat[2 * lane], x1 = flat[2 * lane + 1];
-        const uint32_t e0 = wave_incl_scan(x0 + x1, lane) - (x0 + x1);   // before entry 2*lane
-        const uint32_t ew = (wave & 1) ? e0 + x0 : e0;                   // before entry 2*lane + (wave & 1)
+            for (int v = 0; v < kNV; ++v) {
+                uint32_t c = 0;
+                if (v * kTile < n) {
 #pragma unroll
-        for (int v = 0; v < kNV; ++v) {
-            if (v * kTile >= n) break;             // workgroup-uniform
-            const uint32_t base = __builtin_amdgcn_readlane(ew, (v * kWaves + wave) >> 1);
-            const uint32_t pk = counts(v * kTile + tid * 4, key[v]);
-            const uint32_t pre = base + wave_incl_scan(pk, lane) - pk;
-            place(v * kTile + tid * 4, key[v], pre >> 16, pre & 0xFFFFu);
+                    for (int e = 0; e < 4; ++e) c += key[v][e] >= T;
+                }
+                cw[v / 3] |= c << (10 * (v % 3));
+            }
+            uint32_t ci[3];
+#pragma unroll
+            for (int i = 0; i < 3; ++i) ci[i] = wave_incl_scan(cw[i], lane);
+            uint32_t* w3 = &sh.wtot[0][0];         // [wave][3] wave totals
+            if (lane == 63) {
+#pragma unroll
+                for (int i = 0; i < 3; ++i) w3[wave * 3 + i] = ci[i];
+            }
+            __syncthreads();
+            // entries 2 lane, 2 lane + 1: step lane / 8, waves 2 (lane % 8) and 2 (lane % 8) + 1
+            const int sv = lane >> 3, sw = 2 * (lane & 7);
+            const uint32_t x0 = (w3[sw * 3 + sv / 3] >> (10 * (sv % 3))) & 0x3FFu;
+            const uint32_t x1 = (w3[(sw + 1) * 3 + sv / 3] >> (10 * (sv % 3))) & 0x3FFu;
+            const uint32_t e0 = wave_incl_scan(x0 + x1, lane) - (x0 + x1);   // before entry 2*lane
+            const uint32_t ew = (wave & 1) ? e0 + x0 : e0;                   // before entry 2*lane + (wave & 1)
+            uint32_t* trash = &sh.trash[lane];
+#pragma unroll
+            for (int v = 0; v < kNV; ++v) {
+                if (v * kTile >= n) break;         // workgroup-uniform
+                const int f = 10 * (v % 3);
+                uint32_t pos = __builtin_amdgcn_readlane(ew, (v * kWaves + wave) >> 1) +
+                               ((ci[v / 3] >> f) & 0x3FFu) - ((cw[v / 3] >> f) & 0x3FFu);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const bool pass = key[v][e] >= T;
+                    *(pass ? (uint32_t*)&sh.sel[pos] : trash) = (uint32_t)(v * kTile + tid * 4 + e);
+                    pos += pass;
+                }
+            }
+        } else {
+            // General case (some keys equal to T left out, or k beyond the
+            // LDS assembly): the lowest-index keys equal to T are taken.  The
+            // same two scans, over packed (gt << 16) | eq per step; the
+            // per-step scans are recomputed after the barrier rather than
+            // kept.
+#pragma unroll
+            for (int v = 0; v < kNV; ++v) {
+                const uint32_t incl = (v * kTile < n) ? wave_incl_scan(counts(v * kTile + tid * 4, key[v]), lane) : 0u;
+                if (lane == 63) sh.wtot[v][wave] = incl;
+            }
+            __syncthreads();
+            const uint32_t* flat = &sh.wtot[0][0];
+            const uint32_t x0 = flat[2 * lane], x1 = flat[2 * lane + 1];
+            const uint32_t e0 = wave_incl_scan(x0 + x1, lane) - (x0 + x1);   // before entry 2*lane
+            const uint32_t ew = (wave & 1) ? e0 + x0 : e0;                   // before entry 2*lane + (wave & 1)
+#pragma unroll
+            for (int v = 0; v < kNV; ++v) {
+                if (v * kTile >= n) break;         // workgroup-uniform
+                const uint32_t base = __builtin_amdgcn_readlane(ew, (v * kWaves + wave) >> 1);
+                const uint32_t pk = counts(v * kTile + tid * 4, key[v]);
+                const uint32_t pre = base + wave_incl_scan(pk, lane) - pk;
+                place(v * kTile + tid * 4, key[v], pre >> 16, pre & 0xFFFFu);
+            }
         }
     } else {
         uint32_t base_gt = 0, base_eq = 0;
@@ -412,9 +582,21 @@ void topk_radix_kernel(const float* __restrict__ scores, int32_t* __restrict__ i
 hipError_t launch_topk(const TopkLaunch& a, hipStream_t s)
 {
     if (a.B == 0 || a.t_count == 0) return hipSuccess;
-    hipLaunchKernelGGL(topk_radix_kernel, dim3(a.t_count, a.B), dim3(kT), 0, s,
-                       a.scores, a.idx, a.q_pos0, a.t_begin, a.sc_bstride, a.sc_rstride,
-                       a.idx_bstride, a.k);
+    // Row r (t = t_begin + r) has n = q_pos0 + t_begin + r + 1 candidates, so
+    // with aligned rows the register-resident instance takes the rows with
+    // 4 <= n <= kRegRow, a contiguous range [r_lo, r_hi); the others stream.
+    const bool aligned = ((uintptr_t)a.scores & 15u) == 0 && a.sc_bstride % 4 == 0 && a.sc_rstride % 4 == 0;
+    const int64_t n0 = (int64_t)a.q_pos0 + a.t_begin + 1;                 // n of row 0
+    const int r_lo = aligned ? (int)std::min<int64_t>(std::max<int64_t>(4 - n0, 0), a.t_count) : a.t_count;
+    const int r_hi = aligned ? (int)std::max<int64_t>(std::min<int64_t>(kRegRow - n0 + 1, a.t_count), r_lo) : a.t_count;
+    auto rows = [&](auto kernel, int r0, int r1) {
+        if (r1 > r0)
+            hipLaunchKernelGGL(kernel, dim3(r1 - r0, a.B), dim3(kT), 0, s, a.scores, a.idx, a.q_pos0, a.t_begin, r0,
+                               a.sc_bstride, a.sc_rstride, a.idx_bstride, a.k);
+    };
+    rows(topk_radix_kernel<false>, 0, r_lo);
+    rows(topk_radix_kernel<true>, r_lo, r_hi);
+    rows(topk_radix_kernel<false>, r_hi, a.t_count);
     return hipGetLastError();
 }
 
