@@ -9,19 +9,26 @@
 //   KL_t   = sum_s p[s] log p[s] - sum_s p[s] I[t,s] + LSE(I[t,:]) * sum_s p[s]
 //
 // One workgroup per query row, one wave per 32 heads, the query held in
-// registers as 36 bf16 MFMA operands (v_mfma_f32_32x32x16_bf16, keys as the A
-// operand).  Two sweeps over the row's keys in chunks of 32 rows: the first
-// keeps each head's running maximum and sum (LSE_h), the second recomputes the
-// scores, turns them into per-head probabilities, sums them over the heads
-// through LDS and folds p log p, p I and p into three sums.  The rows stream
-// through a two-slot LDS ring with asynchronous global -> LDS copies issued one
-// chunk ahead: each row's first 512 columns at a 1040-byte pitch (one copy
-// instruction per row; 16 consecutive rows read at one column cover all banks
-// once), its last 64 columns packed 8 rows per 1 KB with piece p of row r at
-// position p ^ (r % 8).  The work is two QK^T products per query row (no value
-// product).
+// registers as 36 bf16 MFMA operands (v_mfma_f32_32x32x16_bf16).  Two sweeps
+// over the row's keys in chunks of 32 rows:
+//  1. S^T (keys as the A operand, so a lane holds 16 keys of one head): each
+//     head's running maximum and sum, LSE_h;
+//  2. S (the same registers with the operands swapped, so a lane holds 16
+//     heads of one key): per key, the wave's sum over its heads of
+//     exp(z - LSE_h), 16 values in the lane plus its partner lane; the waves'
+//     sums meet in LDS and one wave folds p log p, p I and p into three sums
+//     one chunk later, behind the next chunk's barrier.
+// The rows stream through a two-slot LDS ring with asynchronous global -> LDS
+// copies issued one chunk ahead: each row's first 512 columns at a 1040-byte
+// pitch (one copy instruction per row; 16 consecutive rows read at one column
+// cover all banks once), its last 64 columns packed 8 rows per 1 KB with piece
+// p of row r at position p ^ (r % 8), and the chunk's 32 indexer scores.  At
+// 256 registers and under 80 KB of LDS per workgroup, two rows share a CU.
+// The work is two QK^T products per query row (no value product).
 #include "hw.h"
 #include "launch.h"
+
+#include <type_traits>
 
 namespace dsa {
 
@@ -34,7 +41,7 @@ constexpr int kVPitch = 1040;           // bytes per staged row head (first 512 
 constexpr int kVBytes = kKC * kVPitch;
 constexpr int kScoreOff = kVBytes + kKC * 128;  // after the 64-column tails: the chunk's 32 indexer scores
 constexpr int kSlot = kScoreOff + 256;
-constexpr int kRing = 3;                        // slots: copies run two chunks ahead
+constexpr int kRing = 2;
 
 __device__ __forceinline__ float block_sum(float v, float* red, int nwaves)
 {
@@ -61,7 +68,7 @@ __device__ __forceinline__ float block_max(float v, float* red, int nwaves)
 }
 
 template <int NW>
-__global__ __launch_bounds__(64 * NW)
+__global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1)   // 128 heads: two workgroups per CU, at most 256 registers
 void indexer_kl_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
                        const float* __restrict__ scores, float* __restrict__ kl, int Lq, int Lk, int q_pos0,
                        float scale_log2)
@@ -69,7 +76,8 @@ void indexer_kl_kernel(const uint16_t* __restrict__ q, const uint16_t* __restric
     constexpr int H = 32 * NW;
     constexpr int NT = 64 * NW;
     __shared__ __attribute__((aligned(16))) uint8_t ring[kRing][kSlot];
-    __shared__ float E[kKC][H + 1];                  // per key: each head's probability
+    __shared__ float lse_h[H];                       // per head, log2 domain
+    __shared__ float pw[2][NW][kKC];                 // per chunk parity, wave, key: the wave's head sum
     __shared__ float red[NW];
 
     const int t = Lq - 1 - (int)blockIdx.x, b = blockIdx.y;     // longest rows first
@@ -79,7 +87,8 @@ void indexer_kl_kernel(const uint16_t* __restrict__ q, const uint16_t* __restric
     const int col = lane & 31, hi = lane >> 5;
     const int h = wave * 32 + col;
 
-    // query fragments: head h, dims 16 c + 8 hi .. +8
+    // query fragments: head h, dims 16 c + 8 hi .. +8 (the B operand of S^T
+    // and, with the same contents, the A operand of S)
     const uint16_t* qrow = q + (((int64_t)b * Lq + t) * H + h) * kQK;
     v8bf qf[kSteps];
 #pragma unroll
@@ -98,7 +107,8 @@ void indexer_kl_kernel(const uint16_t* __restrict__ q, const uint16_t* __restric
     const int nch = (n + kKC - 1) / kKC;
     // copies of keys c0 .. c0+31 into ring slot `slot` (rows past the row's
     // last key repeat it; masked below): row e on wave e % NW, tail group ti
-    // (rows 8 ti .. 8 ti + 7) on wave ti % NW
+    // (rows 8 ti .. 8 ti + 7) on wave ti % NW, the scores on wave 0 (lanes
+    // 32..63 repeat the last)
     auto issue = [&](int c0, int slot) {
         const uint32_t base = lds_byte_address(ring[slot]);
         for (int e = wave; e < kKC; e += NW) {
@@ -113,24 +123,22 @@ void indexer_kl_kernel(const uint16_t* __restrict__ q, const uint16_t* __restric
             global_to_lds16_async(kvb + (int64_t)sr * kQK + 512 + pc * 8,
                                   __builtin_amdgcn_readfirstlane(base + (uint32_t)(kVBytes + ti * 1024)));
         }
-        // the chunk's indexer scores (wave 0; lanes 32..63 repeat the last)
         if (wave == 0)
             global_to_lds4_async(I + min(c0 + lane, n - 1), __builtin_amdgcn_readfirstlane(base + (uint32_t)kScoreOff));
     };
-    // copy instructions one wave issues per chunk (vmcnt counts them)
-    // top of chunk ch: its copies landed everywhere (those of ch + 1 may still
-    // be in flight), the slot of ch - 1 is free; then ch + 2 is queued into it
+    // top of chunk ch: this wave's copies of ch landed, then every wave's
+    // (and every wave is done with ch - 1, whose slot takes ch + 1)
     auto next_chunk = [&](int ch) {
-        constexpr int kPer = kKC / NW + (kKC / 8 + NW - 1) / NW;
-        if (ch + 1 >= nch) wait_vmcnt0();
-        else if (wave == 0) wait_vmcnt<kPer + 1>();
-        else wait_vmcnt<kPer>();
+        wait_vmcnt0();
         __syncthreads();
-        if (ch + 2 < nch) issue((ch + 2) * kKC, (ch + 2) % kRing);
+        if (ch + 1 < nch) issue((ch + 1) * kKC, (ch + 1) % kRing);
     };
-    // S^T of the chunk in slot `slot` for this wave's heads: element v is key
-    // c0 + 8 (v / 4) + 4 hi + v % 4 (the A operand's row is the lane's key)
-    auto scores_T = [&](int slot) -> v16f {
+    // the 36 K-step fragments of the lane's key (chunk row col) in slot
+    // `slot`, read kPre steps ahead of their MFMA (order pinned: the compiler
+    // would otherwise move each read next to its use); ST selects S^T
+    // (keys x heads) or S (heads x keys)
+    auto product = [&](int slot, auto st_tag) -> v16f {
+        constexpr bool ST = decltype(st_tag)::value;
         v16f acc;
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[v] = 0.f;
@@ -139,30 +147,31 @@ void indexer_kl_kernel(const uint16_t* __restrict__ q, const uint16_t* __restric
         auto frag = [&](int c) -> u32x4 {
             return c < 32 ? *(const u32x4*)(vr + 32 * c) : *(const u32x4*)(tr + (((2 * (c - 32) + hi) ^ (col & 7)) << 4));
         };
-        // fragments read kPre steps ahead of their MFMA (order pinned: the
-        // compiler would otherwise move each read next to its use)
-        constexpr int kPre = 7;
+        constexpr int kPre = 3;
         u32x4 kf[kPre + 1];
 #pragma unroll
         for (int i = 0; i < kPre; ++i) kf[i] = frag(i);
 #pragma unroll
         for (int c = 0; c < kSteps; ++c) {
             if (c + kPre < kSteps) kf[(c + kPre) % (kPre + 1)] = frag(c + kPre);
-            acc = mfma_bf16_32x32x16(as_bf8(kf[c % (kPre + 1)]), qf[c], acc);
+            if constexpr (ST) acc = mfma_bf16_32x32x16(as_bf8(kf[c % (kPre + 1)]), qf[c], acc);
+            else acc = mfma_bf16_32x32x16(qf[c], as_bf8(kf[c % (kPre + 1)]), acc);
             __builtin_amdgcn_sched_barrier(0);
         }
         return acc;
     };
+    using STag = std::integral_constant<bool, true>;
+    using SRow = std::integral_constant<bool, false>;
 
-    // pass 1: per-head maximum and sum (log2 domain)
+    // pass 1: per-head maximum and sum (log2 domain); S^T element v is key
+    // c0 + 8 (v / 4) + 4 hi + v % 4 of head h
     float m = -INFINITY, l = 0.f;
     __syncthreads();
     issue(0, 0);
-    if (nch > 1) issue(kKC, 1);
     for (int ch = 0; ch < nch; ++ch) {
         const int c0 = ch * kKC;
         next_chunk(ch);
-        const v16f st = scores_T(ch % kRing);
+        const v16f st = product(ch % kRing, STag{});
         float z[16], cm = -INFINITY;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
@@ -179,37 +188,45 @@ void indexer_kl_kernel(const uint16_t* __restrict__ q, const uint16_t* __restric
         l = l * exp2f(m - mn) + ps;
         m = mn;
     }
-    const float lse2 = m + log2f(l);
+    if (hi == 0) lse_h[h] = m + log2f(l);
+    __syncthreads();                                           // pass 1 done with the ring; lse_h published
+    // S element v is head wave*32 + 8 (v / 4) + 4 hi + v % 4 of key c0 + col
+    float lsev[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) lsev[v] = lse_h[wave * 32 + 8 * (v >> 2) + 4 * hi + (v & 3)];
 
-    // pass 2: p per key, then the three sums
+    // pass 2: per key, p = mean over heads of exp2(z - lse); wave 0's lanes
+    // col < 32 fold chunk ch - 1's keys in after chunk ch's barrier
     float a_plogp = 0.f, a_pI = 0.f, a_p = 0.f;
-    constexpr int TPK = NT / kKC;                              // threads per key in the head sum
-    __syncthreads();                                           // pass 1 done with the ring
-    issue(0, 0);
-    if (nch > 1) issue(kKC, 1);
-    for (int ch = 0; ch < nch; ++ch) {
-        const int c0 = ch * kKC;
-        next_chunk(ch);
-        const v16f st = scores_T(ch % kRing);
+    float i_prev = 0.f;                                        // indexer score of key (ch - 1) * 32 + col
+    auto fold = [&](int ch_done, float iv) {
+        const int s = ch_done * kKC + col;
+        if (wave == 0 && hi == 0 && s < n) {
+            float ph = 0.f;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int kk = 8 * (v >> 2) + 4 * hi + (v & 3);
-            E[kk][h] = (c0 + kk < n) ? exp2f(st[v] * scale_log2 - lse2) : 0.f;
-        }
-        __syncthreads();
-        const int kk = tid / TPK, part = tid % TPK;
-        float ph = 0.f;
-        for (int j = part; j < H; j += TPK) ph += E[kk][j];
-#pragma unroll
-        for (int o = 1; o < TPK; o <<= 1) ph += __shfl_xor(ph, o, kWave);
-        const int s = c0 + kk;
-        if (part == 0 && s < n) {
+            for (int w = 0; w < NW; ++w) ph += pw[ch_done & 1][w][col];
             const float p = ph * (1.f / H);
             if (p > 0.f) a_plogp += p * logf(p);
-            a_pI += p * *(const float*)(ring[ch % kRing] + kScoreOff + 4 * kk);
+            a_pI += p * iv;
             a_p += p;
         }
+    };
+    issue(0, 0);
+    for (int ch = 0; ch < nch; ++ch) {
+        next_chunk(ch);
+        if (ch > 0) fold(ch - 1, i_prev);
+        const uint8_t* slot = ring[ch % kRing];
+        const float i_cur = *(const float*)(slot + kScoreOff + 4 * col);
+        const v16f sv = product(ch % kRing, SRow{});
+        float ph = 0.f;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) ph += exp2f(fmaf(sv[v], scale_log2, -lsev[v]));
+        ph += __shfl_xor(ph, 32, kWave);
+        if (hi == 0) pw[ch & 1][wave][col] = ph;
+        i_prev = i_cur;
     }
+    __syncthreads();
+    if (nch > 0) fold(nch - 1, i_prev);
     a_plogp = block_sum(a_plogp, red, NW);
     a_pI = block_sum(a_pI, red, NW);
     a_p = block_sum(a_p, red, NW);

@@ -143,10 +143,10 @@ __device__ __forceinline__ uint32_t radix_select(TopkShared& sh, uint32_t& need,
 }
 
 // Two rows per CU: 8 waves per SIMD (64 VGPRs) and under 80 KB of LDS each.
-// IN_REGS: every row of the launch has 4 <= n <= kRegRow, starts 16-byte
-// aligned and is held in registers (a separate instance, so that the
-// registers of the streaming path do not crowd the 32 register-resident
-// keys).  Block x handles row row0 + x.
+// IN_REGS: every row of the launch has n <= kRegRow and either n >= 4 or
+// n <= k, starts 16-byte aligned and is held in registers (a separate
+// instance, so that the registers of the streaming path do not crowd the 32
+// register-resident keys).  Block x handles row row0 + x.
 template <bool IN_REGS>
 __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(8)))
 void topk_radix_kernel(const float* __restrict__ scores, int32_t* __restrict__ idx,
@@ -584,10 +584,12 @@ hipError_t launch_topk(const TopkLaunch& a, hipStream_t s)
     if (a.B == 0 || a.t_count == 0) return hipSuccess;
     // Row r (t = t_begin + r) has n = q_pos0 + t_begin + r + 1 candidates, so
     // with aligned rows the register-resident instance takes the rows with
-    // 4 <= n <= kRegRow, a contiguous range [r_lo, r_hi); the others stream.
+    // n <= kRegRow and either n >= 4 or n <= k (those only write 0..n-1), a
+    // contiguous range [r_lo, r_hi); the others stream.
     const bool aligned = ((uintptr_t)a.scores & 15u) == 0 && a.sc_bstride % 4 == 0 && a.sc_rstride % 4 == 0;
     const int64_t n0 = (int64_t)a.q_pos0 + a.t_begin + 1;                 // n of row 0
-    const int r_lo = aligned ? (int)std::min<int64_t>(std::max<int64_t>(4 - n0, 0), a.t_count) : a.t_count;
+    const int64_t n_lo = a.k >= 3 ? 1 : 4;                                 // smallest n the instance takes
+    const int r_lo = aligned ? (int)std::min<int64_t>(std::max<int64_t>(n_lo - n0, 0), a.t_count) : a.t_count;
     const int r_hi = aligned ? (int)std::max<int64_t>(std::min<int64_t>(kRegRow - n0 + 1, a.t_count), r_lo) : a.t_count;
     auto rows = [&](auto kernel, int r0, int r1) {
         if (r1 > r0)
