@@ -8,10 +8,13 @@
 //
 // Two kernels, both with bf16 MFMAs and fp32 accumulation:
 //  1. dq: one workgroup per (row, group of up to 64 heads), one wave per 16
-//     heads.  q^T and dO^T stay in registers as 16x16x32 operands; per chunk
-//     of 32 selected rows (staged in LDS, plus a transposed copy) it forms
-//     S^T and dP^T, then P and dZ, and accumulates dq^T = K^T dZ^T in 36
-//     register tiles.  P and dZ are also written (bf16, keys-major) for 2.
+//     heads.  q^T and dO^T stay in registers as 16x16x32 operands.  The
+//     selected rows stream through a two-slot LDS ring of 32 rows, copied
+//     asynchronously one chunk ahead (first 512 columns at a 1040-byte pitch,
+//     last 64 packed 8 rows per 1 KB).  Per chunk the wave forms S^T and
+//     dP^T, then P and dZ, and accumulates dq^T = K^T dZ^T in 36 register
+//     tiles; the K^T operand comes straight from the row-major rows through
+//     LDS transpose reads.  P and dZ are also written (bf16, keys-major) for 2.
 //  2. dkv: one workgroup per (row, 8 of the 18 column tiles of 32), one wave
 //     per 2 tiles.  A tile of the first 512 columns takes both products,
 //     scale dZ q and P dO, into one accumulator (one atomic per element, not
@@ -30,8 +33,27 @@ namespace {
 constexpr int kBQK = 576;            // latent row width
 constexpr int kBV = 512;             // value width
 constexpr int kBNC = 32;             // selected rows per chunk
-constexpr int kBKP = kBQK + 8;       // staged row pitch (bf16 elements): conflict-free 16-lane b128 reads
-constexpr int kBTP = kBNC + 8;       // transposed copy pitch (bf16 elements)
+constexpr int kBKMax = 2048;         // largest k (the index list is staged in LDS)
+constexpr int kRowPitch = 1040;      // ring bytes per row of the first 512 columns (+ one skew piece)
+constexpr int kRingV = kBNC * kRowPitch;
+constexpr int kRingSlot = kRingV + kBNC * 128;   // + the 64-column tails, 8 rows per 1 KB
+
+// Chunk row held by row m (0..15) of a 16-row key tile in the S^T products:
+// rows 4i + g of the accumulator (lane group g, element i) hold chunk rows
+// g + 4i, so the four rows one transpose read gathers are 4 apart (distinct
+// LDS banks at the 1040-byte pitch).
+__device__ __forceinline__ constexpr int bwd_tile_row(int m) { return 4 * (m & 3) + (m >> 2); }
+
+// Byte offset in a ring slot of 16-bit column d (d % 8 == 0 for 16-byte reads,
+// d % 4 == 0 for 8-byte reads) of chunk row r: the first 512 columns at the
+// row pitch, the tails packed 8 rows per 1 KB with piece p of row r at
+// position p ^ (r % 8).
+__device__ __forceinline__ uint32_t ring_off(int r, int d)
+{
+    if (d < kBV) return (uint32_t)(r * kRowPitch + 2 * d);
+    const int p = (d - kBV) >> 3;
+    return (uint32_t)(kRingV + (r >> 3) * 1024 + ((r & 7) * 8 + (p ^ (r & 7))) * 16 + 2 * (d & 7));
+}
 
 // ---------------------------------------------------------------- 1. dq, P, dZ
 
@@ -43,10 +65,9 @@ void attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
                         float* __restrict__ dq, uint16_t* __restrict__ wsP, uint16_t* __restrict__ wsZ,
                         int Lq, int Lk, int H, int k, float scale)
 {
-    __shared__ __attribute__((aligned(16))) uint16_t Kc[kBNC * kBKP];   // chunk rows, row-major
-    __shared__ __attribute__((aligned(16))) uint16_t KT[kBQK * kBTP];   // transposed: KT[d][r]
+    __shared__ __attribute__((aligned(16))) uint8_t ring[2][kRingSlot];
+    __shared__ __attribute__((aligned(16))) int32_t sel[kBKMax];          // the row's index list (-1 padded)
     __shared__ __attribute__((aligned(16))) uint16_t T[NW][2][kBNC * 16]; // P / dZ, [key][head] per wave
-    __shared__ int rows[kBNC];
     __shared__ int wlast[NW];
 
     const int t = blockIdx.x, b = blockIdx.y;
@@ -79,12 +100,15 @@ void attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
     const float lse2 = lse[qrow * H + h] * 1.4426950408889634f;
     const float scale_log2 = scale * 1.4426950408889634f;
 
+    // Stage the index list; entries that cannot be read become -1.  Chunks
+    // past the last valid entry are not visited.
     const int32_t* irow = idx + qrow * k;
-    // chunks past the last valid entry are not visited
     int last = -1;
-    for (int i = tid; i < k; i += 64 * NW) {
-        const int s = irow[i];
-        if (s >= 0 && s < Lk) last = i;
+    for (int i = tid; i < kBKMax; i += 64 * NW) {
+        const int s = (i < k) ? irow[i] : -1;
+        const bool ok = s >= 0 && s < Lk;
+        sel[i] = ok ? s : -1;
+        last = ok ? i : last;
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) last = max(last, __shfl_xor(last, o, kWave));
@@ -92,83 +116,122 @@ void attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
     __syncthreads();
 #pragma unroll
     for (int w = 0; w < NW; ++w) last = max(last, wlast[w]);
-    const int nchunks = (last + kBNC) / kBNC;
+    const int nchunks = __builtin_amdgcn_readfirstlane((last + kBNC) / kBNC);
 
     v4f dqa[kBQK / 16];
 #pragma unroll
     for (int m = 0; m < kBQK / 16; ++m) dqa[m] = v4f{0.f, 0.f, 0.f, 0.f};
     const uint16_t* kvb = kv + (int64_t)b * Lk * kBQK;
 
+    // copies of chunk c into ring slot c % 2 (rows past the list copy row 0;
+    // their weights are zero): row e on wave e % NW, tail group ti (rows
+    // 8 ti .. 8 ti + 7) on wave ti % NW
+    auto issue = [&](int c) {
+        const uint32_t base = lds_byte_address(ring[c & 1]);
+        for (int e = wave; e < kBNC; e += NW) {
+            const int sr = max(sel[c * kBNC + e], 0);
+            global_to_lds16_async(kvb + (int64_t)__builtin_amdgcn_readfirstlane(sr) * kBQK + lane * 8,
+                                  __builtin_amdgcn_readfirstlane(base + (uint32_t)(e * kRowPitch)));
+        }
+        for (int ti = wave; ti < kBNC / 8; ti += NW) {
+            const int r = 8 * ti + (lane >> 3);
+            const int sr = max(sel[c * kBNC + r], 0);
+            const int piece = (lane & 7) ^ (r & 7);
+            global_to_lds16_async(kvb + (int64_t)sr * kBQK + kBV + piece * 8,
+                                  __builtin_amdgcn_readfirstlane(base + (uint32_t)(kRingV + ti * 1024)));
+        }
+    };
+
+    const int i16 = lane & 15;
+    if (nchunks > 0) issue(0);
     for (int ch = 0; ch < nchunks; ++ch) {
         const int c0 = ch * kBNC;
-        __syncthreads();                                                // previous chunk consumed
-        if (tid < kBNC) {
-            const int s = (c0 + tid < k) ? irow[c0 + tid] : -1;
-            rows[tid] = (s >= 0 && s < Lk) ? s : -1;
-        }
-        __syncthreads();
-        for (int p = tid; p < kBNC * (kBQK / 8); p += 64 * NW) {
-            const int r = p / (kBQK / 8), c = p - r * (kBQK / 8);
-            const int s = rows[r];
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (s >= 0) v = *(const u32x4*)(kvb + (int64_t)s * kBQK + c * 8);
-            *(u32x4*)(Kc + r * kBKP + c * 8) = v;
-        }
-        __syncthreads();
-        for (int p = tid; p < (kBNC / 2) * kBQK; p += 64 * NW) {
-            const int rp = p % (kBNC / 2), d = p / (kBNC / 2);
-            const uint32_t lo = Kc[(2 * rp) * kBKP + d], hi2 = Kc[(2 * rp + 1) * kBKP + d];
-            *(uint32_t*)(KT + d * kBTP + 2 * rp) = lo | (hi2 << 16);
-        }
-        __syncthreads();
+        wait_vmcnt0();                                                  // this wave's copies of chunk ch
+        __syncthreads();                                                // everyone's; chunk ch - 1 consumed
+        if (ch + 1 < nchunks) issue(ch + 1);
+        const uint8_t* cur = ring[ch & 1];
 
-        // S^T and dP^T, keys 16 j + 4 g + i of tile j, head h
+        // S^T and dP^T: accumulator element i of tile j (lane group g, head
+        // col) is chunk row 16 j + g + 4 i
+        // Key fragments are read kPre steps ahead of their MFMAs over both
+        // tiles (step u = 18 j + c); the order is pinned, as the compiler
+        // would otherwise wait on each read right before its use.
         v4f st[2], dpt[2];
+        {
+            constexpr int kSt = kBQK / 32, kPre = 4;
+            auto kfrag = [&](int u) -> u32x4 {
+                const int j = u / kSt, c = u % kSt;
+                return *(const u32x4*)(cur + ring_off(16 * j + bwd_tile_row(col), 32 * c + 8 * g));
+            };
+            u32x4 kf[kPre + 1];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const uint16_t* kr = Kc + (16 * j + col) * kBKP + 8 * g;
+            for (int u = 0; u < kPre; ++u) kf[u] = kfrag(u);
             v4f a = {0.f, 0.f, 0.f, 0.f}, bq = a;
 #pragma unroll
-            for (int c = 0; c < kBQK / 32; ++c) a = mfma_bf16_16x16x32(as_bf8(*(const u32x4*)(kr + 32 * c)), qT[c], a);
-#pragma unroll
-            for (int c = 0; c < kBV / 32; ++c) bq = mfma_bf16_16x16x32(as_bf8(*(const u32x4*)(kr + 32 * c)), doT[c], bq);
-            st[j] = a;
-            dpt[j] = bq;
+            for (int u = 0; u < 2 * kSt; ++u) {
+                const int c = u % kSt;
+                if (u + kPre < 2 * kSt) kf[(u + kPre) % (kPre + 1)] = kfrag(u + kPre);
+                const v8bf f = as_bf8(kf[u % (kPre + 1)]);
+                a = mfma_bf16_16x16x32(f, qT[c], a);
+                if (c < kBV / 32) bq = mfma_bf16_16x16x32(f, doT[c], bq);
+                if (c == kSt - 1) {
+                    st[u / kSt] = a;
+                    dpt[u / kSt] = bq;
+                    a = v4f{0.f, 0.f, 0.f, 0.f};
+                    bq = a;
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
         float pv[8], zv[8];
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const bool ok = rows[16 * j + 4 * g + i] >= 0;
+                const bool ok = sel[c0 + 16 * j + g + 4 * i] >= 0;
                 const float p = ok ? exp2f(fmaf(st[j][i], scale_log2, -lse2)) : 0.f;
                 pv[4 * j + i] = p;
                 zv[4 * j + i] = p * (dpt[j][i] - Dh) * scale;          // scale dZ, used by dq and dkv
             }
-        // dq^T tiles: A = dZ (head col, key slots 8g..8g+7 = keys 4g..4g+3, 16+4g..16+4g+3),
-        // B = K^T (same key slots, dim 16 m + col) from the transposed copy
+        // dq^T tiles: A = dZ (head col; K slots 8 g + 4 j + i = chunk rows
+        // 16 j + g + 4 i), B = K^T over the same slots, dims 16 m + col: the
+        // transpose read of lane group g gathers rows g + 4 (i16 / 4) (+16),
+        // 4 dims 16 m + 4 (i16 % 4) each, and hands lane col dim 16 m + col
         const v8bf az = as_bf8(u32x4{pack_bf16x2(zv[0], zv[1]), pack_bf16x2(zv[2], zv[3]),
                                      pack_bf16x2(zv[4], zv[5]), pack_bf16x2(zv[6], zv[7])});
+        const int rl = g + 4 * (i16 >> 2);
+        {
+            constexpr int kPre = 3;                                     // tiles read ahead (2 reads each)
+            auto ktfrag = [&](int m) -> u32x4 {
+                const int d = 16 * m + 4 * (i16 & 3);
+                const u32x2 lo = __builtin_bit_cast(u32x2, lds_read_tr16(cur + ring_off(rl, d)));
+                const u32x2 hi2 = __builtin_bit_cast(u32x2, lds_read_tr16(cur + ring_off(rl + 16, d)));
+                return u32x4{lo[0], lo[1], hi2[0], hi2[1]};
+            };
+            u32x4 kt[kPre + 1];
 #pragma unroll
-        for (int m = 0; m < kBQK / 16; ++m) {
-            const uint16_t* kt = KT + (16 * m + col) * kBTP + 4 * g;
-            const u32x2 lo = *(const u32x2*)kt, hi2 = *(const u32x2*)(kt + 16);
-            dqa[m] = mfma_bf16_16x16x32(az, as_bf8(u32x4{lo[0], lo[1], hi2[0], hi2[1]}), dqa[m]);
+            for (int m = 0; m < kPre; ++m) kt[m] = ktfrag(m);
+#pragma unroll
+            for (int m = 0; m < kBQK / 16; ++m) {
+                if (m + kPre < kBQK / 16) kt[(m + kPre) % (kPre + 1)] = ktfrag(m + kPre);
+                dqa[m] = mfma_bf16_16x16x32(az, as_bf8(kt[m % (kPre + 1)]), dqa[m]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
-        // P and dZ (bf16) to the workspace, keys-major: through LDS so that a
-        // lane stores 8 heads of one key
+        // P and dZ (bf16) to the workspace, keys-major: through this wave's
+        // part of LDS so that a lane stores 8 heads of one key
         uint16_t* tp = T[wave][0];
         uint16_t* tz = T[wave][1];
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int kk = 16 * j + 4 * g + i;
+                const int kk = 16 * j + g + 4 * i;
                 const uint32_t pz = pack_bf16x2(pv[4 * j + i], zv[4 * j + i]);
                 tp[kk * 16 + col] = (uint16_t)(pz & 0xFFFFu);
                 tz[kk * 16 + col] = (uint16_t)(pz >> 16);
             }
-        __syncthreads();
+        __builtin_amdgcn_wave_barrier();
         {
             const int kk = lane & 31, half = lane >> 5;
             if (c0 + kk < k) {
@@ -177,6 +240,7 @@ void attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
                 *(u32x4*)(wsZ + wo) = *(const u32x4*)(tz + kk * 16 + 8 * half);
             }
         }
+        __builtin_amdgcn_wave_barrier();
     }
     // keys never visited (past the last valid entry) get zero weights
     for (int i = nchunks * kBNC + (tid >> 1); i < k; i += 32 * NW) {
