@@ -15,7 +15,7 @@
 //     dP^T, then P and dZ, and accumulates dq^T = K^T dZ^T in 36 register
 //     tiles; the K^T operand comes straight from the row-major rows through
 //     LDS transpose reads.  P and dZ are also written (bf16, keys-major) for 2.
-//  2. dkv: one workgroup per (row, 8 of the 18 column tiles of 32), one wave
+//  2. dkv: one workgroup per (row, 6 of the 18 column tiles of 32), one wave
 //     per 2 tiles.  A tile of the first 512 columns takes both products,
 //     scale dZ q and P dO, into one accumulator (one atomic per element, not
 //     two); the last 2 tiles take scale dZ q only.  The B operands (q and dO,
@@ -262,25 +262,31 @@ void attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
 
 constexpr int kTilesPerWave = 2;
 constexpr int kDkvTiles = kBQK / 32;                                    // 18 (16 with a value part)
-constexpr int kTilesPerGroup = 4 * kTilesPerWave;                       // 8 per workgroup
+constexpr int kDkvWaves = 3;                                            // 3 waves x 2 tiles: 18 = 3 x 6
+constexpr int kDkvThreads = 64 * kDkvWaves;
+constexpr int kTilesPerGroup = kDkvWaves * kTilesPerWave;               // 6 per workgroup
 
 template <int KS>                                                       // K steps of 16 heads (H = 16 KS)
-__global__ __launch_bounds__(256)
+__global__ __launch_bounds__(kDkvThreads, 2)                            // two workgroups per CU
 void attn_bwd_dkv_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ idx,
                          const uint16_t* __restrict__ dout, const uint16_t* __restrict__ wsP,
                          const uint16_t* __restrict__ wsZ, float* __restrict__ dkv, int Lq, int Lk, int k,
                          float scale)
 {
     constexpr int H = 16 * KS;
-    __shared__ __attribute__((aligned(16))) uint16_t W[2][kBNC * (H + 8)];   // [P | dZ][key][head]
-    __shared__ int rows[kBNC];
+    constexpr int WP = H + 8;                                           // W row pitch (bf16): conflict-free reads
+    constexpr int WTOT = 2 * kBNC * (H / 8);                            // 16-byte pieces of W per chunk
+    constexpr int WPER = (WTOT + kDkvThreads - 1) / kDkvThreads;        // per thread (the last round partial)
+    __shared__ __attribute__((aligned(16))) uint16_t W[2][2][kBNC * WP];  // [buffer][P | dZ][key][head]
+    __shared__ __attribute__((aligned(16))) int32_t sel[kBKMax];           // the row's index list (-1 padded)
+    __shared__ int wlast[kDkvWaves];
     const int t = blockIdx.x, b = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 31, hs = lane >> 5;
     const int64_t qrow = (int64_t)b * Lq + t;
+    static_assert(kDkvTiles % kTilesPerGroup == 0, "every wave has whole tiles");
     const int tile0 = blockIdx.z * kTilesPerGroup + wave * kTilesPerWave;
-    const int ntl = max(0, min(kTilesPerWave, kDkvTiles - tile0));
 
     // B operands of tile T (dims 32 T + n): q, and for T < 16 also dO; heads
     // 16 st + 8 hs + e along K
@@ -292,49 +298,83 @@ void attn_bwd_dkv_kernel(const uint16_t* __restrict__ q, const int32_t* __restri
 #pragma unroll
         for (int st = 0; st < KS; ++st) {
             uint32_t uq[4] = {0u, 0u, 0u, 0u}, uo[4] = {0u, 0u, 0u, 0u};
-            if (j < ntl) {
 #pragma unroll
-                for (int e = 0; e < 8; e += 2) {
-                    const int64_t h0 = qrow * H + 16 * st + 8 * hs + e;
-                    uq[e / 2] = (uint32_t)q[h0 * kBQK + 32 * T + n] | ((uint32_t)q[(h0 + 1) * kBQK + 32 * T + n] << 16);
-                    if (hasv)
-                        uo[e / 2] = (uint32_t)dout[h0 * kBV + 32 * T + n] |
-                                    ((uint32_t)dout[(h0 + 1) * kBV + 32 * T + n] << 16);
-                }
+            for (int e = 0; e < 8; e += 2) {
+                const int64_t h0 = qrow * H + 16 * st + 8 * hs + e;
+                uq[e / 2] = (uint32_t)q[h0 * kBQK + 32 * T + n] | ((uint32_t)q[(h0 + 1) * kBQK + 32 * T + n] << 16);
+                if (hasv)
+                    uo[e / 2] = (uint32_t)dout[h0 * kBV + 32 * T + n] |
+                                ((uint32_t)dout[(h0 + 1) * kBV + 32 * T + n] << 16);
             }
             bq[j][st] = as_bf8(u32x4{uq[0], uq[1], uq[2], uq[3]});
             bo[j][st] = as_bf8(u32x4{uo[0], uo[1], uo[2], uo[3]});
         }
     }
 
+    // Stage the index list; entries that cannot be read become -1.  Chunks
+    // past the last valid entry are not visited.
     const int32_t* irow = idx + qrow * k;
+    int last = -1;
+    for (int i = tid; i < kBKMax; i += kDkvThreads) {
+        const int s = (i < k) ? irow[i] : -1;
+        const bool ok = s >= 0 && s < Lk;
+        sel[i] = ok ? s : -1;
+        last = ok ? i : last;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) last = max(last, __shfl_xor(last, o, kWave));
+    if (lane == 0) wlast[wave] = last;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kDkvWaves; ++w) last = max(last, wlast[w]);
+    const int nch = __builtin_amdgcn_readfirstlane((last + kBNC) / kBNC);
+
+    // The weights of chunk c + 1 (piece p = tid + 192 e: matrix p / (32 H / 8),
+    // key, 8 heads) are loaded into registers while chunk c computes, before
+    // its atomics, and stored to the other LDS buffer after them.  Nothing
+    // between the loads and the stores branches on memory work, so the
+    // compiler's wait for the loads leaves this chunk's atomics in flight.
+    auto load_w = [&](int c, u32x4 (&wr)[WPER]) {
+#pragma unroll
+        for (int e = 0; e < WPER; ++e) {
+            const int p = (tid + kDkvThreads * e) % WTOT;               // past WTOT: a copy, not stored
+            const int which = p / (kBNC * (H / 8)), rem = p % (kBNC * (H / 8));
+            const int kk = rem / (H / 8), cc = rem % (H / 8);
+            const int key = min(c * kBNC + kk, k - 1);                  // past k: zeroed when stored
+            wr[e] = *(const u32x4*)((which ? wsZ : wsP) + (qrow * k + key) * H + 8 * cc);
+        }
+    };
+    auto store_w = [&](int c, const u32x4 (&wr)[WPER]) {
+#pragma unroll
+        for (int e = 0; e < WPER; ++e) {
+            const int p = tid + kDkvThreads * e;
+            if (p >= WTOT) break;
+            const int which = p / (kBNC * (H / 8)), rem = p % (kBNC * (H / 8));
+            const int kk = rem / (H / 8), cc = rem % (H / 8);
+            const bool in = c * kBNC + kk < k;
+            *(u32x4*)(&W[c & 1][which][kk * WP + 8 * cc]) = in ? wr[e] : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
     float* dkvb = dkv + (int64_t)b * Lk * kBQK;
-    const int nch = (k + kBNC - 1) / kBNC;
+    u32x4 wr[WPER];
+    if (nch > 0) {
+        load_w(0, wr);
+        store_w(0, wr);
+    }
     for (int ch = 0; ch < nch; ++ch) {
         const int c0 = ch * kBNC;
-        __syncthreads();
-        if (tid < kBNC) {
-            const int s = (c0 + tid < k) ? irow[c0 + tid] : -1;
-            rows[tid] = (s >= 0 && s < Lk) ? s : -1;
-        }
-        // the chunk's weights: 32 keys x H heads of P and of dZ
-        for (int p = tid; p < 2 * kBNC * (H / 8); p += 256) {
-            const int which = p / (kBNC * (H / 8)), rem = p % (kBNC * (H / 8));
-            const int kk = rem / (H / 8), c = rem % (H / 8);
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (c0 + kk < k) v = *(const u32x4*)((which ? wsZ : wsP) + (qrow * k + c0 + kk) * H + 8 * c);
-            *(u32x4*)(&W[which][kk * (H + 8) + 8 * c]) = v;
-        }
-        __syncthreads();
-        bool any = false;
-        for (int r = 0; r < kBNC; ++r) any |= rows[r] >= 0;
-        if (!any) continue;                                             // workgroup-uniform
+        const int cn = min(ch + 1, nch - 1);                            // the last chunk reloads itself
+        __syncthreads();                                                // W of ch complete; the other buffer free
+        load_w(cn, wr);
+        // an entry that is not a row (zero weights) adds 0 to the chunk's first
+        // row, so that every atomic instruction is issued
+        const uint64_t vm = __ballot(lane < kBNC && sel[c0 + (lane & 31)] >= 0);
+        const int s_any = __builtin_amdgcn_readfirstlane(vm ? sel[c0 + __builtin_ctzll(vm)] : 0);
 #pragma unroll
         for (int j = 0; j < kTilesPerWave; ++j) {
-            if (j >= ntl) break;                                        // wave-uniform
             const int T = tile0 + j;
-            const uint16_t* wz = W[1] + n * (H + 8) + 8 * hs;           // scale dZ
-            const uint16_t* wp = W[0] + n * (H + 8) + 8 * hs;           // P
+            const uint16_t* wz = W[ch & 1][1] + n * WP + 8 * hs;        // scale dZ
+            const uint16_t* wp = W[ch & 1][0] + n * WP + 8 * hs;        // P
             v16f acc;
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[v] = 0.f;
@@ -349,10 +389,11 @@ void attn_bwd_dkv_kernel(const uint16_t* __restrict__ q, const int32_t* __restri
             const int d = 32 * T + n;
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const int s = rows[8 * (v >> 2) + 4 * hs + (v & 3)];
-                if (s >= 0) unsafeAtomicAdd(dkvb + (int64_t)s * kBQK + d, acc[v]);
+                const int s = sel[c0 + 8 * (v >> 2) + 4 * hs + (v & 3)];
+                unsafeAtomicAdd(dkvb + (int64_t)(s >= 0 ? s : s_any) * kBQK + d, acc[v]);
             }
         }
+        store_w(cn, wr);
     }
 }
 
@@ -398,7 +439,7 @@ hipError_t launch_attn_bwd(const AttnBwdLaunch& a, hipStream_t s)
     if (e != hipSuccess) return e;
     const dim3 g2(a.Lq, a.B, (kDkvTiles + kTilesPerGroup - 1) / kTilesPerGroup);
 #define DSA_DKV(KS)                                                                                           \
-    hipLaunchKernelGGL(attn_bwd_dkv_kernel<KS>, g2, dim3(256), 0, s, (const uint16_t*)a.q, a.idx,             \
+    hipLaunchKernelGGL(attn_bwd_dkv_kernel<KS>, g2, dim3(kDkvThreads), 0, s, (const uint16_t*)a.q, a.idx,     \
                        (const uint16_t*)a.dout, wsP, wsZ, a.dkv, a.Lq, a.Lk, a.k, a.scale)
     switch (a.H / 16) {
     case 1: DSA_DKV(1); break;
