@@ -146,7 +146,11 @@ void attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
     if (nchunks > 0) issue(0);
     for (int ch = 0; ch < nchunks; ++ch) {
         const int c0 = ch * kBNC;
-        wait_vmcnt0();                                                  // this wave's copies of chunk ch
+        // this wave's copies of chunk ch: after them it issued only the two
+        // stores of chunk ch - 1's P and dZ (lane 0 always stores), which
+        // may stay in flight
+        if (ch == 0) wait_vmcnt0();
+        else wait_vmcnt<2>();
         __syncthreads();                                                // everyone's; chunk ch - 1 consumed
         if (ch + 1 < nchunks) issue(ch + 1);
         const uint8_t* cur = ring[ch & 1];
