@@ -358,13 +358,18 @@ void indexer_fp8_row_kernel(const uint8_t* __restrict__ q8, const float* __restr
     // Tile i: A operand = key s_begin + 16 i + (lane % 16), 32-byte slice
     // lane / 16; and the key scales of keys s_begin + 16 i + 4 (lane / 16) + r,
     // which this lane's row of sums will hold.  Both are fetched together so
-    // no load is waited on inside the MFMA step.
+    // no load is waited on inside the MFMA step.  Every step loads a tile
+    // (past the last one: the last one again) and the scores go to LDS, so
+    // the number of memory instructions per step is fixed and the compiler's
+    // waits keep kTileAhead tiles in flight; the row is stored at the end.
+    __shared__ __attribute__((aligned(16))) float sc_lds[kRowKeys];
     struct Tile {
         v8i a;
         float ks[4];
     };
     auto load_tile = [&](int i) -> Tile {
         Tile tl;
+        i = min(i, ntiles - 1);
         const int key = min(s_begin + 16 * i + hcol, Lk - 1);
         const u32x4* p = (const u32x4*)(k8 + ((int64_t)b * Lk + key) * kD + grp * 32);
         tl.a = as_i8(p[0], p[1]);
@@ -375,17 +380,13 @@ void indexer_fp8_row_kernel(const uint8_t* __restrict__ q8, const float* __restr
     };
     Tile tf[kTileAhead];
 #pragma unroll
-    for (int a = 0; a < kTileAhead; ++a) {
-        const int i = wave + 4 * a;
-        if (i < ntiles) tf[a] = load_tile(i);
-    }
+    for (int a = 0; a < kTileAhead; ++a) tf[a] = load_tile(wave + 4 * a);
     for (int i0 = wave; i0 < ntiles; i0 += 4 * kTileAhead) {
 #pragma unroll
         for (int a = 0; a < kTileAhead; ++a) {
             const int i = i0 + 4 * a;
-            if (i >= ntiles) break;                               // wave-uniform
             const Tile cur = tf[a];
-            if (i + 4 * kTileAhead < ntiles) tf[a] = load_tile(i + 4 * kTileAhead);
+            tf[a] = load_tile(i + 4 * kTileAhead);
             v4f acc = zero;
 #pragma unroll
             for (int h = 0; h < 4; ++h) {
@@ -397,15 +398,19 @@ void indexer_fp8_row_kernel(const uint8_t* __restrict__ q8, const float* __restr
             // sum over the 16 lanes (heads) that share keys 4 (lane / 16) + r
 #pragma unroll
             for (int r = 0; r < 4; ++r) acc[r] = row16_sum(acc[r]);
-            if (hcol == 0) {
-                const int sb = s_begin + 16 * i + 4 * grp;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int s = sb + r;
-                    if (s < s_end) dst[s] = acc[r] * cur.ks[r];
-                }
-            }
+            if (hcol == 0 && i < ntiles)
+                *(v4f*)&sc_lds[16 * i + 4 * grp] =
+                    v4f{acc[0] * cur.ks[0], acc[1] * cur.ks[1], acc[2] * cur.ks[2], acc[3] * cur.ks[3]};
         }
+    }
+    __syncthreads();
+    // keys s_begin .. s_end - 1: 16-byte stores where the row allows
+    const int nk = s_end - s_begin;
+    if (((uintptr_t)(dst + s_begin) & 15u) == 0) {
+        for (int e = tid; e < nk / 4; e += kThreads) *(v4f*)(dst + s_begin + 4 * e) = *(const v4f*)&sc_lds[4 * e];
+        for (int e = (nk & ~3) + tid; e < nk; e += kThreads) dst[s_begin + e] = sc_lds[e];
+    } else {
+        for (int e = tid; e < nk; e += kThreads) dst[s_begin + e] = sc_lds[e];
     }
 }
 
