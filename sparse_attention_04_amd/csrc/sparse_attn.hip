@@ -535,6 +535,169 @@ void sparse_attn_bf16_w32_kernel(const uint16_t* __restrict__ q, const void* __r
     }
 }
 
+// bf16 kernel for rows of D = d_qk = d_v in {64, 128} (the MQA shapes): one
+// workgroup per query row, one wave per 16 heads, v_mfma_f32_16x16x32_bf16.
+//  - The query's index list (k <= 2048) is staged in LDS once; the selected
+//    rows stream through a two-slot LDS ring of 32 rows, copied
+//    asynchronously one chunk ahead, 1 KB (1024 / 2D rows) per copy
+//    instruction.  At 24 KB of LDS six rows share a CU, which hides the
+//    copies' latency better than a deeper ring (four slots measured 1.7x
+//    slower).  Piece p (16 bytes) of row r sits at position
+//    p ^ (r % (D / 8)), so the 16 rows a key-fragment read gathers at one
+//    piece, and the rows of a transpose read, hit distinct banks.
+//  - S^T = K_chunk . Q^T per 16-key tile; element i of lane group g holds
+//    chunk row 16 j + g + 4 i (the key-tile rows are read permuted).
+//  - Online softmax in fp32 (exp2 domain) with the usual rescaling of the
+//    16 x D output accumulators when the running maximum grows.
+//  - O^T += V^T . P^T with K = 32 keys: P^T is the two S^T tiles converted to
+//    bf16 in place, and V^T comes from the row-major chunk through LDS
+//    transpose reads over the same key slots (rows g + 4 q, and 16 more).
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW)
+void sparse_attn_bf16_w16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
+                                 const int32_t* __restrict__ idx, uint16_t* __restrict__ out,
+                                 float* __restrict__ lse, int Lq, int Lk, int t_begin, int H, int k,
+                                 int64_t idx_bstride, float scale_log2)
+{
+    constexpr int NC = 32;                       // rows per chunk
+    constexpr int PPR = D / 8;                   // 16-byte pieces per row
+    constexpr int RPI = 64 / PPR;                // rows per copy instruction
+    constexpr int SLOT = NC * D * 2;             // ring bytes per chunk
+    constexpr int NBUF = 2;                      // ring slots: copies run one chunk ahead
+    constexpr int KMAX = 2048;
+    static_assert(D == 64 || D == 128, "64- or 128-wide rows");
+    __shared__ __attribute__((aligned(16))) uint8_t ring[NBUF][SLOT];
+    __shared__ __attribute__((aligned(16))) int32_t sel[KMAX];
+    __shared__ int wlast[NW];
+
+    const int row = blockIdx.x, b = blockIdx.y;
+    const int t = t_begin + row;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 15, g = lane >> 4, i16 = lane & 15;
+    const int h = wave * 16 + col;
+
+    // Q^T operand: head h, dims 32 c + 8 g .. +8
+    const uint16_t* qrow = q + (((int64_t)b * Lq + t) * H + h) * D;
+    v8bf qf[D / 32];
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) qf[c] = as_bf8(*(const u32x4*)(qrow + 32 * c + 8 * g));
+
+    const int32_t* irow = idx + (int64_t)b * idx_bstride + (int64_t)row * k;
+    int last = -1;
+    for (int i = tid; i < KMAX; i += 64 * NW) {
+        const int sidx = (i < k) ? irow[i] : -1;
+        const bool ok = sidx >= 0 && sidx < Lk;
+        sel[i] = ok ? sidx : -1;
+        last = ok ? i : last;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) last = max(last, __shfl_xor(last, o, kWave));
+    if (lane == 0) wlast[wave] = last;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < NW; ++w) last = max(last, wlast[w]);
+    const int nch = __builtin_amdgcn_readfirstlane((last + NC) / NC);
+
+    const uint16_t* kvb = kv + (int64_t)b * Lk * D;
+    // copies of chunk c: instruction i covers rows RPI i .. RPI i + RPI - 1,
+    // lane l row RPI i + l / PPR, position l % PPR, piece (l % PPR) ^ (row % PPR)
+    auto issue = [&](int c) {
+        const uint32_t base = lds_byte_address(ring[c % NBUF]);
+        for (int i = wave; i < NC / RPI; i += NW) {
+            const int r = RPI * i + lane / PPR;
+            const int sr = max(sel[c * NC + r], 0);
+            const int piece = (lane % PPR) ^ (r % PPR);
+            global_to_lds16_async(kvb + (int64_t)sr * D + 8 * piece,
+                                  __builtin_amdgcn_readfirstlane(base + (uint32_t)(i * 1024)));
+        }
+    };
+    // byte offset of 16-bit column d (multiple of 4) of chunk row r
+    auto off = [](int r, int d) -> uint32_t {
+        return (uint32_t)(r * D * 2 + ((((d >> 3) ^ (r % PPR))) << 4) + 2 * (d & 7));
+    };
+
+    const v4f zero = {0.f, 0.f, 0.f, 0.f};
+    v4f o[D / 16];
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) o[dt] = zero;
+    float m = -INFINITY, l = 0.f;
+
+    if (nch > 0) issue(0);
+    for (int ch = 0; ch < nch; ++ch) {
+        const int c0 = ch * NC;
+        wait_vmcnt0();
+        __syncthreads();                                           // chunk ch landed; chunk ch - 1 consumed
+        if (ch + 1 < nch) issue(ch + 1);                           // into chunk ch - 1's slot
+        const uint8_t* cur = ring[ch % NBUF];
+
+        // S^T tiles
+        v4f st[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int r = 16 * j + 4 * (col & 3) + (col >> 2);
+            v4f a = zero;
+#pragma unroll
+            for (int c = 0; c < D / 32; ++c)
+                a = mfma_bf16_16x16x32(as_bf8(*(const u32x4*)(cur + off(r, 32 * c + 8 * g))), qf[c], a);
+            st[j] = a;
+        }
+        // online softmax of head h over the chunk's rows 16 j + g + 4 i
+        float z[8], mx = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bool valid = sel[c0 + 16 * j + g + 4 * i] >= 0;
+                const float v = valid ? st[j][i] * scale_log2 : -INFINITY;
+                z[4 * j + i] = v;
+                mx = fmaxf(mx, v);
+            }
+        mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+        const float m_new = fmaxf(m, mx);
+        const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m - m_new);
+        float psum = 0.f;
+        uint32_t pb[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float p0 = (z[2 * e] == -INFINITY) ? 0.f : exp2f(z[2 * e] - m_new);
+            const float p1 = (z[2 * e + 1] == -INFINITY) ? 0.f : exp2f(z[2 * e + 1] - m_new);
+            psum += p0 + p1;
+            pb[e] = pack_bf16x2(p0, p1);
+        }
+        psum += __shfl_xor(psum, 16, kWave);
+        psum += __shfl_xor(psum, 32, kWave);
+        l = l * alpha + psum;
+        m = m_new;
+        const v8bf pfrag = as_bf8(u32x4{pb[0], pb[1], pb[2], pb[3]});
+        // O^T tiles: A = V^T over key slots 8 g + q (rows g + 4 q) and
+        // 8 g + 4 + q (rows 16 + g + 4 q), dims 16 dt + col
+        const int rl = g + 4 * (i16 >> 2);
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) {
+            const int d = 16 * dt + 4 * (i16 & 3);
+            const u32x2 lo = __builtin_bit_cast(u32x2, lds_read_tr16(cur + off(rl, d)));
+            const u32x2 hi2 = __builtin_bit_cast(u32x2, lds_read_tr16(cur + off(rl + 16, d)));
+            v4f acc = o[dt];
+            acc[0] *= alpha; acc[1] *= alpha; acc[2] *= alpha; acc[3] *= alpha;
+            o[dt] = mfma_bf16_16x16x32(as_bf8(u32x4{lo[0], lo[1], hi2[0], hi2[1]}), pfrag, acc);
+        }
+    }
+
+    // O^T tile dt: lane (head col, group g) holds dims 16 dt + 4 g .. +3
+    const float inv = (l > 0.f) ? 1.f / l : 0.f;
+    uint16_t* orow = out + (((int64_t)b * Lq + t) * H + h) * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+        const uint32_t w0 = pack_bf16x2(o[dt][0] * inv, o[dt][1] * inv);
+        const uint32_t w1 = pack_bf16x2(o[dt][2] * inv, o[dt][3] * inv);
+        *(u32x2*)(orow + 16 * dt + 4 * g) = u32x2{w0, w1};
+    }
+    if (lse != nullptr && g == 0)
+        lse[((int64_t)b * Lq + t) * H + h] = (l > 0.f) ? (m + log2f(l)) * 0.69314718055994531f : -INFINITY;
+}
+
 // Merge of the split partials: per (b, row, head), the log-sum-exp of the
 // parts and the parts' outputs weighted by exp(lse_z - lse), in fp32, then
 // rounded to bf16.  One thread per 4 output values; the parts are summed in
@@ -754,6 +917,29 @@ hipError_t launch_sparse_attn(const AttnLaunch& a, hipStream_t s)
         hipError_t e = hipSuccess;
         if (a.Dqk == 576 && a.Dv == 512) e = launch_bf16_w32_any<576, 512>(a, s, &handled);
         if (handled) return e;
+    }
+    if (a.bf16 && a.k <= 2048 && a.Dqk == a.Dv && (a.Dqk == 128 || a.Dqk == 64)) {
+        const float scale_log2 = a.scale * 1.4426950408889634f;
+#define DSA_W16(D, NW)                                                                                          \
+        hipLaunchKernelGGL((sparse_attn_bf16_w16_kernel<D, NW>), dim3(a.t_count, a.B), dim3(64 * NW), 0, s,    \
+                           (const uint16_t*)a.q, (const uint16_t*)a.kv, a.idx, (uint16_t*)a.out, a.lse, a.Lq,  \
+                           a.Lk, a.t_begin, a.H, a.k, a.idx_bstride, scale_log2)
+#define DSA_W16_NW(D)                                                                                           \
+        switch (a.H / 16) {                                                                                     \
+        case 1: DSA_W16(D, 1); break;                                                                           \
+        case 2: DSA_W16(D, 2); break;                                                                           \
+        case 3: DSA_W16(D, 3); break;                                                                           \
+        case 4: DSA_W16(D, 4); break;                                                                           \
+        case 5: DSA_W16(D, 5); break;                                                                           \
+        case 6: DSA_W16(D, 6); break;                                                                           \
+        case 7: DSA_W16(D, 7); break;                                                                           \
+        case 8: DSA_W16(D, 8); break;                                                                           \
+        default: return hipErrorInvalidValue;                                                                   \
+        }
+        if (a.Dqk == 128) { DSA_W16_NW(128) } else { DSA_W16_NW(64) }
+#undef DSA_W16_NW
+#undef DSA_W16
+        return hipGetLastError();
     }
     if (a.bf16) {
         if (a.Dqk == 576 && a.Dv == 512) return launch_bf16<576, 512>(a, s);
