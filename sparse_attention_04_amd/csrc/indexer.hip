@@ -32,6 +32,8 @@
 #include "hw.h"
 #include "launch.h"
 
+#include <algorithm>
+
 namespace dsa {
 
 namespace {
@@ -56,7 +58,7 @@ void indexer_fp8_kernel(const uint8_t* __restrict__ q8, const float* __restrict_
                         const uint8_t* __restrict__ k8, const float* __restrict__ k_scale,
                         const float* __restrict__ w, float* __restrict__ scores,
                         int Lq, int Lk, int q_pos0, int t_begin, int t_count,
-                        int64_t sc_bstride, int64_t sc_rstride, int write_masked, int skip_upto_k)
+                        int64_t sc_bstride, int64_t sc_rstride, int write_masked, int skip_upto_k, int gps)
 {
     __shared__ __attribute__((aligned(16))) uint8_t ktile[2][kKG * kD];
     __shared__ __attribute__((aligned(16))) v4f red[2][4][4][kWave];     // [buffer][wave][tile][lane]
@@ -69,6 +71,14 @@ void indexer_fp8_kernel(const uint8_t* __restrict__ q8, const float* __restrict_
     const int rows_here = min(kQB, t_begin + t_count - t0);
     const int tpos_last = q_pos0 + t0 + rows_here - 1;
     if (!write_masked && skip_upto_k > 0 && tpos_last + 1 <= skip_upto_k)
+        return;
+    // Key groups of this block: [g0, g1) of the ngroups its rows need (split
+    // over blockIdx.z when there are few row blocks); a split past the
+    // block's keys has nothing to do.
+    const int ngroups = (tpos_last + 1 + kKG - 1) / kKG;
+    const int g0 = (int)blockIdx.z * gps;
+    const int g1 = min(g0 + gps, ngroups);
+    if (g0 >= g1)
         return;
 
     // The -inf upper triangle.  Block qb writes the masked tail of its mirror
@@ -142,8 +152,6 @@ void indexer_fp8_kernel(const uint8_t* __restrict__ q8, const float* __restrict_
         }
     }
 
-    const int nkeys = tpos_last + 1;
-    const int ngroups = (nkeys + kKG - 1) / kKG;
     const v4f zero = {0.f, 0.f, 0.f, 0.f};
 
     // Keys of group g go global -> LDS by direct copies: chunk p (16 B) of the
@@ -162,7 +170,7 @@ void indexer_fp8_kernel(const uint8_t* __restrict__ q8, const float* __restrict_
             global_to_lds16_async(src, __builtin_amdgcn_readfirstlane(dst));
         }
     };
-    issue_keys(0, 0);
+    issue_keys(g0, g0 & 1);
     wait_vmcnt0();
     __syncthreads();
 
@@ -176,11 +184,11 @@ void indexer_fp8_kernel(const uint8_t* __restrict__ q8, const float* __restrict_
     // Per group: the copy of group g+1 into the other tile slot runs while g
     // is computed; one wait + barrier publishes both the next key tile and
     // this group's partial sums (the reduction buffer is double-buffered too).
-    for (int g = 0; g < ngroups; ++g) {
+    for (int g = g0; g < g1; ++g) {
         const int s0 = g * kKG;
         const int kb = g & 1;
         const uint8_t* kt = ktile[kb];
-        if (g + 1 < ngroups) issue_keys(g + 1, kb ^ 1);
+        if (g + 1 < g1) issue_keys(g + 1, kb ^ 1);
         // key scales of the four keys this thread finishes after the barrier,
         // fetched now so the epilogue does not wait on memory
         const int sb = s0 + wave * 16 + grp * 4;
@@ -278,9 +286,10 @@ void indexer_fp8_kernel(const uint8_t* __restrict__ q8, const float* __restrict_
         }
     }
 
-    if (write_masked) {
+    if (write_masked && g1 == ngroups) {
         // what is left of the mirror tail after one 64-column slice per group
-        // (16-byte stores where the row allows, the ragged end one by one)
+        // (16-byte stores where the row allows, the ragged end one by one;
+        // the split holding the last group writes it)
         const int s_from = mfrom + ngroups * kKG;
         const v4f ninf = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
         for (int r = 0; r < rows_m; ++r) {
@@ -465,11 +474,19 @@ hipError_t launch_indexer(const IndexerLaunch& a, hipStream_t s)
                            a.scores, a.Lq, a.Lk, a.q_pos0, a.t_begin,
                            a.sc_bstride, a.sc_rstride, (int)a.write_masked, a.skip_upto_k);
     } else if (a.fp8) {
+        // With fewer than 1024 row blocks the keys are split as well, so that
+        // about 1024 workgroups run and the longest block's chain of key
+        // groups is cut (splits past a block's keys return at once).
         const int nqb = (a.t_count + kQB - 1) / kQB;
-        hipLaunchKernelGGL(indexer_fp8_kernel, dim3(nqb, a.B), dim3(kThreads), 0, s,
+        const int gmax = (int)(((int64_t)a.q_pos0 + a.t_begin + a.t_count + kKG - 1) / kKG);
+        const int64_t blocks = (int64_t)nqb * a.B;
+        int nz = blocks >= 1024 ? 1 : (int)std::min<int64_t>((1024 + blocks - 1) / blocks, gmax);
+        const int gps = (gmax + nz - 1) / nz;
+        nz = (gmax + gps - 1) / gps;
+        hipLaunchKernelGGL(indexer_fp8_kernel, dim3(nqb, a.B, nz), dim3(kThreads), 0, s,
                            (const uint8_t*)a.q, a.q_scale, (const uint8_t*)a.k, a.k_scale, a.w,
                            a.scores, a.Lq, a.Lk, a.q_pos0, a.t_begin, a.t_count,
-                           a.sc_bstride, a.sc_rstride, (int)a.write_masked, a.skip_upto_k);
+                           a.sc_bstride, a.sc_rstride, (int)a.write_masked, a.skip_upto_k, gps);
     } else {
         const size_t shm = sizeof(float) * ((size_t)a.H * a.D + a.H);
         hipLaunchKernelGGL(indexer_f32_kernel, dim3(a.t_count, a.B), dim3(kF32Threads), shm, s,
