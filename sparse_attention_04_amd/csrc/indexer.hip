@@ -462,6 +462,8 @@ void indexer_f32_kernel(const float* __restrict__ q, const float* __restrict__ k
 
 }  // namespace
 
+constexpr int64_t kMinBlocks = 1024;    // below this many row blocks the keys are split too
+
 hipError_t launch_indexer(const IndexerLaunch& a, hipStream_t s)
 {
     if (a.B == 0 || a.t_count == 0) return hipSuccess;
@@ -480,7 +482,7 @@ hipError_t launch_indexer(const IndexerLaunch& a, hipStream_t s)
         const int nqb = (a.t_count + kQB - 1) / kQB;
         const int gmax = (int)(((int64_t)a.q_pos0 + a.t_begin + a.t_count + kKG - 1) / kKG);
         const int64_t blocks = (int64_t)nqb * a.B;
-        int nz = blocks >= 1024 ? 1 : (int)std::min<int64_t>((1024 + blocks - 1) / blocks, gmax);
+        int nz = blocks >= kMinBlocks ? 1 : (int)std::min<int64_t>((kMinBlocks + blocks - 1) / blocks, gmax);
         const int gps = (gmax + nz - 1) / nz;
         nz = (gmax + gps - 1) / gps;
         hipLaunchKernelGGL(indexer_fp8_kernel, dim3(nqb, a.B, nz), dim3(kThreads), 0, s,
