@@ -313,7 +313,12 @@ def test_topk_k_beyond_lds_assembly(dsa, k):
 # ------------------------------------------------------------------ attention on crafted index sets
 
 @pytest.mark.parametrize("H,dqk,dv,k", [(128, 576, 512, 2048), (16, 576, 512, 100), (16, 128, 128, 2048),
-                                        (32, 64, 64, 77)])
+                                        (32, 64, 64, 77),
+                                        # 16-head waves at every wave count the 64/128 kernel has (1..8),
+                                        # and k past the LDS index list (the synchronous kernel)
+                                        (48, 64, 64, 2048), (64, 128, 128, 333), (80, 128, 128, 1000),
+                                        (96, 64, 64, 31), (112, 64, 64, 2048), (128, 128, 128, 2048),
+                                        (16, 128, 128, 2500)])
 def test_attention_crafted_sets(dsa, H, dqk, dv, k):
     dev = torch.device("cuda:0")
     g = torch.Generator(device=dev).manual_seed(11)
