@@ -238,6 +238,37 @@ void topk_radix_kernel(const float* __restrict__ scores, int32_t* __restrict__ i
                     for (int e = 0; e < 3; ++e) key[v][e] = own ? px[e] : key[v][e];
         }
     }
+    // A row streamed from memory, in ascending steps: the whole steps of an
+    // aligned row are read kPf steps ahead (the loads are always issued,
+    // clamped to the last whole step, so the compiler's waits keep them in
+    // flight); the partial last step, and every step of an unaligned row,
+    // are read as they come.
+    constexpr int kPf = 4;
+    auto stream_steps = [&](auto&& fn) {
+        const int nfull = vec ? n / kTile : 0;
+        if (nfull > 0) {
+            u32x4 raw[kPf];
+#pragma unroll
+            for (int j = 0; j < kPf; ++j) raw[j] = *(const u32x4*)(src + min(j, nfull - 1) * kTile + tid * 4);
+            for (int st0 = 0; st0 < nfull; st0 += kPf) {
+#pragma unroll
+                for (int u = 0; u < kPf; ++u) {
+                    const int step = st0 + u;
+                    if (step >= nfull) break;                      // workgroup-uniform
+                    uint32_t kk[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) kk[e] = score_key(__uint_as_float(raw[u][e]));
+                    raw[u] = *(const u32x4*)(src + min(step + kPf, nfull - 1) * kTile + tid * 4);
+                    fn(step * kTile + tid * 4, kk);
+                }
+            }
+        }
+        for (int t0 = nfull * kTile; t0 < n; t0 += kTile) {
+            uint32_t kk[4];
+            load4(t0 + tid * 4, kk);
+            fn(t0 + tid * 4, kk);
+        }
+    };
     // fn(step start s0, keys of s0..s0+3) over the whole row, in ascending steps
     auto for_each_step = [&](auto&& fn) {
         if (in_regs) {
@@ -245,11 +276,7 @@ void topk_radix_kernel(const float* __restrict__ scores, int32_t* __restrict__ i
             for (int v = 0; v < kNV; ++v)
                 if (v * kTile < n) fn(v * kTile + tid * 4, key[v]);
         } else {
-            for (int t0 = 0; t0 < n; t0 += kTile) {
-                uint32_t kk[4];
-                load4(t0 + tid * 4, kk);
-                fn(t0 + tid * 4, kk);
-            }
+            stream_steps(fn);
         }
     };
     __syncthreads();                               // zero histogram and counters published
@@ -550,10 +577,7 @@ void topk_radix_kernel(const float* __restrict__ scores, int32_t* __restrict__ i
         }
     } else {
         uint32_t base_gt = 0, base_eq = 0;
-        for (int t0 = 0; t0 < n; t0 += kTile) {
-            const int s0 = t0 + tid * 4;
-            uint32_t kk[4];
-            load4(s0, kk);
+        stream_steps([&](int s0, const uint32_t (&kk)[4]) {
             const uint32_t pk = counts(s0, kk);
             const uint32_t incl = wave_incl_scan(pk, lane);
             if (lane == 63) sh.wtot[0][wave] = incl;
@@ -569,7 +593,7 @@ void topk_radix_kernel(const float* __restrict__ scores, int32_t* __restrict__ i
             place(s0, kk, base_gt + (pre >> 16), base_eq + (pre & 0xFFFFu));
             base_gt += total >> 16;
             base_eq += total & 0xFFFFu;
-        }
+        });
     }
     if (to_lds) {
         __syncthreads();
