@@ -243,6 +243,19 @@ def test_topk_crafted_bit_exact(dsa, case):
     _topk_exact(dsa, s.to(dev).contiguous(), k)
 
 
+@pytest.mark.parametrize("k", [2, 700])
+def test_topk_unaligned_rows(dsa, k):
+    """Rows of an odd length (3001 scores per row, so most rows start off a
+    16-byte boundary and go to the streamed instance) with ties, and k = 2
+    (rows of 3 candidates are neither short nor register-resident)."""
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device="cpu").manual_seed(k)
+    L = 3001
+    s = torch.randint(-20, 20, (1, L, L), generator=g).float() * 0.25
+    s[0, ::2] = torch.randn(L, generator=g)                      # alternate rows without ties
+    _topk_exact(dsa, s.to(dev).contiguous(), k)
+
+
 def test_topk_long_rows(dsa):
     """Rows of 131071 and 131072 candidates (the long-context row length)."""
     dev = torch.device("cuda:0")
