@@ -150,7 +150,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
-              f"the path shards by query rows but no multi-GPU run is part of this build", file=sys.stderr)
+              f"the path shards by query rows, but this program measures a single GPU", file=sys.stderr)
         sys.exit(2)
 
     import torch
