@@ -28,8 +28,8 @@ PEAK_HBM = 8.0e12        # HBM3E bytes/s
 # FETCH_SIZE / WRITE_SIZE runs scaled by a 1 GiB plain copy measured in the same
 # runs (fetch factor 2.0, write factor 1.0).  Valid only for the attention
 # source it was measured on; any other source reports null.
-ATTN_TRAFFIC = {"source_sha256_16": "25ef68cec4253573", "fetch_bytes": 55219754719.0,
-                "write_bytes": 5898303264.0}
+ATTN_TRAFFIC = {"source_sha256_16": "d574ec853ebdf46f", "fetch_bytes": 54871843357.0,
+                "write_bytes": 5892121120.0}
 
 
 def log(*a):
