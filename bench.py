@@ -28,8 +28,8 @@ PEAK_HBM = 8.0e12        # HBM3E bytes/s
 # FETCH_SIZE / WRITE_SIZE runs scaled by a 1 GiB plain copy measured in the same
 # runs (fetch factor 2.0, write factor 1.0).  Valid only for the attention
 # source it was measured on; any other source reports null.
-ATTN_TRAFFIC = {"source_sha256_16": "d574ec853ebdf46f", "fetch_bytes": 54871843357.0,
-                "write_bytes": 5892121120.0}
+ATTN_TRAFFIC = {"source_sha256_16": "d574ec853ebdf46f", "fetch_bytes": 54342329330.0,
+                "write_bytes": 5678485792.0}
 
 
 def log(*a):
@@ -112,6 +112,67 @@ def input_side(cfg, dev, stream, steps):
     return res
 
 
+def training_side(cfg, dev, stream, steps):
+    """The two training-time steps next to the forward, each timed alone on
+    inputs of their own (not part of the forward step):
+      - the indexer distillation loss at L = 8192 (dense attention
+        probabilities of all heads against the FP8 indexer's scores; two
+        Q.K sweeps of 2*H*d_qk FLOP per (query, key) pair, causal);
+      - the sparse-attention backward at L = 4096 over the forward's own
+        selected sets (Q.K, dO.V, dq, and the two dkv products:
+        2*H*(3*d_qk + 2*d_v) FLOP per selected entry)."""
+    import torch
+    import sparse_attention_04_amd as dsa
+    from dsa_inputs import make_inputs
+    res = {}
+    H, dqk, dv = cfg.n_heads, cfg.d_qk, cfg.d_v
+    if cfg.io_dtype != "bf16" or cfg.B != 1:
+        return res
+    # distillation loss
+    L = 8192
+    kc = cfg.with_(name="kl_L8192", Lq=L, Lk=L, q_pos0=0, q_tile_rows=0)
+    inp = make_inputs(kc, seed=1, device=dev)
+    sc = dsa.dsa_indexer_scores(inp["q_idx"], inp["q_scale"], inp["k_idx"], inp["k_scale"], inp["w"],
+                                stream=stream)
+    kl = torch.empty((1, L), dtype=torch.float32, device=dev)
+    f = lambda: dsa.dsa_indexer_kl(inp["q"], inp["kv"], sc, kc.softmax_scale, kl=kl, stream=stream)
+    f()
+    t = time_loop(f, steps, stream)
+    flop = 2.0 * 2 * H * dqk * (L * (L + 1) / 2)
+    res["indexer_kl"] = {"workload": f"L={L}, {H} heads x {dqk}", "ms": t, "bound": "mfma",
+                         "achieved_tflops": flop / (t * 1e-3) / 1e12, "peak_tflops": PEAK_BF16 / 1e12,
+                         "frac": flop / (t * 1e-3) / PEAK_BF16}
+    log(f"[bench] training side indexer_kl: {t:.3f} ms ({res['indexer_kl']['frac'] * 100:.1f}% of bf16 peak)")
+    del inp, sc, kl
+    # sparse-attention backward
+    L = 4096
+    bc = cfg.with_(name="bwd_L4096", Lq=L, Lk=L, q_pos0=0, q_tile_rows=0)
+    inp = make_inputs(bc, seed=2, device=dev)
+    fwd = dsa.Forward(1, L, L, bc.k, H, dv, inp["q"].dtype, dev, d_qk=dqk)
+    fwd(inp["q_idx"], inp["q_scale"], inp["k_idx"], inp["k_scale"], inp["w"], inp["q"], inp["kv"],
+        bc.softmax_scale, stream=stream)
+    g = torch.Generator(device=dev).manual_seed(3)
+    dout = torch.randn(fwd.out.shape, device=dev, generator=g).to(torch.bfloat16)
+    dq = torch.empty((1, L, H, dqk), dtype=torch.float32, device=dev)
+    dkv = torch.empty((1, L, dqk), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(int(dsa.lib.dsa_sparse_attn_bwd_workspace_size(1, L, H, bc.k)), 256), dtype=torch.uint8,
+                     device=dev)
+    f = lambda: dsa.dsa_sparse_attn_bwd(inp["q"], inp["kv"], fwd.idx, fwd.out, fwd.lse, dout, bc.softmax_scale,
+                                        dq=dq, dkv=dkv, workspace=ws, stream=stream)
+    f()
+    t = time_loop(f, steps, stream)
+    n_sel = sum(min(bc.k, tp + 1) for tp in range(L))
+    flop = 2.0 * H * (3 * dqk + 2 * dv) * n_sel
+    res["attn_backward"] = {"workload": f"L={L}, k={bc.k}, {H} heads, selected sets from the forward", "ms": t,
+                            "bound": "atomics (dkv scatter)", "achieved_tflops": flop / (t * 1e-3) / 1e12,
+                            "peak_tflops": PEAK_BF16 / 1e12, "frac": flop / (t * 1e-3) / PEAK_BF16,
+                            "dkv_atomic_adds": n_sel * dqk}
+    log(f"[bench] training side attn_backward: {t:.3f} ms ({res['attn_backward']['frac'] * 100:.1f}% of bf16 peak)")
+    del inp, fwd, dout, dq, dkv, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(cfg, inp, n_rows):
     """The oracle, as it stands, on a uniform sample of query rows."""
     import numpy as np
@@ -146,6 +207,9 @@ def main():
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before timing (counter calibration)")
     ap.add_argument("--no-stages", action="store_true", help="skip the per-stage timing loops")
+    ap.add_argument("--no-training", action="store_true",
+                    help="skip the training-side steps (distillation loss, backward), which also run the forward "
+                         "kernels at their own sizes")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -249,6 +313,8 @@ def main():
         res["e2e_frac_of_floor"] = floor / (ms * 1e-3)
         res["input_side"] = input_side(cfg, dev, stream, max(1, args.steps))
         torch.cuda.empty_cache()
+        if cfg.name == "mla_prefill_L32768" and not args.no_training:
+            res["training_side"] = training_side(cfg, dev, stream, max(1, args.steps))
     if args.cpu_rows > 0:
         log(f"[bench] oracle on {args.cpu_rows} sampled rows")
         res["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_rows)
