@@ -112,6 +112,24 @@ def input_side(cfg, dev, stream, steps):
     return res
 
 
+def measured_mfma_peaks(dev, stream):
+    """MFMA issue-rate probe (the library's dsa_probe_mfma): back-to-back
+    independent MFMAs with operands in registers.  FP8 16x16x128 at two waves
+    per SIMD (the indexer's occupancy) and BF16 32x32x16 at one wave per SIMD
+    (the attention's), each also at eight waves per SIMD."""
+    import torch
+    import sparse_attention_04_amd as dsa
+    sink = torch.empty(256 * 8 * 4 * 4, dtype=torch.float32, device=dev)
+    res = {}
+    for name, kind, wps, iters in (("fp8_2_waves_per_simd", 0, 2, 20000), ("fp8_8_waves_per_simd", 0, 8, 5000),
+                                   ("bf16_1_wave_per_simd", 1, 1, 50000), ("bf16_8_waves_per_simd", 1, 8, 6000)):
+        flop = dsa.dsa_probe_mfma(kind, wps, iters, sink=sink, stream=stream)
+        t = time_loop(lambda: dsa.dsa_probe_mfma(kind, wps, iters, sink=sink, stream=stream), 3, stream)
+        res[name] = flop / (t * 1e-3) / 1e12
+        log(f"[bench] MFMA probe {name}: {res[name]:.0f} TFLOP/s")
+    return res
+
+
 def training_side(cfg, dev, stream, steps):
     """The two training-time steps next to the forward, each timed alone on
     inputs of their own (not part of the forward step):
@@ -311,6 +329,10 @@ def main():
         }
         floor = max(work["indexer_flop"] / PEAK_FP8, 0) + work["topk_bytes"] / PEAK_HBM + work["attn_flop"] / PEAK_BF16
         res["e2e_frac_of_floor"] = floor / (ms * 1e-3)
+        peaks = measured_mfma_peaks(dev, stream)
+        res["measured_mfma_tflops"] = peaks
+        res["indexer_frac_measured_peak"] = work["indexer_flop"] / t_idx / 1e12 / peaks["fp8_2_waves_per_simd"]
+        res["stage_roofline"]["attention"]["frac_measured_peak"] = att / 1e12 / peaks["bf16_1_wave_per_simd"]
         res["input_side"] = input_side(cfg, dev, stream, max(1, args.steps))
         torch.cuda.empty_cache()
         if cfg.name == "mla_prefill_L32768" and not args.no_training:

@@ -322,6 +322,24 @@ dsa_status dsa_rope_assemble(const void* nope, const void* rope, void* out,
                              int B, int L, int heads, int d_nope, int d_rope, int pos0,
                              double rope_base, void* stream);
 
+/* Measurement only (no step of the forward calls it).  The published dense
+ * MFMA peaks assume the matrix units never wait; a kernel whose register or
+ * LDS use allows only one or two waves per SIMD cannot always issue every
+ * cycle.  This probe enqueues on `stream` back-to-back independent MFMAs with
+ * all operands in registers, at `waves_per_simd` (1, 2, 4 or 8) waves per
+ * SIMD on every CU of the current device, `iters` rounds each:
+ *   kind 0: v_mfma_f32_16x16x128_f8f6f4 (e4m3, the indexer's instruction),
+ *           8 per round;
+ *   kind 1: v_mfma_f32_32x32x16_bf16 (the attention's instruction), 4 per
+ *           round.
+ * *flop (host) receives the FLOPs of the launch; the caller times it (events
+ * on `stream`) and divides.  sink: device fp32 [sink_elems], caller-owned,
+ * receives one value per wave; it needs n_cu * waves_per_simd * 4 elements
+ * (DSA_ERR_WORKSPACE if smaller).  Errors: kind or waves_per_simd out of range
+ * → DSA_ERR_UNSUPPORTED; iters outside 1..2^24 → DSA_ERR_SHAPE. */
+dsa_status dsa_probe_mfma(int kind, int waves_per_simd, int iters, float* sink, size_t sink_elems, double* flop,
+                          void* stream);
+
 /* Static description of a status code. */
 const char* dsa_status_string(dsa_status s);
 

@@ -26,6 +26,7 @@ SOURCES = [
     ("inputs.hip", []),
     ("kl.hip", []),
     ("attn_bwd.hip", []),
+    ("probe.hip", []),
 ]
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

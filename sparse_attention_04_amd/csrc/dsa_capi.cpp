@@ -341,6 +341,28 @@ dsa_status dsa_kv_pack_fp8(const void* kv, void* kv_fp8, int64_t n_tok, void* st
     return hip_status(fn, dsa::launch_kv_pack_fp8(a, (hipStream_t)stream));
 }
 
+dsa_status dsa_probe_mfma(int kind, int waves_per_simd, int iters, float* sink, size_t sink_elems, double* flop,
+                          void* stream)
+{
+    const char* fn = "dsa_probe_mfma";
+    if (kind != 0 && kind != 1)
+        return fail(DSA_ERR_UNSUPPORTED, "%s: kind=%d is neither 0 (FP8 16x16x128) nor 1 (BF16 32x32x16)", fn, kind);
+    if (waves_per_simd != 1 && waves_per_simd != 2 && waves_per_simd != 4 && waves_per_simd != 8)
+        return fail(DSA_ERR_UNSUPPORTED, "%s: waves_per_simd=%d is not 1, 2, 4 or 8", fn, waves_per_simd);
+    if (iters < 1 || iters > (1 << 24)) return fail(DSA_ERR_SHAPE, "%s: iters=%d outside 1..2^24", fn, iters);
+    if (flop == nullptr) return fail(DSA_ERR_NULL, "%s: flop is NULL", fn);
+    REQUIRE_PTR(sink);
+    int dev = 0, n_cu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_status(fn, e);
+    const size_t waves = (size_t)n_cu * waves_per_simd * 4;
+    if (sink_elems < waves)
+        return fail(DSA_ERR_WORKSPACE, "%s: sink holds %zu floats, %zu needed", fn, sink_elems, waves);
+    *flop = (double)waves * iters * dsa::mfma_probe_mfmas_per_iter(kind) * dsa::mfma_probe_flop_per_mfma(kind);
+    return hip_status(fn, dsa::launch_mfma_probe(kind, waves_per_simd, iters, n_cu, sink, (hipStream_t)stream));
+}
+
 size_t dsa_forward_workspace_size(int B, int Lq, int Lk, int k, int n_heads, int d_qk, int d_v,
                                   dsa_dtype io_dtype, int q_tile_rows)
 {

@@ -104,6 +104,12 @@ hipError_t launch_rope_assemble(const RopeLaunch& a, hipStream_t s);
 hipError_t launch_kv_pack_fp8(const KvPackLaunch& a, hipStream_t s);
 hipError_t launch_indexer_kl(const KlLaunch& a, hipStream_t s);
 hipError_t launch_attn_bwd(const AttnBwdLaunch& a, hipStream_t s);
+// MFMA issue-rate probe (measurement only): kind 0 = FP8 16x16x128, 1 = BF16
+// 32x32x16; n_cu * waves_per_simd workgroups of four waves; sink holds one
+// float per wave.
+hipError_t launch_mfma_probe(int kind, int waves_per_simd, int iters, int n_cu, float* sink, hipStream_t s);
+int mfma_probe_mfmas_per_iter(int kind);
+double mfma_probe_flop_per_mfma(int kind);
 size_t attn_bwd_workspace_bytes(int B, int Lq, int H, int k);
 
 // Split factor for the selected set when few query rows are attended (1 = no

@@ -179,3 +179,16 @@ def test_rope_assemble_validation(L):
     assert r(base=1.0) == SHAPE and r(base=float("nan")) == SHAPE
     assert r(h=0) == SHAPE and r(p0=-1) == SHAPE and r(B=-1) == SHAPE
     assert r(B=0) == OK and r(L=0) == OK
+
+
+def test_mfma_probe_validation(L):
+    """The MFMA probe checks its arguments before touching the device."""
+    import ctypes
+    flop = ctypes.c_double(0.0)
+    sink = ctypes.c_void_p(1 << 20)   # never dereferenced: every call below fails validation first
+    assert L.dsa_probe_mfma(2, 1, 10, sink, 1 << 16, ctypes.byref(flop), None) == UNSUP
+    assert L.dsa_probe_mfma(0, 3, 10, sink, 1 << 16, ctypes.byref(flop), None) == UNSUP
+    assert L.dsa_probe_mfma(1, 1, 0, sink, 1 << 16, ctypes.byref(flop), None) == SHAPE
+    assert L.dsa_probe_mfma(1, 1, 10, sink, 1 << 16, None, None) == NULL
+    assert L.dsa_probe_mfma(1, 1, 10, None, 1 << 16, ctypes.byref(flop), None) == NULL
+    assert b"dsa_probe_mfma" in L.dsa_last_error()
