@@ -155,7 +155,8 @@ void topk_radix_kernel(const float* __restrict__ scores, int32_t* __restrict__ i
 {
     __shared__ TopkShared sh;
 
-    const int row = row0 + (int)blockIdx.x, b = blockIdx.y;
+    // longest rows first: a causal launch would otherwise end on its longest rows
+    const int row = row0 + (int)(gridDim.x - 1 - blockIdx.x), b = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int t = t_begin + row;
     const int n = q_pos0 + t + 1;                  // candidates s = 0 .. t_pos
