@@ -28,8 +28,8 @@ PEAK_HBM = 8.0e12        # HBM3E bytes/s
 # FETCH_SIZE / WRITE_SIZE runs scaled by a 1 GiB plain copy measured in the same
 # runs (fetch factor 2.0, write factor 1.0).  Valid only for the attention
 # source it was measured on; any other source reports null.
-ATTN_TRAFFIC = {"source_sha256_16": "d574ec853ebdf46f", "fetch_bytes": 53977417774.0,
-                "write_bytes": 5838621216.0}
+ATTN_TRAFFIC = {"source_sha256_16": "d574ec853ebdf46f", "fetch_bytes": 55110908519.0,
+                "write_bytes": 5431578400.0}
 
 
 def log(*a):
