@@ -113,20 +113,28 @@ def input_side(cfg, dev, stream, steps):
 
 
 def measured_mfma_peaks(dev, stream):
-    """MFMA issue-rate probe (the library's dsa_probe_mfma): back-to-back
-    independent MFMAs with operands in registers.  FP8 16x16x128 at two waves
-    per SIMD (the indexer's occupancy) and BF16 32x32x16 at one wave per SIMD
-    (the attention's), each also at eight waves per SIMD."""
+    """MFMA issue rate and shader clock from the measurement probe
+    (measure/libdsa_probe.so): back-to-back independent MFMAs with operands in
+    registers, FP8 16x16x128 at two waves per SIMD (the indexer's occupancy)
+    and BF16 32x32x16 at one wave per SIMD (the attention's), on
+    near-constant and on pseudo-random operands (the clock drops further when
+    the operand bits toggle), and at eight waves per SIMD."""
     import torch
-    import sparse_attention_04_amd as dsa
+    import measure
     sink = torch.empty(256 * 8 * 4 * 4, dtype=torch.float32, device=dev)
+    clocks = torch.zeros(256 * 8 * 2 * 4, dtype=torch.int64, device=dev)
     res = {}
-    for name, kind, wps, iters in (("fp8_2_waves_per_simd", 0, 2, 20000), ("fp8_8_waves_per_simd", 0, 8, 5000),
-                                   ("bf16_1_wave_per_simd", 1, 1, 50000), ("bf16_8_waves_per_simd", 1, 8, 6000)):
-        flop = dsa.dsa_probe_mfma(kind, wps, iters, sink=sink, stream=stream)
-        t = time_loop(lambda: dsa.dsa_probe_mfma(kind, wps, iters, sink=sink, stream=stream), 3, stream)
-        res[name] = flop / (t * 1e-3) / 1e12
-        log(f"[bench] MFMA probe {name}: {res[name]:.0f} TFLOP/s")
+    for name, kind, wps, rnd, iters in (("fp8_2_waves_per_simd", 0, 2, False, 20000),
+                                        ("fp8_2_waves_per_simd_random", 0, 2, True, 20000),
+                                        ("fp8_8_waves_per_simd", 0, 8, False, 5000),
+                                        ("bf16_1_wave_per_simd", 1, 1, False, 50000),
+                                        ("bf16_1_wave_per_simd_random", 1, 1, True, 50000),
+                                        ("bf16_8_waves_per_simd", 1, 8, False, 6000)):
+        f = lambda: measure.probe_mfma(kind, wps, iters, rnd, sink=sink, clocks=clocks, stream=stream)
+        flop = f()
+        t = time_loop(f, 3, stream)
+        res[name] = {"tflops": flop / (t * 1e-3) / 1e12, "clock_ghz": measure.clock_ghz(clocks)}
+        log(f"[bench] MFMA probe {name}: {res[name]['tflops']:.0f} TFLOP/s at {res[name]['clock_ghz']:.2f} GHz")
     return res
 
 
@@ -331,8 +339,10 @@ def main():
         res["e2e_frac_of_floor"] = floor / (ms * 1e-3)
         peaks = measured_mfma_peaks(dev, stream)
         res["measured_mfma_tflops"] = peaks
-        res["indexer_frac_measured_peak"] = work["indexer_flop"] / t_idx / 1e12 / peaks["fp8_2_waves_per_simd"]
-        res["stage_roofline"]["attention"]["frac_measured_peak"] = att / 1e12 / peaks["bf16_1_wave_per_simd"]
+        res["indexer_frac_measured_peak"] = (work["indexer_flop"] / t_idx / 1e12 /
+                                             peaks["fp8_2_waves_per_simd_random"]["tflops"])
+        res["stage_roofline"]["attention"]["frac_measured_peak"] = (att / 1e12 /
+                                                                    peaks["bf16_1_wave_per_simd_random"]["tflops"])
         res["input_side"] = input_side(cfg, dev, stream, max(1, args.steps))
         torch.cuda.empty_cache()
         if cfg.name == "mla_prefill_L32768" and not args.no_training:

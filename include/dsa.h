@@ -231,29 +231,39 @@ dsa_status dsa_sparse_attn_bwd(const void* q, const void* kv, const int32_t* idx
                                float softmax_scale, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Bytes of device workspace dsa_forward needs for these sizes.  q_tile_rows is
- * the number of query rows (per batch entry) whose scores are held at once;
- * 0 picks Lq, or fewer rows when Lq rows of scores would exceed 4 GiB.  The
- * workspace also holds the attention's split partials when
- * dsa_sparse_attn_workspace_size(B, Lq, ...) is non-zero.  Returns 0 for an
- * empty problem.
+ * Bytes of device workspace dsa_forward needs for these sizes: one tile of
+ * B * T * Lk fp32 scores (T = the query-tile rows), the selected sets of all
+ * B * Lq rows (int32, k each), and the attention's split partials when
+ * dsa_sparse_attn_workspace_size(B, Lq, ...) is non-zero.  q_tile_rows = 0
+ * picks T automatically (the largest T whose score tile fits the automatic
+ * tile budget, at most Lq).  Returns 0 for an empty problem.
  */
 size_t dsa_forward_workspace_size(int B, int Lq, int Lk, int k, int n_heads, int d_qk, int d_v,
                                   dsa_dtype io_dtype, int q_tile_rows);
 
 /*
- * The whole forward: scores -> top-k -> sparse attention, processed in tiles of
- * q_tile_rows query rows so that at most B * q_tile_rows * Lk scores exist at
- * once (the full Lq x Lk matrix is never held when q_tile_rows < Lq).
+ * The whole forward ("DeepseekV3.2 拆解", section 核心组件: the output u_t of
+ * query t is the attention of h_t over the latent rows c_s of the tokens whose
+ * indexer scores I[t,s] are among its k largest):
+ *
+ *   out[b,t] = dsa_sparse_attn(q, kv, dsa_topk(dsa_indexer_scores(...), k))[b,t]
+ *
+ * The scores are formed in tiles of q_tile_rows query rows, each tile's top-k
+ * following at once, so that at most B * q_tile_rows * Lk scores exist at a time
+ * (the full Lq x Lk score matrix is never held when q_tile_rows < Lq); the
+ * attention then runs once over every row.  Rows with t_pos + 1 <= k select
+ * every preceding token, so their scores are not computed.
  *
  * Results are identical, bit for bit, to calling dsa_indexer_scores, dsa_topk
- * and dsa_sparse_attn (with its workspace) in turn.  Rows with t_pos + 1 <= k select every
- * preceding token, so their scores are not computed.
+ * and dsa_sparse_attn (with its workspace) in turn on the whole problem, for
+ * every q_tile_rows.
  *
- * Arguments are those of the three calls; idx_out [B,Lq,k] and lse may be NULL.
- * workspace must hold dsa_forward_workspace_size(B, Lq, Lk, k, n_heads, d_qk,
- * d_v, io_dtype, q_tile_rows)
- * bytes, 256-byte aligned; its contents on entry do not matter.
+ * Arguments are those of the three calls; idx_out [B,Lq,k] and lse may be
+ * NULL (without idx_out the selected sets stay in the workspace).  workspace
+ * must hold dsa_forward_workspace_size(B, Lq, Lk, k, n_heads, d_qk, d_v,
+ * io_dtype, q_tile_rows) bytes, 256-byte aligned; its contents on entry do not
+ * matter.  Errors: those of the three calls; DSA_ERR_WORKSPACE for a missing,
+ * short or misaligned workspace; DSA_ERR_SHAPE for q_tile_rows < 0.
  */
 dsa_status dsa_forward(const void* q_idx, const float* q_scale,
                        const void* k_idx, const float* k_scale, const float* w,
@@ -321,24 +331,6 @@ dsa_status dsa_quantize_e4m3(const void* x, dsa_dtype x_dtype, uint8_t* codes, f
 dsa_status dsa_rope_assemble(const void* nope, const void* rope, void* out,
                              int B, int L, int heads, int d_nope, int d_rope, int pos0,
                              double rope_base, void* stream);
-
-/* Measurement only (no step of the forward calls it).  The published dense
- * MFMA peaks assume the matrix units never wait; a kernel whose register or
- * LDS use allows only one or two waves per SIMD cannot always issue every
- * cycle.  This probe enqueues on `stream` back-to-back independent MFMAs with
- * all operands in registers, at `waves_per_simd` (1, 2, 4 or 8) waves per
- * SIMD on every CU of the current device, `iters` rounds each:
- *   kind 0: v_mfma_f32_16x16x128_f8f6f4 (e4m3, the indexer's instruction),
- *           8 per round;
- *   kind 1: v_mfma_f32_32x32x16_bf16 (the attention's instruction), 4 per
- *           round.
- * *flop (host) receives the FLOPs of the launch; the caller times it (events
- * on `stream`) and divides.  sink: device fp32 [sink_elems], caller-owned,
- * receives one value per wave; it needs n_cu * waves_per_simd * 4 elements
- * (DSA_ERR_WORKSPACE if smaller).  Errors: kind or waves_per_simd out of range
- * → DSA_ERR_UNSUPPORTED; iters outside 1..2^24 → DSA_ERR_SHAPE. */
-dsa_status dsa_probe_mfma(int kind, int waves_per_simd, int iters, float* sink, size_t sink_elems, double* flop,
-                          void* stream);
 
 /* Static description of a status code. */
 const char* dsa_status_string(dsa_status s);

@@ -65,10 +65,9 @@ def _load() -> ctypes.CDLL:
     L.dsa_sparse_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, f32,
                                       vp, sz, vp]
     L.dsa_sparse_attn_fp8kv.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, vp, sz, vp]
-    L.dsa_probe_mfma.argtypes = [i32, i32, i32, vp, sz, ctypes.POINTER(f64), vp]
     for fn in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_attn", "dsa_forward", "dsa_quantize_e4m3",
                "dsa_rope_assemble", "dsa_kv_pack_fp8", "dsa_sparse_attn_fp8kv", "dsa_indexer_kl",
-               "dsa_sparse_attn_bwd", "dsa_probe_mfma"):
+               "dsa_sparse_attn_bwd"):
         getattr(L, fn).restype = i32
     L.dsa_status_string.argtypes = [i32]
     L.dsa_status_string.restype = ctypes.c_char_p
@@ -338,16 +337,3 @@ def dsa_sparse_attn_bwd(q, kv, idx, out, lse, dout, softmax_scale: float, q_pos0
         _p(q), _p(kv), _p(idx), _p(out), _p(lse), _p(dout), _p(dq), _p(dkv), B, Lq, Lk, q_pos0, H, Dqk, Dv, k,
         float(softmax_scale), _p(workspace), workspace.numel(), _stream(stream)))
     return dq, dkv
-
-
-def dsa_probe_mfma(kind: int, waves_per_simd: int, iters: int, sink: Optional[torch.Tensor] = None,
-                   stream=None) -> float:
-    """Enqueue the MFMA issue-rate probe (kind 0 = FP8 16x16x128, 1 = BF16
-    32x32x16) at waves_per_simd waves per SIMD; returns the launch's FLOPs.
-    The caller times the launch on `stream`."""
-    if sink is None:
-        sink = torch.empty(256 * 8 * 4 * 4, dtype=torch.float32, device="cuda")
-    flop = ctypes.c_double(0.0)
-    _check("dsa_probe_mfma", lib.dsa_probe_mfma(int(kind), int(waves_per_simd), int(iters), _p(sink), sink.numel(),
-                                                ctypes.byref(flop), _stream(stream)))
-    return flop.value

@@ -26,8 +26,11 @@ SOURCES = [
     ("inputs.hip", []),
     ("kl.hip", []),
     ("attn_bwd.hip", []),
-    ("probe.hip", []),
 ]
+# The measurement-only MFMA / clock probe: a library of its own, which the
+# benchmark loads; the forward path's library does not contain it.
+PROBE_SRC = os.path.join(os.path.dirname(HERE), "measure", "mfma_probe.hip")
+PROBE_LIB = os.path.join(os.path.dirname(HERE), "measure", "libdsa_probe.so")
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     # packed fp32 VALU forms are disabled on purpose: plain v_fma/v_mul only
@@ -47,8 +50,9 @@ def hipcc() -> str:
 
 
 def compile_command(src: str, obj: str, extra=()) -> list:
-    flags = dict(SOURCES)[src]
-    return [hipcc(), *COMMON, *flags, *extra, "-c", "-x", "hip", os.path.join(CSRC, src), "-o", obj]
+    flags = dict(SOURCES).get(src, [])
+    path = src if os.path.isabs(src) else os.path.join(CSRC, src)
+    return [hipcc(), *COMMON, *flags, *extra, "-c", "-x", "hip", path, "-o", obj]
 
 
 def link_command(objs, out: str) -> list:
@@ -74,13 +78,17 @@ def _run(cmds, verbose: bool):
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every source for gfx950 (in parallel) and link libdsa.so."""
+    """Compile every source for gfx950 (in parallel), link libdsa.so and the
+    probe library."""
     os.makedirs(OBJ_DIR, exist_ok=True)
     objs = [os.path.join(OBJ_DIR, os.path.splitext(s)[0] + ".o") for s, _ in SOURCES]
-    _run([compile_command(s, o) for (s, _), o in zip(SOURCES, objs)], verbose)
-    tmp = LIB + ".tmp"
-    _run([link_command(objs, tmp)], verbose)
-    os.replace(tmp, LIB)
+    probe_obj = os.path.join(OBJ_DIR, "mfma_probe.o")
+    _run([compile_command(s, o) for (s, _), o in zip(SOURCES, objs)] + [compile_command(PROBE_SRC, probe_obj)],
+         verbose)
+    for out, ins in ((LIB, objs), (PROBE_LIB, [probe_obj])):
+        tmp = out + ".tmp"
+        _run([link_command(ins, tmp)], verbose)
+        os.replace(tmp, out)
     return LIB
 
 

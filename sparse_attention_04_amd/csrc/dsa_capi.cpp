@@ -138,6 +138,90 @@ int auto_tile_rows(int B, int Lq, int Lk)
 
 size_t round256(size_t x) { return (x + 255u) & ~(size_t)255u; }
 
+// Workspace of the forward for query tiles of T rows: one tile of scores,
+// the selected sets of every row (the attention runs once over all rows
+// after the last tile), and the attention's split partials (decided by the
+// whole problem's rows, as dsa_sparse_attn decides).
+struct ForwardLayout {
+    size_t scores, idx, part, total;
+};
+
+ForwardLayout forward_layout(int B, int Lq, int Lk, int k, int n_heads, int d_qk, int d_v, dsa_dtype io_dtype,
+                             int T)
+{
+    ForwardLayout L{};
+    L.scores = round256((size_t)B * (size_t)T * (size_t)Lk * sizeof(float));
+    L.idx = round256((size_t)B * (size_t)Lq * (size_t)k * sizeof(int32_t));
+    const int ns = dsa::sparse_attn_split((int64_t)B * Lq, n_heads, d_qk, d_v, k, io_dtype == DSA_BF16);
+    L.part = round256(dsa::sparse_attn_split_bytes((int64_t)B * Lq, n_heads, d_v, ns));
+    L.total = L.scores + L.idx + L.part;
+    return L;
+}
+
+dsa_status check_forward(const char* fn, const void* q_idx, const float* q_scale, const void* k_idx,
+                         const float* k_scale, const float* w, int n_idx_heads, int idx_dim, dsa_dtype idx_dtype,
+                         const void* q, const void* kv, int n_heads, int d_qk, int d_v, dsa_dtype io_dtype,
+                         float softmax_scale, int B, int Lq, int Lk, int q_pos0, int k, const int32_t* idx_out,
+                         void* out, float* lse, bool* empty)
+{
+    dsa_status st = check_positions(fn, B, Lq, Lk, q_pos0, empty);
+    if (st != DSA_OK || *empty) return st;
+    st = check_indexer(fn, q_idx, q_scale, k_idx, k_scale, w, n_idx_heads, idx_dim, idx_dtype);
+    if (st != DSA_OK) return st;
+    st = check_k(fn, k, Lk);
+    if (st != DSA_OK) return st;
+    st = check_attn(fn, q, kv, out, lse, n_heads, d_qk, d_v, k, softmax_scale, io_dtype);
+    if (st != DSA_OK) return st;
+    OPTIONAL_PTR(idx_out);
+    return DSA_OK;
+}
+
+// The forward on checked arguments: per tile of T query rows the indexer
+// scores (no masked entries written; rows that select every preceding token
+// skipped) and the top-k into the selected sets of all rows; then one
+// attention launch over every row.  Nothing here allocates: `ws` holds
+// forward_layout(..., T).total bytes.
+dsa_status forward_run(const char* fn, const void* q_idx, const float* q_scale, const void* k_idx,
+                       const float* k_scale, const float* w, int n_idx_heads, int idx_dim, dsa_dtype idx_dtype,
+                       const void* q, const void* kv, int n_heads, int d_qk, int d_v, dsa_dtype io_dtype,
+                       float softmax_scale, int B, int Lq, int Lk, int q_pos0, int k, int32_t* idx_out, void* out,
+                       float* lse, int T, void* ws, hipStream_t s)
+{
+    const ForwardLayout L = forward_layout(B, Lq, Lk, k, n_heads, d_qk, d_v, io_dtype, T);
+    float* ws_scores = (float*)ws;
+    int32_t* idx_all = idx_out ? idx_out : (int32_t*)((char*)ws + L.scores);
+    float* ws_part = (float*)((char*)ws + L.scores + L.idx);
+    const int64_t idx_bstride = (int64_t)Lq * k;
+
+    for (int t0 = 0; t0 < Lq; t0 += T) {
+        const int tc = (Lq - t0 < T) ? (Lq - t0) : T;
+        dsa::IndexerLaunch ia{};
+        ia.q = q_idx; ia.q_scale = q_scale; ia.k = k_idx; ia.k_scale = k_scale; ia.w = w;
+        ia.scores = ws_scores; ia.B = B; ia.Lq = Lq; ia.Lk = Lk; ia.q_pos0 = q_pos0;
+        ia.t_begin = t0; ia.t_count = tc; ia.sc_bstride = (int64_t)T * Lk; ia.sc_rstride = Lk;
+        ia.H = n_idx_heads; ia.D = idx_dim; ia.fp8 = (idx_dtype == DSA_FP8_E4M3);
+        ia.write_masked = false; ia.skip_upto_k = k;
+        hipError_t e = dsa::launch_indexer(ia, s);
+        if (e != hipSuccess) return hip_status(fn, e);
+
+        dsa::TopkLaunch ta{};
+        ta.scores = ws_scores; ta.idx = idx_all + (int64_t)t0 * k; ta.B = B; ta.Lq = Lq; ta.Lk = Lk;
+        ta.q_pos0 = q_pos0; ta.t_begin = t0; ta.t_count = tc; ta.sc_bstride = (int64_t)T * Lk; ta.sc_rstride = Lk;
+        ta.idx_bstride = idx_bstride; ta.k = k;
+        e = dsa::launch_topk(ta, s);
+        if (e != hipSuccess) return hip_status(fn, e);
+    }
+
+    dsa::AttnLaunch aa{};
+    aa.q = q; aa.kv = kv; aa.idx = idx_all; aa.out = out; aa.lse = lse;
+    aa.B = B; aa.Lq = Lq; aa.Lk = Lk; aa.t_begin = 0; aa.t_count = Lq; aa.idx_bstride = idx_bstride;
+    aa.H = n_heads; aa.Dqk = d_qk; aa.Dv = d_v; aa.k = k; aa.scale = softmax_scale;
+    aa.bf16 = (io_dtype == DSA_BF16);
+    aa.nsplit = dsa::sparse_attn_split((int64_t)B * Lq, n_heads, d_qk, d_v, k, aa.bf16);
+    aa.part = aa.nsplit > 1 ? ws_part : nullptr;
+    return hip_status(fn, dsa::launch_sparse_attn(aa, s));
+}
+
 }  // namespace
 
 extern "C" {
@@ -341,40 +425,12 @@ dsa_status dsa_kv_pack_fp8(const void* kv, void* kv_fp8, int64_t n_tok, void* st
     return hip_status(fn, dsa::launch_kv_pack_fp8(a, (hipStream_t)stream));
 }
 
-dsa_status dsa_probe_mfma(int kind, int waves_per_simd, int iters, float* sink, size_t sink_elems, double* flop,
-                          void* stream)
-{
-    const char* fn = "dsa_probe_mfma";
-    if (kind != 0 && kind != 1)
-        return fail(DSA_ERR_UNSUPPORTED, "%s: kind=%d is neither 0 (FP8 16x16x128) nor 1 (BF16 32x32x16)", fn, kind);
-    if (waves_per_simd != 1 && waves_per_simd != 2 && waves_per_simd != 4 && waves_per_simd != 8)
-        return fail(DSA_ERR_UNSUPPORTED, "%s: waves_per_simd=%d is not 1, 2, 4 or 8", fn, waves_per_simd);
-    if (iters < 1 || iters > (1 << 24)) return fail(DSA_ERR_SHAPE, "%s: iters=%d outside 1..2^24", fn, iters);
-    if (flop == nullptr) return fail(DSA_ERR_NULL, "%s: flop is NULL", fn);
-    REQUIRE_PTR(sink);
-    int dev = 0, n_cu = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return hip_status(fn, e);
-    const size_t waves = (size_t)n_cu * waves_per_simd * 4;
-    if (sink_elems < waves)
-        return fail(DSA_ERR_WORKSPACE, "%s: sink holds %zu floats, %zu needed", fn, sink_elems, waves);
-    *flop = (double)waves * iters * dsa::mfma_probe_mfmas_per_iter(kind) * dsa::mfma_probe_flop_per_mfma(kind);
-    return hip_status(fn, dsa::launch_mfma_probe(kind, waves_per_simd, iters, n_cu, sink, (hipStream_t)stream));
-}
-
 size_t dsa_forward_workspace_size(int B, int Lq, int Lk, int k, int n_heads, int d_qk, int d_v,
                                   dsa_dtype io_dtype, int q_tile_rows)
 {
     if (B <= 0 || Lq <= 0 || Lk <= 0 || k <= 0 || q_tile_rows < 0) return 0;
     const int T = q_tile_rows > 0 ? (q_tile_rows < Lq ? q_tile_rows : Lq) : auto_tile_rows(B, Lq, Lk);
-    const size_t scores = round256((size_t)B * (size_t)T * (size_t)Lk * sizeof(float));
-    const size_t idx = round256((size_t)B * (size_t)T * (size_t)k * sizeof(int32_t));
-    // the attention's split partials: decided by the whole problem's rows
-    // (as dsa_sparse_attn decides), sized for one tile
-    const int ns = dsa::sparse_attn_split((int64_t)B * Lq, n_heads, d_qk, d_v, k, io_dtype == DSA_BF16);
-    const size_t part = round256(dsa::sparse_attn_split_bytes((int64_t)B * T, n_heads, d_v, ns));
-    return scores + idx + part;
+    return forward_layout(B, Lq, Lk, k, n_heads, d_qk, d_v, io_dtype, T).total;
 }
 
 dsa_status dsa_forward(const void* q_idx, const float* q_scale, const void* k_idx,
@@ -386,59 +442,19 @@ dsa_status dsa_forward(const void* q_idx, const float* q_scale, const void* k_id
 {
     const char* fn = "dsa_forward";
     bool empty = false;
-    dsa_status st = check_positions(fn, B, Lq, Lk, q_pos0, &empty);
+    dsa_status st = check_forward(fn, q_idx, q_scale, k_idx, k_scale, w, n_idx_heads, idx_dim, idx_dtype, q, kv,
+                                  n_heads, d_qk, d_v, io_dtype, softmax_scale, B, Lq, Lk, q_pos0, k, idx_out, out,
+                                  lse, &empty);
     if (st != DSA_OK || empty) return st == DSA_OK ? ok() : st;
-    st = check_indexer(fn, q_idx, q_scale, k_idx, k_scale, w, n_idx_heads, idx_dim, idx_dtype);
-    if (st != DSA_OK) return st;
-    st = check_k(fn, k, Lk);
-    if (st != DSA_OK) return st;
-    st = check_attn(fn, q, kv, out, lse, n_heads, d_qk, d_v, k, softmax_scale, io_dtype);
-    if (st != DSA_OK) return st;
-    OPTIONAL_PTR(idx_out);
     if (q_tile_rows < 0) return fail(DSA_ERR_SHAPE, "%s: q_tile_rows=%d must be >= 0", fn, q_tile_rows);
     const int T = q_tile_rows > 0 ? (q_tile_rows < Lq ? q_tile_rows : Lq) : auto_tile_rows(B, Lq, Lk);
-    const size_t need = dsa_forward_workspace_size(B, Lq, Lk, k, n_heads, d_qk, d_v, io_dtype, q_tile_rows);
+    const size_t need = forward_layout(B, Lq, Lk, k, n_heads, d_qk, d_v, io_dtype, T).total;
     if (workspace == nullptr || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0)
         return fail(DSA_ERR_WORKSPACE, "%s: workspace needs %zu bytes, 256-byte aligned (got %zu at %p)",
                     fn, need, workspace_bytes, workspace);
-
-    float* ws_scores = (float*)workspace;
-    int32_t* ws_idx = (int32_t*)((char*)workspace + round256((size_t)B * T * (size_t)Lk * sizeof(float)));
-    float* ws_part = (float*)((char*)ws_idx + round256((size_t)B * T * (size_t)k * sizeof(int32_t)));
-    const int nsplit = dsa::sparse_attn_split((int64_t)B * Lq, n_heads, d_qk, d_v, k, io_dtype == DSA_BF16);
-    hipStream_t s = (hipStream_t)stream;
-
-    for (int t0 = 0; t0 < Lq; t0 += T) {
-        const int tc = (Lq - t0 < T) ? (Lq - t0) : T;
-        dsa::IndexerLaunch ia{};
-        ia.q = q_idx; ia.q_scale = q_scale; ia.k = k_idx; ia.k_scale = k_scale; ia.w = w;
-        ia.scores = ws_scores; ia.B = B; ia.Lq = Lq; ia.Lk = Lk; ia.q_pos0 = q_pos0;
-        ia.t_begin = t0; ia.t_count = tc; ia.sc_bstride = (int64_t)T * Lk; ia.sc_rstride = Lk;
-        ia.H = n_idx_heads; ia.D = idx_dim; ia.fp8 = (idx_dtype == DSA_FP8_E4M3);
-        ia.write_masked = false; ia.skip_upto_k = k;
-        hipError_t e = dsa::launch_indexer(ia, s);
-        if (e != hipSuccess) return hip_status(fn, e);
-
-        int32_t* idx_tile = idx_out ? idx_out + (int64_t)t0 * k : ws_idx;
-        const int64_t idx_bstride = idx_out ? (int64_t)Lq * k : (int64_t)T * k;
-        dsa::TopkLaunch ta{};
-        ta.scores = ws_scores; ta.idx = idx_tile; ta.B = B; ta.Lq = Lq; ta.Lk = Lk; ta.q_pos0 = q_pos0;
-        ta.t_begin = t0; ta.t_count = tc; ta.sc_bstride = (int64_t)T * Lk; ta.sc_rstride = Lk;
-        ta.idx_bstride = idx_bstride; ta.k = k;
-        e = dsa::launch_topk(ta, s);
-        if (e != hipSuccess) return hip_status(fn, e);
-
-        dsa::AttnLaunch aa{};
-        aa.q = q; aa.kv = kv; aa.idx = idx_tile; aa.out = out; aa.lse = lse;
-        aa.B = B; aa.Lq = Lq; aa.Lk = Lk; aa.t_begin = t0; aa.t_count = tc; aa.idx_bstride = idx_bstride;
-        aa.H = n_heads; aa.Dqk = d_qk; aa.Dv = d_v; aa.k = k; aa.scale = softmax_scale;
-        aa.bf16 = (io_dtype == DSA_BF16);
-        aa.nsplit = nsplit;
-        aa.part = nsplit > 1 ? ws_part : nullptr;
-        e = dsa::launch_sparse_attn(aa, s);
-        if (e != hipSuccess) return hip_status(fn, e);
-    }
-    return ok();
+    return forward_run(fn, q_idx, q_scale, k_idx, k_scale, w, n_idx_heads, idx_dim, idx_dtype, q, kv, n_heads,
+                       d_qk, d_v, io_dtype, softmax_scale, B, Lq, Lk, q_pos0, k, idx_out, out, lse, T, workspace,
+                       (hipStream_t)stream);
 }
 
 dsa_status dsa_quantize_e4m3(const void* x, dsa_dtype x_dtype, uint8_t* codes, float* scales,

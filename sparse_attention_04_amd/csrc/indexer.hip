@@ -467,7 +467,11 @@ constexpr int64_t kMinBlocks = 1024;    // below this many row blocks the keys a
 hipError_t launch_indexer(const IndexerLaunch& a, hipStream_t s)
 {
     if (a.B == 0 || a.t_count == 0) return hipSuccess;
-    if (a.fp8 && a.t_count < kQB / 2) {
+    // The kernel is chosen by the whole problem's rows per sequence (a.Lq),
+    // never by the tile's: both kernels round a row's sum differently, and a
+    // forward in query-row tiles must give every row the scores the
+    // whole-problem call gives it, whatever the size of its tile.
+    if (a.fp8 && a.Lq < kQB / 2) {
         // few query rows per sequence: split the keys instead of blocking queries
         const int last = a.write_masked ? a.Lk : min(a.Lk, a.q_pos0 + a.t_begin + a.t_count);
         const int nz = (last + kRowKeys - 1) / kRowKeys;

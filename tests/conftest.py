@@ -33,3 +33,20 @@ def pytest_runtest_setup(item):
     # leaves the test id in the log.
     if item.get_closest_marker("gpu") is not None:
         print(f"\n[gpu-case] {item.nodeid}", flush=True)
+
+
+def pytest_terminal_summary(terminalreporter, exitstatus, config):
+    """Print the parity statistics the GPU cases recorded (plain 1e-3
+    relative share of the scores, top-k rows required to match exactly and
+    exempted, largest errors), one line per case, also in quiet runs."""
+    import json
+    try:
+        from tests.parity import STATS
+    except Exception:
+        return
+    if not STATS:
+        return
+    terminalreporter.write_sep("-", "parity statistics")
+    for st in STATS:
+        terminalreporter.write_line(json.dumps({k: (round(v, 6) if isinstance(v, float) else v)
+                                                for k, v in st.items()}))

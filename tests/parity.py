@@ -16,10 +16,18 @@ Tolerances:
                           linear part plus an absolute part stays inside the
                           same bound: each half has weight 1/2 and the linear
                           part's own mass sum_d |c_d k_d| is at most M/2.
+             The floor eps * M is an empirical bound for the FP8 path (the
+             measured worst case with a 2.6x margin), so every comparison
+             also reports the share of scores that meet the plain 1e-3
+             relative bar, and every score of at least 2.5% of its row's
+             largest magnitude must meet that plain bar outright.
   top-k      bit-exact where the oracle's gap (v_k - v_{k+1}) / |v_k| > 1e-3
-             and the gap exceeds twice the absolute score tolerance; every row
-             must be a valid top-k of the oracle's scores within the score
-             tolerance (size, range, order, distinctness, threshold).
+             and the gap exceeds the two elements' absolute score floors
+             eps * (M_k + M_{k+1}) (below that an FP8 ordering flip is within
+             the score tolerance); the rows required to match and the rows
+             exempted by the floor are counted.  Every row must be a valid
+             top-k of the oracle's scores within the score tolerance (size,
+             range, order, distinctness, threshold).
   attention  |o_gpu - o_ref| <= 1e-2 + half a bf16 ulp of o_ref (the output
              must be rounded to bf16); 1e-4 for the fp32 path.  lse within 2e-3.
 """
@@ -43,34 +51,56 @@ def score_tol(ref_rows: np.ndarray, mass_rows: np.ndarray, eps: float) -> np.nda
     return SCORE_RTOL * fin + eps * m
 
 
+BIG_FRAC = 0.025   # scores of at least this share of the row's largest |I| meet 1e-3 relative outright
+
+
 def check_scores(gpu_rows, ref_rows, mass_rows, t_pos, eps, masked_written=True):
     """gpu_rows fp32 [n, Lk]; ref/mass float64 [n, Lk] (-inf past t_pos).
-    Returns the largest err/tol and the largest err/mass seen."""
+
+    Asserts every valid score within the tolerance, and every score with
+    |I_ref| >= 2.5% of its row's largest |I_ref| within plain 1e-3 relative.
+    Returns a dict: err_over_tol (largest err/tol), err_over_mass (largest
+    err/M), frac_plain_rel (share of valid scores within plain 1e-3
+    relative), n_valid, n_big (scores held to the plain bar)."""
     n, Lk = ref_rows.shape
     s = np.arange(Lk)[None, :]
     valid = s <= t_pos[:, None]
     g = gpu_rows.astype(np.float64)
     tol = score_tol(ref_rows, mass_rows, eps)
-    err = np.where(valid, np.abs(np.where(valid, g, 0.0) - np.where(valid, ref_rows, 0.0)), 0.0)
+    ref0 = np.where(valid, ref_rows, 0.0)
+    err = np.where(valid, np.abs(np.where(valid, g, 0.0) - ref0), 0.0)
     bad = err > tol
     ratio = float((err / np.maximum(tol, 1e-300)).max()) if valid.any() else 0.0
     rel_mass = float(np.where(valid, err / np.maximum(np.where(valid, mass_rows, 1.0), 1e-300), 0.0).max())
     assert not bad.any(), (
         f"{int(bad.sum())} score mismatches; worst at {np.unravel_index(np.argmax(err - tol), err.shape)} "
         f"err/tol={ratio:.3g} err/mass={rel_mass:.3g}")
+    plain = err <= SCORE_RTOL * np.abs(ref0)
+    rowmax = np.abs(ref0).max(axis=1, keepdims=True)
+    big = valid & (np.abs(ref0) >= BIG_FRAC * rowmax) & (rowmax > 0)
+    n_valid = int(valid.sum())
+    frac_plain = float(plain[valid].mean()) if n_valid else 1.0
+    big_bad = big & ~plain
+    assert not big_bad.any(), (
+        f"{int(big_bad.sum())} scores of >= {BIG_FRAC} of the row maximum miss plain {SCORE_RTOL} relative; "
+        f"worst rel err {float((err / np.maximum(np.abs(ref0), 1e-300))[big].max()):.3g}")
     if masked_written:
         assert np.all(gpu_rows[~valid] == -np.inf), "masked scores must be -inf"
-    return ratio, rel_mass
+    return {"err_over_tol": ratio, "err_over_mass": rel_mass, "frac_plain_rel": frac_plain, "n_valid": n_valid,
+            "n_big": int(big.sum())}
 
 
 def check_topk_rows(gpu_idx: np.ndarray, ref_scores: np.ndarray, mass_rows: np.ndarray, eps: float,
                     t_pos: np.ndarray, k: int, ref_idx: np.ndarray):
     """End-to-end top-k check against the oracle's float64 scores.
 
-    Returns (exact-match fraction, number of rows required to be exact)."""
+    Returns a dict: exact (share of rows identical to the oracle's), rows,
+    required (rows whose gap makes an exact match mandatory), exempted (rows
+    with gap_rel > 1e-3 whose absolute gap is inside the FP8 score floor)."""
     n_rows = gpu_idx.shape[0]
     exact = 0
     required = 0
+    exempted = 0
     for r in range(n_rows):
         n = int(t_pos[r]) + 1
         g = gpu_idx[r]
@@ -84,13 +114,16 @@ def check_topk_rows(gpu_idx: np.ndarray, ref_scores: np.ndarray, mass_rows: np.n
         if n > k:
             v = ref_scores[r, :n]
             order = np.lexsort((np.arange(n), -np.where(v == 0, 0.0, v)))
-            vk, vk1 = v[order[k - 1]], v[order[k]]
+            sk, sk1 = order[k - 1], order[k]
+            vk, vk1 = v[sk], v[sk1]
             gap = (vk - vk1) / max(abs(vk), 1e-30)
-            atol = eps * mass_rows[r, :n].max()
-            if gap > GAP_EXACT and (vk - vk1) > 2 * atol:
-                required += 1
-                assert same, f"row {r}: gap {gap:.3g} > {GAP_EXACT} but sets differ"
-            tol = SCORE_RTOL * abs(vk) + atol
+            if gap > GAP_EXACT:
+                if (vk - vk1) > eps * (mass_rows[r, sk] + mass_rows[r, sk1]):
+                    required += 1
+                    assert same, f"row {r}: gap {gap:.3g} > {GAP_EXACT} but sets differ"
+                else:
+                    exempted += 1
+            tol = SCORE_RTOL * abs(vk) + eps * mass_rows[r, :n].max()
             mask = np.zeros(n, bool)
             mask[sel] = True
             assert v[mask].min() >= vk - tol, f"row {r}: selected score below threshold"
@@ -98,7 +131,16 @@ def check_topk_rows(gpu_idx: np.ndarray, ref_scores: np.ndarray, mass_rows: np.n
                 assert v[~mask].max() <= vk + tol, f"row {r}: unselected score above threshold"
         else:
             assert np.array_equal(sel, np.arange(n)), f"row {r}: short row must keep every token"
-    return exact / max(n_rows, 1), required
+    return {"exact": exact / max(n_rows, 1), "rows": n_rows, "required": required, "exempted": exempted}
+
+
+# Parity statistics of the cases run in this session, printed at the end of
+# the run (tests/conftest.py) so that a quiet run still records them.
+STATS = []
+
+
+def record(case: str, **kw):
+    STATS.append(dict(case=case, **kw))
 
 
 def bf16_half_ulp(x: np.ndarray) -> np.ndarray:

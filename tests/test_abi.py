@@ -26,7 +26,7 @@ def L():
 def _declared():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(dsa_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(dsa_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_every_declared_symbol_is_exported(L):
@@ -35,6 +35,16 @@ def test_every_declared_symbol_is_exported(L):
             "dsa_forward_workspace_size", "dsa_status_string", "dsa_last_error"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
+
+
+def test_exports_are_the_declared_entry_points(L):
+    """The product library exports exactly the header's entry points (the
+    measurement probe lives in a library of its own)."""
+    import subprocess
+    path = L._name
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True, check=True).stdout
+    exported = sorted({ln.split()[-1] for ln in out.splitlines() if " T " in ln and ln.split()[-1].startswith("dsa_")})
+    assert exported == _declared(), (exported, _declared())
 
 
 def test_status_strings(L):
@@ -125,12 +135,19 @@ def test_attention_split_workspace(L):
     assert ws(0, 8, 128, 576, 512, 2048, BF16) == 0
 
 
+AUTO_TILE_BYTES = 4 << 30      # the forward's automatic query tile: score tile cap
+
+
 def test_forward_workspace(L):
     ws = lambda B, Lq, Lk, k, T: L.dsa_forward_workspace_size(B, Lq, Lk, k, 128, 576, 512, BF16, T)
-    assert ws(1, 32768, 32768, 2048, 0) == 32768 * 32768 * 4 + 32768 * 2048 * 4
-    assert ws(1, 131072, 131072, 2048, 4096) == 4096 * 131072 * 4 + 4096 * 2048 * 4
-    # auto tile caps the score tile at 4 GiB
-    assert ws(1, 131072, 131072, 2048, 0) == 8192 * 131072 * 4 + 8192 * 2048 * 4
+    # one tile of scores plus the selected sets of every row (the attention
+    # runs once over all rows after the last tile)
+    assert ws(1, 32768, 32768, 2048, 1024) == 1024 * 32768 * 4 + 32768 * 2048 * 4
+    assert ws(1, 131072, 131072, 2048, 4096) == 4096 * 131072 * 4 + 131072 * 2048 * 4
+    # auto tile: the largest score tile within AUTO_TILE_BYTES
+    for Lk in (4096, 32768, 131072):
+        T = min(Lk, AUTO_TILE_BYTES // (Lk * 4))
+        assert ws(1, Lk, Lk, 2048, 0) == T * Lk * 4 + Lk * 2048 * 4
     # decode batch: scores, indices and the attention's split partials (4 splits)
     assert ws(64, 1, 65536, 2048, 0) == 64 * 65536 * 4 + 64 * 2048 * 4 + 64 * 4 * 128 * 513 * 4
     assert ws(0, 1, 1, 1, 0) == 0
@@ -179,16 +196,3 @@ def test_rope_assemble_validation(L):
     assert r(base=1.0) == SHAPE and r(base=float("nan")) == SHAPE
     assert r(h=0) == SHAPE and r(p0=-1) == SHAPE and r(B=-1) == SHAPE
     assert r(B=0) == OK and r(L=0) == OK
-
-
-def test_mfma_probe_validation(L):
-    """The MFMA probe checks its arguments before touching the device."""
-    import ctypes
-    flop = ctypes.c_double(0.0)
-    sink = ctypes.c_void_p(1 << 20)   # never dereferenced: every call below fails validation first
-    assert L.dsa_probe_mfma(2, 1, 10, sink, 1 << 16, ctypes.byref(flop), None) == UNSUP
-    assert L.dsa_probe_mfma(0, 3, 10, sink, 1 << 16, ctypes.byref(flop), None) == UNSUP
-    assert L.dsa_probe_mfma(1, 1, 0, sink, 1 << 16, ctypes.byref(flop), None) == SHAPE
-    assert L.dsa_probe_mfma(1, 1, 10, sink, 1 << 16, None, None) == NULL
-    assert L.dsa_probe_mfma(1, 1, 10, None, 1 << 16, ctypes.byref(flop), None) == NULL
-    assert b"dsa_probe_mfma" in L.dsa_last_error()
