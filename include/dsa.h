@@ -277,6 +277,32 @@ dsa_status dsa_forward(const void* q_idx, const float* q_scale,
                        void* stream);
 
 /*
+ * dsa_forward without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  It calls no allocating routine.  Its workspace is a
+ * device array of DSA_NOALLOC_SCRATCH_BYTES inside the library, one per GPU,
+ * held from the first call on that GPU until the process ends.
+ *
+ * Arguments and results are those of dsa_forward (bit for bit the same
+ * output): the query tile is the largest one whose workspace fits the array.
+ * Problems for which even a one-row tile does not fit (B * Lk * 4 bytes of
+ * scores, plus B * Lq * k * 4 for the selected sets when idx_out is NULL,
+ * plus the attention's split partials) return DSA_ERR_UNSUPPORTED before any
+ * launch.  All calls on one GPU share its array: calls that overlap in time
+ * on one GPU (other streams, other host threads) race and must not be made.
+ */
+#define DSA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+
+dsa_status dsa_forward_noalloc(const void* q_idx, const float* q_scale,
+                               const void* k_idx, const float* k_scale, const float* w,
+                               int n_idx_heads, int idx_dim, dsa_dtype idx_dtype,
+                               const void* q, const void* kv,
+                               int n_heads, int d_qk, int d_v, dsa_dtype io_dtype,
+                               float softmax_scale,
+                               int B, int Lq, int Lk, int q_pos0, int k,
+                               int32_t* idx_out, void* out, float* lse, void* stream);
+
+/*
  * Per-token FP8 e4m3 quantisation of the indexer vectors ("DeepseekV3.2 拆解",
  * section 核心组件: the indexer computes in FP8; "DeepSeek模型架构创新解析"
  * section 4.3: enlarge the scale's safety margin, e.g. 1.2x, against FP8

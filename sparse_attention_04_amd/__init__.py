@@ -6,6 +6,8 @@ current stream.  The functions carry the C names:
 
     dsa_indexer_scores, dsa_topk, dsa_sparse_attn,
     dsa_sparse_attn_workspace_size, dsa_forward_workspace_size, dsa_forward,
+    dsa_forward_noalloc                          (no workspace argument; for callers
+                                                  that cannot allocate)
     dsa_quantize_e4m3, dsa_rope_assemble         (input side)
     dsa_kv_pack_fp8, dsa_sparse_attn_fp8kv       (FP8 latent rows)
     dsa_indexer_kl                               (indexer distillation loss)
@@ -28,7 +30,7 @@ LIB_PATH = os.path.join(_HERE, "libdsa.so")
 DSA_F32, DSA_BF16, DSA_FP8_E4M3 = 0, 1, 2
 EXPORTS = ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_attn", "dsa_sparse_attn_workspace_size",
            "dsa_forward_workspace_size",
-           "dsa_forward", "dsa_quantize_e4m3", "dsa_rope_assemble", "dsa_kv_pack_fp8", "dsa_sparse_attn_fp8kv",
+           "dsa_forward", "dsa_forward_noalloc", "dsa_quantize_e4m3", "dsa_rope_assemble", "dsa_kv_pack_fp8", "dsa_sparse_attn_fp8kv",
            "dsa_indexer_kl", "dsa_sparse_attn_bwd_workspace_size", "dsa_sparse_attn_bwd", "dsa_status_string", "dsa_last_error")
 
 
@@ -56,6 +58,10 @@ def _load() -> ctypes.CDLL:
                               i32, i32, i32, i32, i32,
                               vp, vp, vp, i32, vp, sz, vp]
     i64, f64 = ctypes.c_int64, ctypes.c_double
+    L.dsa_forward_noalloc.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32,
+                                      vp, vp, i32, i32, i32, i32, f32,
+                                      i32, i32, i32, i32, i32,
+                                      vp, vp, vp, vp]
     L.dsa_quantize_e4m3.argtypes = [vp, i32, vp, vp, i64, i32, i32, f32, vp]
     L.dsa_rope_assemble.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, f64, vp]
     L.dsa_kv_pack_fp8.argtypes = [vp, vp, i64, vp]
@@ -65,7 +71,8 @@ def _load() -> ctypes.CDLL:
     L.dsa_sparse_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, f32,
                                       vp, sz, vp]
     L.dsa_sparse_attn_fp8kv.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, vp, sz, vp]
-    for fn in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_attn", "dsa_forward", "dsa_quantize_e4m3",
+    for fn in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_attn", "dsa_forward", "dsa_forward_noalloc",
+               "dsa_quantize_e4m3",
                "dsa_rope_assemble", "dsa_kv_pack_fp8", "dsa_sparse_attn_fp8kv", "dsa_indexer_kl",
                "dsa_sparse_attn_bwd"):
         getattr(L, fn).restype = i32
@@ -219,6 +226,34 @@ def dsa_forward(q_idx, q_scale, k_idx, k_scale, w, q, kv, k: int = 2048,
         _p(q), _p(kv), H, Dqk, d_v, _io_dtype(q), float(softmax_scale),
         B, Lq, Lk, q_pos0, k, _p(idx), _p(out), _p(lse), q_tile_rows,
         _p(workspace), workspace.numel(), _stream(stream)))
+    return out, idx, lse
+
+
+# Bytes of the device array dsa_forward_noalloc uses as its workspace
+# (DSA_NOALLOC_SCRATCH_BYTES in include/dsa.h).
+NOALLOC_SCRATCH_BYTES = 128 << 20
+
+
+def dsa_forward_noalloc(q_idx, q_scale, k_idx, k_scale, w, q, kv, k: int = 2048,
+                        softmax_scale: Optional[float] = None, q_pos0: int = 0,
+                        out: Optional[torch.Tensor] = None, idx: Optional[torch.Tensor] = None,
+                        lse: Optional[torch.Tensor] = None, d_v: Optional[int] = None, stream=None):
+    """dsa_forward with the library's own device array as workspace (no
+    workspace argument, nothing allocated by the library).  Outputs not given
+    are allocated here by torch.  Returns (out, idx, lse)."""
+    B, Lq, HI, DI = q_idx.shape
+    Lk = k_idx.shape[1]
+    _, _, H, Dqk = q.shape
+    if d_v is None:
+        d_v = out.shape[-1] if out is not None else Dqk
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(Dqk)
+    if out is None:
+        out = torch.empty((B, Lq, H, d_v), dtype=q.dtype, device=q.device)
+    _check("dsa_forward_noalloc", lib.dsa_forward_noalloc(
+        _p(q_idx), _p(q_scale), _p(k_idx), _p(k_scale), _p(w), HI, DI, _idx_dtype(q_idx),
+        _p(q), _p(kv), H, Dqk, d_v, _io_dtype(q), float(softmax_scale),
+        B, Lq, Lk, q_pos0, k, _p(idx), _p(out), _p(lse), _stream(stream)))
     return out, idx, lse
 
 

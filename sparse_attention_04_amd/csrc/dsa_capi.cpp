@@ -4,10 +4,12 @@
 // thread-local buffer.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/dsa.h"
 #include "launch.h"
@@ -147,11 +149,11 @@ struct ForwardLayout {
 };
 
 ForwardLayout forward_layout(int B, int Lq, int Lk, int k, int n_heads, int d_qk, int d_v, dsa_dtype io_dtype,
-                             int T)
+                             int T, bool idx_in_workspace = true)
 {
     ForwardLayout L{};
     L.scores = round256((size_t)B * (size_t)T * (size_t)Lk * sizeof(float));
-    L.idx = round256((size_t)B * (size_t)Lq * (size_t)k * sizeof(int32_t));
+    L.idx = idx_in_workspace ? round256((size_t)B * (size_t)Lq * (size_t)k * sizeof(int32_t)) : 0;
     const int ns = dsa::sparse_attn_split((int64_t)B * Lq, n_heads, d_qk, d_v, k, io_dtype == DSA_BF16);
     L.part = round256(dsa::sparse_attn_split_bytes((int64_t)B * Lq, n_heads, d_v, ns));
     L.total = L.scores + L.idx + L.part;
@@ -187,7 +189,7 @@ dsa_status forward_run(const char* fn, const void* q_idx, const float* q_scale, 
                        float softmax_scale, int B, int Lq, int Lk, int q_pos0, int k, int32_t* idx_out, void* out,
                        float* lse, int T, void* ws, hipStream_t s)
 {
-    const ForwardLayout L = forward_layout(B, Lq, Lk, k, n_heads, d_qk, d_v, io_dtype, T);
+    const ForwardLayout L = forward_layout(B, Lq, Lk, k, n_heads, d_qk, d_v, io_dtype, T, idx_out == nullptr);
     float* ws_scores = (float*)ws;
     int32_t* idx_all = idx_out ? idx_out : (int32_t*)((char*)ws + L.scores);
     float* ws_part = (float*)((char*)ws + L.scores + L.idx);
@@ -220,6 +222,38 @@ dsa_status forward_run(const char* fn, const void* q_idx, const float* q_scale, 
     aa.nsplit = dsa::sparse_attn_split((int64_t)B * Lq, n_heads, d_qk, d_v, k, aa.bf16);
     aa.part = aa.nsplit > 1 ? ws_part : nullptr;
     return hip_status(fn, dsa::launch_sparse_attn(aa, s));
+}
+
+// The no-allocation forward's workspace: a file-scope device array, one copy
+// per GPU the library runs on, held until the process ends.  In host code
+// `scratch` names a host-side stand-in, never a device address: its device
+// address is looked up once per device (hipGetSymbolAddress, with that device
+// current) and only that address is passed to kernels.
+static __device__ __align__(256) uint8_t scratch[DSA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array, looked up on the
+// first use on that device.
+dsa_status scratch_address(const char* fn, void** ptr)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(DSA_ERR_HIP, "%s: hipGetDevice: %s", fn, hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(DSA_ERR_UNSUPPORTED, "%s: device %d out of range", fn, dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr)
+            return fail(DSA_ERR_HIP, "%s: hipGetSymbolAddress(scratch) on device %d: %s", fn, dev,
+                        hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return DSA_OK;
 }
 
 }  // namespace
@@ -454,6 +488,39 @@ dsa_status dsa_forward(const void* q_idx, const float* q_scale, const void* k_id
                     fn, need, workspace_bytes, workspace);
     return forward_run(fn, q_idx, q_scale, k_idx, k_scale, w, n_idx_heads, idx_dim, idx_dtype, q, kv, n_heads,
                        d_qk, d_v, io_dtype, softmax_scale, B, Lq, Lk, q_pos0, k, idx_out, out, lse, T, workspace,
+                       (hipStream_t)stream);
+}
+
+dsa_status dsa_forward_noalloc(const void* q_idx, const float* q_scale, const void* k_idx, const float* k_scale,
+                               const float* w, int n_idx_heads, int idx_dim, dsa_dtype idx_dtype, const void* q,
+                               const void* kv, int n_heads, int d_qk, int d_v, dsa_dtype io_dtype,
+                               float softmax_scale, int B, int Lq, int Lk, int q_pos0, int k, int32_t* idx_out,
+                               void* out, float* lse, void* stream)
+{
+    const char* fn = "dsa_forward_noalloc";
+    bool empty = false;
+    dsa_status st = check_forward(fn, q_idx, q_scale, k_idx, k_scale, w, n_idx_heads, idx_dim, idx_dtype, q, kv,
+                                  n_heads, d_qk, d_v, io_dtype, softmax_scale, B, Lq, Lk, q_pos0, k, idx_out, out,
+                                  lse, &empty);
+    if (st != DSA_OK || empty) return st == DSA_OK ? ok() : st;
+    // the largest query tile (at most the automatic one) whose workspace fits
+    // the scratch array; the result does not depend on the tile
+    const bool idx_ws = idx_out == nullptr;
+    const size_t cap = (size_t)DSA_NOALLOC_SCRATCH_BYTES;
+    const ForwardLayout fixed = forward_layout(B, Lq, Lk, k, n_heads, d_qk, d_v, io_dtype, 0, idx_ws);
+    const size_t per_row = (size_t)B * (size_t)Lk * sizeof(float);
+    if (fixed.total + round256(per_row) > cap)
+        return fail(DSA_ERR_UNSUPPORTED,
+                    "%s: even a one-row query tile needs %zu bytes of workspace, above the %zu-byte scratch array "
+                    "(pass idx_out, or use dsa_forward with a caller workspace)",
+                    fn, fixed.total + round256(per_row), cap);
+    int T = (int)std::min<size_t>((cap - fixed.total) / per_row, (size_t)auto_tile_rows(B, Lq, Lk));
+    while (T > 1 && forward_layout(B, Lq, Lk, k, n_heads, d_qk, d_v, io_dtype, T, idx_ws).total > cap) --T;
+    void* ws = nullptr;
+    st = scratch_address(fn, &ws);
+    if (st != DSA_OK) return st;
+    return forward_run(fn, q_idx, q_scale, k_idx, k_scale, w, n_idx_heads, idx_dim, idx_dtype, q, kv, n_heads,
+                       d_qk, d_v, io_dtype, softmax_scale, B, Lq, Lk, q_pos0, k, idx_out, out, lse, T, ws,
                        (hipStream_t)stream);
 }
 
