@@ -3,16 +3,20 @@
 
 One step = one fused forward (lightning-indexer scores -> top-k -> sparse
 attention) over one batch of synthetic inputs already resident in HBM.  The
-default workload is MLA-style prefill at L = 32768, k = 2048 (64 indexer heads
+headline workload is MLA-style prefill at L = 32768, k = 2048 (64 indexer heads
 x 128 in FP8 e4m3; 128 query heads over 576-wide bf16 latent rows, value width
-512, softmax scale 1/sqrt(192)).
+512, softmax scale 1/sqrt(192)).  After it, the other four workloads (tiny
+fp32 L = 256, L = 4096 MQA, decode 64 x 65536, L = 131072 in query tiles of
+4096) are timed the same way and reported under "workloads", each stage
+against the roofline that bounds it; the CPU oracle is timed on a bounded
+sample of every workload.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
 import argparse
 import json
-import math
 import os
+import statistics
 import sys
 import time
 
@@ -22,9 +26,16 @@ sys.path.insert(0, ROOT)
 METRIC = "DSA prefill tokens/s at L=32K,k=2048 (1 GPU); indexer % FP8 MFMA peak"
 PEAK_FP8 = 5.0e15        # dense FP8 MFMA, MI355X
 PEAK_BF16 = 2.5e15       # dense BF16 MFMA, MI355X
+PEAK_FP32 = 157.3e12     # fp32 vector ALU, MI355X
 PEAK_HBM = 8.0e12        # HBM3E bytes/s
+HEADLINE = "mla_prefill_L32768"
+OTHER_WORKLOADS = ("tiny_fp32_L256", "prefill_L4096", "decode_B64_ctx65536", "prefill_L131072")
+# oracle sample per workload: query rows (prefill, evenly spaced over the
+# sequence) or sequences (decode); chosen for a few seconds of CPU work each
+ORACLE_SAMPLE = {"tiny_fp32_L256": 256, "prefill_L4096": 128, HEADLINE: 384, "decode_B64_ctx65536": 12,
+                 "prefill_L131072": 48}
 
-# HBM traffic of one attention launch at the bench workload, from rocprofv3
+# HBM traffic of one attention launch at the headline workload, from rocprofv3
 # FETCH_SIZE / WRITE_SIZE runs scaled by a 1 GiB plain copy measured in the same
 # runs (fetch factor 2.0, write factor 1.0).  Valid only for the attention
 # source it was measured on; any other source reports null.
@@ -37,17 +48,63 @@ def log(*a):
 
 
 def algorithmic(cfg):
-    """Algorithmic work of one forward (causal, no credit for masked work)."""
-    t_pos = [cfg.q_pos0 + t for t in range(cfg.Lq)]
+    """Algorithmic work of one forward (causal, no credit for masked work)
+    and the bytes each stage must move at least."""
+    t_pos = range(cfg.q_pos0, cfg.q_pos0 + cfg.Lq)
     n_all = cfg.B * sum(tp + 1 for tp in t_pos)
     n_sel = cfg.B * sum(min(cfg.k, tp + 1) for tp in t_pos)
     n_topk_read = cfg.B * sum(tp + 1 for tp in t_pos if tp + 1 > cfg.k)
+    idx_bytes = 1 if cfg.idx_dtype == "fp8" else 4
+    io_bytes = 2 if cfg.io_dtype == "bf16" else 4
+    rows = cfg.B * cfg.Lq
     return {
+        "rows": rows,
         "indexer_flop": 2.0 * cfg.n_idx_heads * cfg.idx_dim * n_all,
+        # query codes, weights and scales once; every key (and its scale) once
+        "indexer_bytes": float(rows * cfg.n_idx_heads * (cfg.idx_dim * idx_bytes + 8)
+                               + cfg.B * cfg.Lk * (cfg.idx_dim * idx_bytes + 4)),
+        "topk_bytes": 4.0 * n_topk_read + 4.0 * rows * cfg.k,
         "attn_flop": 2.0 * cfg.n_heads * (cfg.d_qk + cfg.d_v) * n_sel,
-        "topk_bytes": 4.0 * n_topk_read + 4.0 * cfg.B * cfg.Lq * cfg.k,
-        "attn_gather_bytes": 2.0 * cfg.d_qk * n_sel,
+        "attn_gather_bytes": float(io_bytes * cfg.d_qk * n_sel),
+        # q and out once, the index lists, the latent rows once
+        "attn_unique_bytes": float(rows * cfg.n_heads * (cfg.d_qk + cfg.d_v) * io_bytes + 4 * rows * cfg.k
+                                   + cfg.B * cfg.Lk * cfg.d_qk * io_bytes),
     }
+
+
+def stage_bounds(cfg, work):
+    """The roofline each stage is measured against, with its algorithmic
+    work: FP8 / BF16 MFMA for the prefill indexer and attention, HBM for the
+    top-k and for the decode indexer and gather, fp32 ALU for the fp32 path."""
+    fp32 = cfg.idx_dtype == "f32"
+    decode = cfg.Lq == 1
+    if fp32:
+        idx = ("alu", work["indexer_flop"], PEAK_FP32, "TFLOP/s")
+        att = ("alu", work["attn_flop"], PEAK_FP32, "TFLOP/s")
+    elif decode:
+        idx = ("hbm", work["indexer_bytes"], PEAK_HBM, "GB/s")
+        att = ("hbm", work["attn_gather_bytes"] + work["attn_unique_bytes"] - cfg.B * cfg.Lk * cfg.d_qk * 2,
+               PEAK_HBM, "GB/s")
+    else:
+        idx = ("mfma", work["indexer_flop"], PEAK_FP8, "TFLOP/s")
+        att = ("mfma", work["attn_flop"], PEAK_BF16, "TFLOP/s")
+    return {"indexer": idx, "topk": ("hbm", work["topk_bytes"], PEAK_HBM, "GB/s"), "attention": att}
+
+
+def stage_roofline(cfg, work, stages_ms):
+    out = {}
+    floor_s = 0.0
+    for name, (bound, amount, peak, unit) in stage_bounds(cfg, work).items():
+        floor = amount / peak
+        floor_s += floor
+        t = stages_ms.get(name)
+        if t is None:
+            continue
+        rate = amount / (t * 1e-3)
+        scale = 1e12 if unit == "TFLOP/s" else 1e9
+        out[name] = {"bound": bound, "achieved": rate / scale, "peak": peak / scale, "unit": unit,
+                     "frac": rate / peak, "floor_ms": floor * 1e3, "ms": t}
+    return out, floor_s
 
 
 def attn_traffic_bytes():
@@ -60,17 +117,23 @@ def attn_traffic_bytes():
     return ATTN_TRAFFIC["fetch_bytes"] + ATTN_TRAFFIC["write_bytes"]
 
 
-def time_loop(fn, steps, stream):
+def time_steps(fn, steps, stream):
+    """Per-call times (ms) of `steps` back-to-back calls, from events recorded
+    on `stream` between the calls; the region is bracketed by device
+    synchronisation."""
     import torch
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(steps):
+    ev[0].record(stream)
+    for i in range(steps):
         fn()
-    e1.record(stream)
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps
+    return [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+
+
+def median_ms(fn, steps, stream):
+    return statistics.median(time_steps(fn, steps, stream))
 
 
 def input_side(cfg, dev, stream, steps):
@@ -105,7 +168,7 @@ def input_side(cfg, dev, stream, steps):
                  ("rope_assemble_kv", lambda: dsa.dsa_rope_assemble(cn, cr, out=co, stream=stream), 4 * co.numel())]
     for name, f, nbytes in jobs:
         f()
-        t = time_loop(f, steps, stream)
+        t = median_ms(f, steps, stream)
         res[name] = {"ms": t, "bytes": nbytes, "achieved_gbs": nbytes / (t * 1e-3) / 1e9,
                      "frac_hbm_peak": nbytes / (t * 1e-3) / PEAK_HBM}
         log(f"[bench] input side {name}: {t:.3f} ms ({res[name]['achieved_gbs']:.0f} GB/s)")
@@ -132,7 +195,7 @@ def measured_mfma_peaks(dev, stream):
                                         ("bf16_8_waves_per_simd", 1, 8, False, 6000)):
         f = lambda: measure.probe_mfma(kind, wps, iters, rnd, sink=sink, clocks=clocks, stream=stream)
         flop = f()
-        t = time_loop(f, 3, stream)
+        t = median_ms(f, 3, stream)
         res[name] = {"tflops": flop / (t * 1e-3) / 1e12, "clock_ghz": measure.clock_ghz(clocks)}
         log(f"[bench] MFMA probe {name}: {res[name]['tflops']:.0f} TFLOP/s at {res[name]['clock_ghz']:.2f} GHz")
     return res
@@ -163,7 +226,7 @@ def training_side(cfg, dev, stream, steps):
     kl = torch.empty((1, L), dtype=torch.float32, device=dev)
     f = lambda: dsa.dsa_indexer_kl(inp["q"], inp["kv"], sc, kc.softmax_scale, kl=kl, stream=stream)
     f()
-    t = time_loop(f, steps, stream)
+    t = median_ms(f, steps, stream)
     flop = 2.0 * 2 * H * dqk * (L * (L + 1) / 2)
     res["indexer_kl"] = {"workload": f"L={L}, {H} heads x {dqk}", "ms": t, "bound": "mfma",
                          "achieved_tflops": flop / (t * 1e-3) / 1e12, "peak_tflops": PEAK_BF16 / 1e12,
@@ -186,7 +249,7 @@ def training_side(cfg, dev, stream, steps):
     f = lambda: dsa.dsa_sparse_attn_bwd(inp["q"], inp["kv"], fwd.idx, fwd.out, fwd.lse, dout, bc.softmax_scale,
                                         dq=dq, dkv=dkv, workspace=ws, stream=stream)
     f()
-    t = time_loop(f, steps, stream)
+    t = median_ms(f, steps, stream)
     n_sel = sum(min(bc.k, tp + 1) for tp in range(L))
     flop = 2.0 * H * (3 * dqk + 2 * dv) * n_sel
     res["attn_backward"] = {"workload": f"L={L}, k={bc.k}, {H} heads, selected sets from the forward", "ms": t,
@@ -199,28 +262,146 @@ def training_side(cfg, dev, stream, steps):
     return res
 
 
-def cpu_baseline(cfg, inp, n_rows):
-    """The oracle, as it stands, on a uniform sample of query rows."""
+def forward_runner(cfg, inp, dev, stream):
+    import sparse_attention_04_amd as dsa
+    fwd = dsa.Forward(cfg.B, cfg.Lq, cfg.Lk, cfg.k, cfg.n_heads, cfg.d_v, inp["q"].dtype, dev, d_qk=cfg.d_qk,
+                      q_tile_rows=cfg.q_tile_rows)
+    run = lambda: fwd(inp["q_idx"], inp.get("q_scale"), inp["k_idx"], inp.get("k_scale"), inp["w"], inp["q"],
+                      inp["kv"], cfg.softmax_scale, q_pos0=cfg.q_pos0, stream=stream)
+    return fwd, run
+
+
+def time_stages(cfg, inp, fwd, dev, stream, steps):
+    """Each stage alone through its own entry point, on the forward's inputs
+    (the attention on the forward's selected sets).  Workloads the forward runs
+    in query tiles time the indexer and the top-k tile by tile (the standalone
+    indexer also writes each tile's masked scores); the attention runs once."""
+    import torch
+    import sparse_attention_04_amd as dsa
+    T = cfg.q_tile_rows if cfg.q_tile_rows > 0 else cfg.Lq
+    tiles = [(t0, min(T, cfg.Lq - t0)) for t0 in range(0, cfg.Lq, T)]
+    assert len(tiles) == 1 or cfg.B == 1
+    scores = torch.empty((cfg.B, T, cfg.Lk), dtype=torch.float32, device=dev)
+    idx = torch.empty((cfg.B, cfg.Lq, cfg.k), dtype=torch.int32, device=dev)
+    out = torch.empty_like(fwd.out)
+    lse = torch.empty_like(fwd.lse)
+    qs = inp.get("q_scale")
+
+    def f_idx():
+        for t0, tc in tiles:
+            dsa.dsa_indexer_scores(inp["q_idx"][:, t0:t0 + tc], None if qs is None else qs[:, t0:t0 + tc],
+                                   inp["k_idx"], inp.get("k_scale"), inp["w"][:, t0:t0 + tc],
+                                   q_pos0=cfg.q_pos0 + t0, scores=scores[:, :tc], stream=stream)
+
+    def f_topk():
+        for t0, tc in tiles:
+            dsa.dsa_topk(scores[:, :tc], cfg.k, q_pos0=cfg.q_pos0 + t0, idx=idx[:, t0:t0 + tc], stream=stream)
+
+    f_attn = lambda: dsa.dsa_sparse_attn(inp["q"], inp["kv"], fwd.idx, cfg.d_v, cfg.softmax_scale,
+                                         q_pos0=cfg.q_pos0, out=out, lse=lse, stream=stream)
+    res = {}
+    for name, f in (("indexer", f_idx), ("topk", f_topk), ("attention", f_attn)):
+        f()
+        res[name] = median_ms(f, steps, stream)
+        log(f"[bench] {cfg.name} stage {name}: {res[name]:.3f} ms")
+    del scores, idx, out, lse
+    return res
+
+
+def cpu_info():
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model, len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(cfg, inp, n_sample):
+    """The oracle, as it stands, on a bounded sample of the workload: query
+    rows evenly spaced over the sequence (prefill) or whole sequences
+    (decode), from the same input bytes (copied to the host).  Each stage is
+    timed on the monotonic clock; tokens/s is the sample's rows over the
+    sample's time."""
     import numpy as np
     import torch
     import oracle
-    rows = np.unique(np.linspace(0, cfg.Lq - 1, n_rows).astype(np.int64))
-    rt = torch.as_tensor(rows, device=inp["q"].device)
-    b = 0
-    qi = inp["q_idx"][b].index_select(0, rt).cpu()
-    qs = inp["q_scale"][b].index_select(0, rt).cpu()
-    w = inp["w"][b].index_select(0, rt).cpu()
-    q = inp["q"][b].index_select(0, rt).cpu()
-    ki, ks, kv = inp["k_idx"][b].cpu(), inp["k_scale"][b].cpu(), inp["kv"][b].cpu()
-    t_pos = cfg.q_pos0 + rows
-    t0 = time.perf_counter()
-    sc = oracle.indexer(qi, qs, ki, ks, w, t_pos, oracle.E4M3)
-    ix = oracle.topk(sc, t_pos, cfg.k)
-    oracle.sparse_attn(q, kv, ix, cfg.d_v, cfg.softmax_scale, oracle.BF16)
-    dt = time.perf_counter() - t0
-    return {"value": len(rows) / dt, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"{len(rows)} query rows evenly spaced over t=0..{cfg.Lq - 1} of the same inputs "
-                      f"(indexer + top-k + attention per row, fp64), {dt:.1f} s"}
+    fp8 = cfg.idx_dtype == "fp8"
+    dt = oracle.E4M3 if fp8 else oracle.F32
+    io = oracle.BF16 if cfg.io_dtype == "bf16" else oracle.F32
+    if cfg.Lq == 1:
+        batches = np.unique(np.linspace(0, cfg.B - 1, min(n_sample, cfg.B)).astype(np.int64))
+        plan = [(int(b), np.array([0])) for b in batches]
+    else:
+        rows = np.unique(np.linspace(0, cfg.Lq - 1, min(n_sample, cfg.Lq)).astype(np.int64))
+        plan = [(0, rows)]
+    st = {"indexer": 0.0, "topk": 0.0, "attention": 0.0}
+    n_rows = 0
+    for b, rows in plan:
+        rt = torch.as_tensor(rows, device=inp["q"].device)
+        host = lambda key: inp[key][b].index_select(0, rt).cpu()
+        qi, w, q = host("q_idx"), host("w"), host("q")
+        qs = host("q_scale") if fp8 else None
+        ki, kv = inp["k_idx"][b].cpu(), inp["kv"][b].cpu()
+        ks = inp["k_scale"][b].cpu() if fp8 else None
+        t_pos = cfg.q_pos0 + rows
+        t0 = time.perf_counter()
+        sc = oracle.indexer(qi, qs, ki, ks, w, t_pos, dt)
+        t1 = time.perf_counter()
+        ix = oracle.topk(sc, t_pos, cfg.k)
+        t2 = time.perf_counter()
+        oracle.sparse_attn(q, kv, ix, cfg.d_v, cfg.softmax_scale, io)
+        t3 = time.perf_counter()
+        st["indexer"] += t1 - t0
+        st["topk"] += t2 - t1
+        st["attention"] += t3 - t2
+        n_rows += len(rows)
+    total = sum(st.values())
+    model, cores = cpu_info()
+    full = n_rows == cfg.B * cfg.Lq
+    what = ("every row" if full else
+            (f"{n_rows} of {cfg.B} sequences" if cfg.Lq == 1 else
+             f"{n_rows} query rows evenly spaced over t=0..{cfg.Lq - 1}"))
+    return {"value": n_rows / total, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{what} of the same inputs (indexer + top-k + attention per row, fp64), {total:.1f} s",
+            "extrapolated": not full, "rows": n_rows, "stage_s": st, "affinity_cpus": cores, "cpu_model": model}
+
+
+def bench_workload(cfg, dev, stream, steps, warmup, want_oracle):
+    """One of the non-headline workloads: forward (median of `steps`), each
+    stage alone against its bound, the oracle on a bounded sample."""
+    import torch
+    from dsa_inputs import make_inputs
+    log(f"[bench] {cfg.name}: drawing inputs")
+    inp = make_inputs(cfg, seed=0, device=dev)
+    torch.cuda.synchronize()
+    work = algorithmic(cfg)
+    fwd, run = forward_runner(cfg, inp, dev, stream)
+    for _ in range(warmup):
+        run()
+    ms = median_ms(run, steps, stream)
+    tokens = cfg.B * cfg.Lq
+    log(f"[bench] {cfg.name}: forward {ms:.3f} ms -> {tokens / (ms * 1e-3):.4g} tokens/s")
+    stages = time_stages(cfg, inp, fwd, dev, stream, steps)
+    roof, floor_s = stage_roofline(cfg, work, stages)
+    res = {"tokens_per_s": tokens / (ms * 1e-3), "ms_per_step": ms, "steps": steps, "tokens": tokens,
+           "config": {"B": cfg.B, "Lq": cfg.Lq, "Lk": cfg.Lk, "q_pos0": cfg.q_pos0, "k": cfg.k,
+                      "n_idx_heads": cfg.n_idx_heads, "idx_dim": cfg.idx_dim, "idx_dtype": cfg.idx_dtype,
+                      "n_heads": cfg.n_heads, "d_qk": cfg.d_qk, "d_v": cfg.d_v, "io_dtype": cfg.io_dtype,
+                      "q_tile_rows": cfg.q_tile_rows},
+           "stages_ms": stages, "stage_roofline": roof, "floor_ms": floor_s * 1e3,
+           "e2e_frac_of_floor": floor_s / (ms * 1e-3)}
+    if want_oracle:
+        log(f"[bench] {cfg.name}: oracle on a sample")
+        res["cpu_baseline"] = cpu_baseline(cfg, inp, ORACLE_SAMPLE[cfg.name])
+        log(f"[bench] {cfg.name}: oracle {res['cpu_baseline']['value']:.3g} tokens/s")
+    del inp, fwd, run
+    torch.cuda.empty_cache()
+    return res
 
 
 def main():
@@ -228,14 +409,16 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="mla_prefill_L32768")
-    ap.add_argument("--cpu-rows", type=int, default=768, help="oracle sample size in query rows (0 = skip)")
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--cpu-rows", type=int, default=ORACLE_SAMPLE[HEADLINE],
+                    help="oracle sample size in query rows of the headline workload (0 = no oracle at all)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before timing (counter calibration)")
     ap.add_argument("--no-stages", action="store_true", help="skip the per-stage timing loops")
     ap.add_argument("--no-training", action="store_true",
                     help="skip the training-side steps (distillation loss, backward), which also run the forward "
                          "kernels at their own sizes")
+    ap.add_argument("--no-workloads", action="store_true", help="skip the other four workloads")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -244,7 +427,6 @@ def main():
         sys.exit(2)
 
     import torch
-    import sparse_attention_04_amd as dsa
     from dsa_inputs import CONFIGS, make_inputs
 
     cfg = CONFIGS[args.workload]
@@ -266,38 +448,17 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    fwd = dsa.Forward(cfg.B, cfg.Lq, cfg.Lk, cfg.k, cfg.n_heads, cfg.d_v, inp["q"].dtype, dev, d_qk=cfg.d_qk,
-                      q_tile_rows=cfg.q_tile_rows)
-    run = lambda: fwd(inp["q_idx"], inp["q_scale"], inp["k_idx"], inp["k_scale"], inp["w"], inp["q"],
-                      inp["kv"], cfg.softmax_scale, q_pos0=cfg.q_pos0, stream=stream)
+    fwd, run = forward_runner(cfg, inp, dev, stream)
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
         run()
     torch.cuda.synchronize()
     log(f"[bench] timing {args.steps} steps")
-    ms = time_loop(run, args.steps, stream)
+    step_ms = time_steps(run, args.steps, stream)
+    ms = statistics.median(step_ms)
     tokens = cfg.B * cfg.Lq
-    log(f"[bench] forward {ms:.3f} ms/step -> {tokens / (ms * 1e-3):.4g} tokens/s")
-
-    stages = {}
-    if not args.no_stages:
-        # each stage alone, on the same stream, same inputs; the attention uses
-        # the forward's own selected sets
-        scores = torch.empty((cfg.B, cfg.Lq, cfg.Lk), dtype=torch.float32, device=dev)
-        idx = torch.empty((cfg.B, cfg.Lq, cfg.k), dtype=torch.int32, device=dev)
-        out = torch.empty_like(fwd.out)
-        lse = torch.empty_like(fwd.lse)
-        f_idx = lambda: dsa.dsa_indexer_scores(inp["q_idx"], inp["q_scale"], inp["k_idx"], inp["k_scale"],
-                                               inp["w"], q_pos0=cfg.q_pos0, scores=scores, stream=stream)
-        f_topk = lambda: dsa.dsa_topk(scores, cfg.k, q_pos0=cfg.q_pos0, idx=idx, stream=stream)
-        f_attn = lambda: dsa.dsa_sparse_attn(inp["q"], inp["kv"], fwd.idx, cfg.d_v, cfg.softmax_scale,
-                                             q_pos0=cfg.q_pos0, out=out, lse=lse, stream=stream)
-        for name, f in (("indexer", f_idx), ("topk", f_topk), ("attention", f_attn)):
-            f()
-            stages[name] = time_loop(f, max(1, args.steps), stream)
-            log(f"[bench] stage {name}: {stages[name]:.3f} ms")
-        del scores, idx, out, lse
-        torch.cuda.empty_cache()
+    log(f"[bench] forward median {ms:.3f} ms/step (mean {statistics.mean(step_ms):.3f}) -> "
+        f"{tokens / (ms * 1e-3):.4g} tokens/s")
 
     res = {
         "metric": METRIC,
@@ -307,6 +468,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms,
+        "ms_per_step_mean": statistics.mean(step_ms),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -316,40 +478,42 @@ def main():
                    "n_idx_heads": cfg.n_idx_heads, "idx_dim": cfg.idx_dim, "n_heads": cfg.n_heads,
                    "d_qk": cfg.d_qk, "d_v": cfg.d_v, "q_tile_rows": cfg.q_tile_rows},
     }
-    if stages:
-        t_att = stages["attention"] * 1e-3
-        t_idx = stages["indexer"] * 1e-3
-        t_tk = stages["topk"] * 1e-3
-        att = work["attn_flop"] / t_att
-        res["roofline"] = {"bound": "mfma", "kernel": "sparse_attn_bf16", "achieved": att / 1e12,
-                           "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s", "frac": att / PEAK_BF16,
-                           "traffic": attn_traffic_bytes() if cfg.name == "mla_prefill_L32768" else None}
-        res["indexer_frac_fp8_peak"] = work["indexer_flop"] / t_idx / PEAK_FP8
+    if not args.no_stages:
+        stages = time_stages(cfg, inp, fwd, dev, stream, max(1, args.steps))
+        torch.cuda.empty_cache()
+        roof, floor_s = stage_roofline(cfg, work, stages)
+        att = roof["attention"]
+        res["roofline"] = {"bound": att["bound"], "kernel": "sparse_attn_bf16_w32", "achieved": att["achieved"],
+                           "peak": att["peak"], "unit": att["unit"], "frac": att["frac"],
+                           "traffic": attn_traffic_bytes() if cfg.name == HEADLINE else None}
+        res["indexer_frac_fp8_peak"] = roof["indexer"]["frac"]
         res["stages_ms"] = stages
-        res["stage_roofline"] = {
-            "indexer": {"bound": "mfma", "achieved_tflops": work["indexer_flop"] / t_idx / 1e12,
-                        "peak_tflops": PEAK_FP8 / 1e12, "frac": work["indexer_flop"] / t_idx / PEAK_FP8},
-            "topk": {"bound": "hbm", "achieved_gbs": work["topk_bytes"] / t_tk / 1e9,
-                     "peak_gbs": PEAK_HBM / 1e9, "frac": work["topk_bytes"] / t_tk / PEAK_HBM},
-            "attention": {"bound": "mfma", "achieved_tflops": att / 1e12, "peak_tflops": PEAK_BF16 / 1e12,
-                          "frac": att / PEAK_BF16,
-                          "gather_tbs": work["attn_gather_bytes"] / t_att / 1e12},
-        }
-        floor = max(work["indexer_flop"] / PEAK_FP8, 0) + work["topk_bytes"] / PEAK_HBM + work["attn_flop"] / PEAK_BF16
-        res["e2e_frac_of_floor"] = floor / (ms * 1e-3)
+        res["stage_roofline"] = roof
+        res["stage_roofline"]["attention"]["gather_tbs"] = work["attn_gather_bytes"] / (stages["attention"] * 1e-3) / 1e12
+        res["floor_ms"] = floor_s * 1e3
+        res["e2e_frac_of_floor"] = floor_s / (ms * 1e-3)
         peaks = measured_mfma_peaks(dev, stream)
-        res["measured_mfma_tflops"] = peaks
-        res["indexer_frac_measured_peak"] = (work["indexer_flop"] / t_idx / 1e12 /
+        res["measured_mfma"] = peaks
+        res["indexer_frac_measured_peak"] = (work["indexer_flop"] / (stages["indexer"] * 1e-3) / 1e12 /
                                              peaks["fp8_2_waves_per_simd_random"]["tflops"])
-        res["stage_roofline"]["attention"]["frac_measured_peak"] = (att / 1e12 /
-                                                                    peaks["bf16_1_wave_per_simd_random"]["tflops"])
+        res["stage_roofline"]["attention"]["frac_measured_peak"] = (
+            att["achieved"] / peaks["bf16_1_wave_per_simd_random"]["tflops"])
         res["input_side"] = input_side(cfg, dev, stream, max(1, args.steps))
         torch.cuda.empty_cache()
-        if cfg.name == "mla_prefill_L32768" and not args.no_training:
+        if cfg.name == HEADLINE and not args.no_training:
             res["training_side"] = training_side(cfg, dev, stream, max(1, args.steps))
     if args.cpu_rows > 0:
         log(f"[bench] oracle on {args.cpu_rows} sampled rows")
         res["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_rows)
+    del inp, fwd, run
+    torch.cuda.empty_cache()
+    if not args.no_workloads and cfg.name == HEADLINE:
+        res["workloads"] = {}
+        for name in OTHER_WORKLOADS:
+            wcfg = CONFIGS[name]
+            steps = max(3, args.steps // 2) if name == "prefill_L131072" else max(1, args.steps)
+            res["workloads"][name] = bench_workload(wcfg, dev, stream, steps, max(1, args.warmup // 2 + 1),
+                                                    args.cpu_rows > 0)
     print(json.dumps(res), flush=True)
 
 
