@@ -23,6 +23,7 @@ SOURCES = [
     ("indexer.hip", ["-mllvm", "-amdgpu-mfma-vgpr-form"]),
     ("topk.hip", []),
     ("sparse_attn.hip", []),
+    ("attn_mla.hip", []),
     ("inputs.hip", []),
     ("kl.hip", []),
     ("attn_bwd.hip", []),

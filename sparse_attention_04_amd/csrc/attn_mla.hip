@@ -1,0 +1,345 @@
+// Sparse MQA attention over the selected latent rows for the MLA shape
+// (576-wide bf16 rows, value = the first 512 columns, 32/64/128 heads, k <=
+// 2048) on gfx950 ("DeepseekV3.2 拆解", section 核心组件: u_t = Attn(h_t,
+// {c_s : s in top-k}); the latent row is key and value because the key
+// up-projection is absorbed into the query, "DeepSeek模型架构创新解析"
+// section 1.1).
+//
+// One workgroup per query row (per split of its selected set for few rows),
+// one wave per 32 heads, v_mfma_f32_32x32x16_bf16 throughout, in the LDS
+// layout of attn_layout.h (value parts at a 1040-byte pitch, tails packed 8
+// rows per 1 KB, S^T row slot m holding chunk row slot_row(m)):
+//  - S^T[32 rows x 32 heads] = K_chunk . Q^T with the query operand (36 steps
+//    of 32 heads x 16 dims) in registers for the whole row;
+//  - softmax in fp32 (exp2 domain) against a per-head reference maximum m
+//    fixed at the first chunk holding a valid row, so O is never rescaled; a
+//    logit more than 64 (log2 units) above m makes the workgroup recompute
+//    the row once with the true maximum;
+//  - O^T[32 dims x 32 heads] += V^T . P^T with P^T the S^T accumulator in
+//    bf16 in place and V^T from LDS transpose reads.
+// The schedule is what differs from the 32-head kernel in sparse_attn.hip,
+// which measured (cycle stamps per chunk and wave) about 680 cycles issuing
+// its row copies in one burst after Q.K and 920 cycles of softmax between
+// Q.K and P.V, of about 4700:
+//  - the ring holds three chunks, and the copies of chunk i+2 are issued one
+//    at a time between the Q.K MFMAs of chunk i, so the CU's memory path
+//    moves them while the matrix units work and they have two iterations to
+//    land;
+//  - the softmax needs no cross-lane step per chunk: each half-wave keeps
+//    its own partial sum and running maximum (combined once per row), and
+//    checks its own logits against m;
+//  - the second half of the softmax (rows of the second 16-key step) runs
+//    between the MFMAs of the first P.V step.
+#include "attn_layout.h"
+#include "hw.h"
+#include "launch.h"
+
+namespace dsa {
+
+namespace {
+
+// Asynchronous 16-byte copy global -> LDS with a wave-uniform 64-bit base in
+// SGPRs and a 32-bit per-lane byte offset (the saddr form, no per-lane 64-bit
+// address arithmetic).  Lane l's 16 bytes land at lds_byte_addr + 16 l; the
+// wave fences it itself (s_waitcnt vmcnt + a barrier before the slot is read).
+__device__ __forceinline__ void global_to_lds16_saddr(const void* sbase, uint32_t voff, uint32_t lds_byte_addr)
+{
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(sbase), "s"(lds_byte_addr)
+                 : "memory");
+}
+
+template <int NW, bool SPLIT>
+__global__ __launch_bounds__(64 * NW)
+void sparse_attn_mla_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
+                            const int32_t* __restrict__ idx, uint16_t* __restrict__ out,
+                            float* __restrict__ lse, int Lq, int Lk, int t_begin, int H, int k,
+                            int64_t idx_bstride, float scale_log2, int cps,
+                            float* __restrict__ part_o, float* __restrict__ part_lse)
+{
+    using S = W32Shape<576, 512, NW>;
+    constexpr int NC = S::NC;
+    constexpr int NBUF = 3;                                   // ring slots
+    constexpr int SPW = S::SPW;                               // copy instructions per wave per chunk
+    constexpr int TPW = S::TI / NW;                           // of which tails
+    __shared__ __attribute__((aligned(16))) uint8_t ring[NBUF][S::BUF_BYTES];
+    __shared__ __attribute__((aligned(16))) int32_t sel[S::KMAX];   // the query's index list (-1 padded)
+    __shared__ int wlast[NW];                                       // per wave: last valid list position
+
+    const int row = blockIdx.x, b = blockIdx.y;
+    const int t = t_begin + row;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+    const int col = lane & 31, hi = lane >> 5;
+    const int h = wave * 32 + col;
+
+    const uint16_t* qrow = q + (((int64_t)b * Lq + t) * H + h) * 576;
+    v8bf qf[S::QC];
+#pragma unroll
+    for (int c = 0; c < S::QC; ++c) qf[c] = as_bf8(*(const u32x4*)(qrow + c * 16 + hi * 8));
+
+    v16f o[S::DT];
+#pragma unroll
+    for (int i = 0; i < S::DT; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[i][v] = 0.f;
+
+    const int32_t* irow = idx + (int64_t)b * idx_bstride + (int64_t)row * k;
+    const uint16_t* kvb = kv + (int64_t)b * Lk * 576;
+    // Stage the index list; entries that cannot be read become -1.  Chunks
+    // past the last valid entry (a short row's -1 padding) are not visited.
+    int last = -1;
+    for (int i = tid; i < S::KMAX; i += 64 * NW) {
+        const int sidx = (i < k) ? irow[i] : -1;
+        const bool ok = sidx >= 0 && sidx < Lk;
+        sel[i] = ok ? sidx : -1;
+        last = ok ? i : last;
+    }
+#pragma unroll
+    for (int o2 = 32; o2 > 0; o2 >>= 1) last = max(last, __shfl_xor(last, o2, kWave));
+    if (lane == 0) wlast[wave] = last;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < NW; ++w) last = max(last, wlast[w]);
+    last = __builtin_amdgcn_readfirstlane(last);                   // workgroup-uniform
+    // Split over the selected set (gridDim.z > 1): this workgroup takes chunks
+    // [c0, c0 + cps) of the list and leaves a normalised partial output and
+    // its log-sum-exp for the merge kernel.
+    const int c0 = (int)blockIdx.z * cps;
+    const int nchunks = max(0, min((last + NC) / NC - c0, cps));   // last = -1: nothing to attend
+
+    // bit r set when entry r of (absolute) chunk c is a real row
+    auto valid_mask = [&](int c) -> uint32_t {
+        return (uint32_t)__ballot(lane < NC && sel[c * NC + (lane & 31)] >= 0);
+    };
+    // Copy sources of this wave's SPW copies of chunk c: RPW value rows (lane
+    // i < RPW holds value row i; a copy takes its row with one lane read) and
+    // TPW tail rows (8 rows per copy, one per group of 8 lanes).  Padding
+    // entries copy row 0; they are masked.
+    struct CopySrc {
+        int vrl;
+        int tr[TPW];
+    };
+    auto copy_src = [&](int c) -> CopySrc {
+        CopySrc cs;
+        const int32_t* rr_ = &sel[c * NC];
+        cs.vrl = max(rr_[wave * S::RPW + (lane % S::RPW)], 0);
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) cs.tr[j] = max(rr_[8 * (wave * TPW + j) + (lane >> 3)], 0);
+        return cs;
+    };
+    // copy number j (< SPW) of chunk c into its ring slot
+    auto issue_copy = [&](const CopySrc& cs, int c, int j) {
+        const uint32_t base = lds_byte_address(ring[c % NBUF]);
+        if (j < S::RPW) {
+            const int r = wave * S::RPW + j;
+            const int sr = __builtin_amdgcn_readlane(cs.vrl, j);
+            // the row's address as a wave-uniform (scalar) 64-bit base
+            const uint64_t ga = (uint64_t)(uintptr_t)(kvb + (int64_t)sr * 576);
+            const uint32_t glo = __builtin_amdgcn_readfirstlane((uint32_t)ga);
+            const uint32_t ghi = __builtin_amdgcn_readfirstlane((uint32_t)(ga >> 32));
+            global_to_lds16_saddr((const void*)(uintptr_t)(((uint64_t)ghi << 32) | glo), (uint32_t)lane * 16u,
+                                  __builtin_amdgcn_readfirstlane(base + (uint32_t)r * S::VPITCH));
+        } else {
+            const int jj = j - S::RPW;
+            const int ti = wave * TPW + jj;                  // tail instruction: rows 8*ti .. 8*ti+7
+            const int r = 8 * ti + (lane >> 3);
+            const int piece = (lane & 7) ^ (r & 7);
+            global_to_lds16_async(kvb + (int64_t)cs.tr[jj] * 576 + 512 + piece * 8,
+                                  __builtin_amdgcn_readfirstlane(base + (uint32_t)(S::VBYTES + ti * 1024)));
+        }
+    };
+    auto issue_chunk = [&](int c) {
+        const CopySrc cs = copy_src(c);
+#pragma unroll
+        for (int j = 0; j < SPW; ++j) issue_copy(cs, c, j);
+    };
+
+    const int krow_i = slot_row(col);
+    const int tsw = krow_i & 7;
+    const int js = (lane & 15) >> 2, qs = lane & 3, g2 = (lane >> 4) & 1;
+    constexpr float kHeadroom = 64.f;                        // log2 units
+    constexpr int kPre = 6;                                  // key fragments read ahead of their MFMA
+    constexpr int kPvPre = 2;                                // V^T fragments read ahead of their MFMA
+    float m = -INFINITY;                                     // reference maximum (log2 domain), per head
+    float l = 0.f;                                           // this half-wave's sum of p
+    float m_seen = -INFINITY;                                // this half-wave's largest logit (log2 domain)
+    for (int pass = 0; pass < 2; ++pass) {
+        bool overflow = false;
+        if (nchunks > 0) issue_chunk(c0);
+        if (nchunks > 1) issue_chunk(c0 + 1);
+        for (int it = 0; it < nchunks; ++it) {
+            if (it + 1 < nchunks) wait_vmcnt<SPW>();         // chunk it landed; chunk it+1 may be in flight
+            else wait_vmcnt0();
+            __syncthreads();                                 // ... for every wave; chunk it-1 consumed
+            const int c = c0 + it;
+            const uint8_t* cur = ring[c % NBUF];
+            const bool copies = it + 2 < nchunks;            // chunk it+2 goes into chunk it-1's slot
+            CopySrc cs;
+            if (copies) cs = copy_src(c + 2);
+
+            // S^T (32 rows x 32 heads).  Step c2 < 32 reads value-part piece
+            // 2*c2 + hi of row slot_row(col); later steps read the tail.  Copy
+            // j of chunk it+2 is issued after MFMA 36 j / SPW (every step has one
+            // when a wave copies 36 pieces per chunk).
+            v16f sacc;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) sacc[v] = 0.f;
+            {
+                const uint8_t* vrow = cur + krow_i * S::VPITCH + hi * 16;
+                const uint8_t* trw = cur + S::VBYTES + krow_i * (S::TP * 16);
+                auto kfrag = [&](int c2) -> u32x4 {
+                    if (c2 < 32) return *(const u32x4*)(vrow + 32 * c2);
+                    return *(const u32x4*)(trw + (((2 * (c2 - 32) + hi) ^ tsw) << 4));
+                };
+                u32x4 kf[kPre + 1];
+#pragma unroll
+                for (int i = 0; i < kPre; ++i) kf[i] = kfrag(i);
+#pragma unroll
+                for (int c2 = 0; c2 < S::QC; ++c2) {
+                    if (c2 + kPre < S::QC) kf[(c2 + kPre) % (kPre + 1)] = kfrag(c2 + kPre);
+                    sacc = mfma_bf16_32x32x16(as_bf8(kf[c2 % (kPre + 1)]), qf[c2], sacc);
+#pragma unroll
+                    for (int j = 0; j < SPW; ++j)
+                        if (c2 == (j * S::QC) / SPW && copies) issue_copy(cs, c + 2, j);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+
+            const uint32_t vmask = valid_mask(c);
+            if (vmask == 0u) continue;                       // nothing selected here (uniform)
+            if (vmask != 0xFFFFFFFFu) {
+                // element v holds chunk row slot_row(8 (v/4) + 4 hi + v%4) = hi + rv(v)
+                const uint32_t vmh = vmask >> hi;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int rv = slot_row(8 * (v >> 2) + (v & 3));
+                    sacc[v] = ((vmh >> rv) & 1u) ? sacc[v] : -INFINITY;
+                }
+            }
+            if (__any(m == -INFINITY)) {                     // first chunk holding a valid row
+                float cmax0 = -INFINITY;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) cmax0 = fmaxf(cmax0, sacc[v]);
+                m = fmaxf(cmax0, __shfl_xor(cmax0, 32, kWave)) * scale_log2;   // both halves share m
+            }
+            const float negm = -m;
+            // p = exp2(z - m) (masked entries are -inf: exp2 gives 0), packed
+            // into bf16 pairs in place: P^T's lane layout is the B operand's
+            uint32_t pw[8];
+            float psum = 0.f, cmax = -INFINITY, peven = 0.f;
+            auto soft = [&](int v) {
+                const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[v], scale_log2, negm));
+                psum += pv;
+                cmax = fmaxf(cmax, sacc[v]);
+                if (v & 1) pw[v >> 1] = pack_bf16x2(peven, pv);
+                else peven = pv;
+            };
+#pragma unroll
+            for (int v = 0; v < 8; ++v) soft(v);
+
+            // O^T += V^T . P^T, two 16-row K steps (step s = 16 tt + dt).  K
+            // slot (a, j) of lane group hi is S^T row slot 16*tt + 8a + 4*hi + j,
+            // i.e. chunk row 16*tt + 2a + hi + 4j; the lane reads dims
+            // dt*32 + 16*g2 + 4*qs .. +3 of its source row.  The softmax of
+            // elements 8..15 runs between the first eight MFMAs.
+            const uint8_t* vb = cur + 32 * g2 + 8 * qs;
+            auto vfrag = [&](int s) -> u32x4 {
+                const int tt = s >> 4, dt = s & 15;
+                const int r0 = 16 * tt + hi + 4 * js;
+                const u32x2 a = __builtin_bit_cast(u32x2, lds_read_tr16(vb + r0 * S::VPITCH + 64 * dt));
+                const u32x2 bq = __builtin_bit_cast(u32x2, lds_read_tr16(vb + (r0 + 2) * S::VPITCH + 64 * dt));
+                return u32x4{a[0], a[1], bq[0], bq[1]};
+            };
+            u32x4 vf[kPvPre + 1];
+#pragma unroll
+            for (int i = 0; i < kPvPre; ++i) vf[i] = vfrag(i);
+#pragma unroll
+            for (int s = 0; s < 2 * S::DT; ++s) {
+                if (s + kPvPre < 2 * S::DT) vf[(s + kPvPre) % (kPvPre + 1)] = vfrag(s + kPvPre);
+                const int tt = s >> 4, dt = s & 15;
+                const v8bf pfrag = as_bf8(tt == 0 ? u32x4{pw[0], pw[1], pw[2], pw[3]}
+                                                  : u32x4{pw[4], pw[5], pw[6], pw[7]});
+                o[dt] = mfma_bf16_32x32x16(as_bf8(vf[s % (kPvPre + 1)]), pfrag, o[dt]);
+                if (s < 8) soft(8 + s);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            l += psum;
+            cmax *= scale_log2;
+            m_seen = fmaxf(m_seen, cmax);
+            overflow = overflow || (cmax > m + kHeadroom);
+        }
+        // every wave must agree before the ring is reused by a second pass
+        if (!__syncthreads_or(overflow ? 1 : 0)) break;
+        // recompute with the true maximum (both halves') as the reference
+        m = fmaxf(m_seen, __shfl_xor(m_seen, 32, kWave));
+        l = 0.f;
+#pragma unroll
+        for (int i = 0; i < S::DT; ++i)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) o[i][v] = 0.f;
+    }
+
+    l += __shfl_xor(l, 32, kWave);
+    const float inv = (l > 0.f) ? 1.f / l : 0.f;
+    const float lse_row = (l > 0.f) ? (m + log2f(l)) * 0.69314718055994531f : -INFINITY;
+    if constexpr (SPLIT) {
+        // partial (b, row, split z, head h): fp32, normalised by its own sum
+        const int64_t pr = ((int64_t)b * gridDim.x + row) * gridDim.z + blockIdx.z;
+        float* prow = part_o + (pr * H + h) * 512;
+#pragma unroll
+        for (int dt = 0; dt < S::DT; ++dt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int d0 = dt * 32 + 8 * g + 4 * hi;
+                *(v4f*)(prow + d0) = v4f{o[dt][4 * g] * inv, o[dt][4 * g + 1] * inv, o[dt][4 * g + 2] * inv,
+                                         o[dt][4 * g + 3] * inv};
+            }
+        if (hi == 0) part_lse[pr * H + h] = lse_row;
+    } else {
+        uint16_t* orow = out + (((int64_t)b * Lq + t) * H + h) * 512;
+#pragma unroll
+        for (int dt = 0; dt < S::DT; ++dt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int d0 = dt * 32 + 8 * g + 4 * hi;
+                const uint32_t w0 = pack_bf16x2(o[dt][4 * g] * inv, o[dt][4 * g + 1] * inv);
+                const uint32_t w1 = pack_bf16x2(o[dt][4 * g + 2] * inv, o[dt][4 * g + 3] * inv);
+                *(u32x2*)(orow + d0) = u32x2{w0, w1};
+            }
+        if (lse != nullptr && hi == 0)
+            lse[((int64_t)b * Lq + t) * H + h] = lse_row;
+    }
+}
+
+
+template <int NW>
+hipError_t launch_mla(const AttnLaunch& a, hipStream_t s, int ns, int cps, float* part_o, float* part_lse)
+{
+    const float scale_log2 = a.scale * 1.4426950408889634f;
+    if (ns == 1)
+        hipLaunchKernelGGL((sparse_attn_mla_kernel<NW, false>), dim3(a.t_count, a.B, 1), dim3(64 * NW), 0, s,
+                           (const uint16_t*)a.q, (const uint16_t*)a.kv, a.idx, (uint16_t*)a.out, a.lse, a.Lq,
+                           a.Lk, a.t_begin, a.H, a.k, a.idx_bstride, scale_log2, cps, part_o, part_lse);
+    else
+        hipLaunchKernelGGL((sparse_attn_mla_kernel<NW, true>), dim3(a.t_count, a.B, ns), dim3(64 * NW), 0, s,
+                           (const uint16_t*)a.q, (const uint16_t*)a.kv, a.idx, (uint16_t*)a.out, a.lse, a.Lq,
+                           a.Lk, a.t_begin, a.H, a.k, a.idx_bstride, scale_log2, cps, part_o, part_lse);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_sparse_attn_mla(const AttnLaunch& a, hipStream_t s, int ns, int cps, float* part_o,
+                                  float* part_lse)
+{
+    switch (a.H) {
+    case 32: return launch_mla<1>(a, s, ns, cps, part_o, part_lse);
+    case 64: return launch_mla<2>(a, s, ns, cps, part_o, part_lse);
+    case 128: return launch_mla<4>(a, s, ns, cps, part_o, part_lse);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace dsa

@@ -99,6 +99,10 @@ struct RopeLaunch {
 hipError_t launch_indexer(const IndexerLaunch& a, hipStream_t s);
 hipError_t launch_topk(const TopkLaunch& a, hipStream_t s);
 hipError_t launch_sparse_attn(const AttnLaunch& a, hipStream_t s);
+// bf16 576/512 rows, 32/64/128 heads, k <= 2048 (attn_mla.hip): ns splits
+// of cps chunks each (ns > 1: partials to part_o / part_lse for the merge)
+hipError_t launch_sparse_attn_mla(const AttnLaunch& a, hipStream_t s, int ns, int cps, float* part_o,
+                                  float* part_lse);
 hipError_t launch_quantize_e4m3(const QuantLaunch& a, hipStream_t s);
 hipError_t launch_rope_assemble(const RopeLaunch& a, hipStream_t s);
 hipError_t launch_kv_pack_fp8(const KvPackLaunch& a, hipStream_t s);

@@ -17,6 +17,7 @@
 // {4g..4g+3, 16+4g..16+4g+3} for lane group g; the transposed V copy is read
 // with the same slot order.  Output is rounded to bf16 (nearest even); the
 // log-sum-exp is written in fp32.
+#include "attn_layout.h"
 #include "hw.h"
 #include "launch.h"
 
@@ -195,32 +196,6 @@ void sparse_attn_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __r
 //    converted to bf16 in place (its lane layout is the B-operand layout) and
 //    V^T fragments come straight from the row-major chunk through LDS
 //    transpose reads (no transposed copy of V).
-template <int DQK, int DV, int NW>
-struct W32Shape {
-    static constexpr int NC = 32;                         // rows per chunk
-    static constexpr int NBUF = 2;                        // ring slots
-    static constexpr int VP = DV / 8;                     // 16-byte pieces of the value part
-    static constexpr int TP = (DQK - DV) / 8;             // pieces of the tail
-    static constexpr int VPITCH = VP * 16 + 16;           // bytes per value part in LDS (+1 skew piece)
-    static constexpr int VBYTES = NC * VPITCH;            // value parts of one chunk
-    static constexpr int TBYTES = NC * TP * 16;           // tails of one chunk
-    static constexpr int BUF_BYTES = VBYTES + TBYTES;
-    static constexpr int RPW = NC / NW;                   // value rows copied per wave
-    static constexpr int TI = TBYTES / 1024;              // tail copy instructions per chunk
-    static constexpr int SPW = RPW + TI / NW;             // copy instructions per wave per chunk
-    static constexpr int QC = DQK / 16;                   // MFMA K steps for Q.K (all held in registers)
-    static constexpr int DT = DV / 32;                    // 32-wide value tiles
-    static constexpr int KMAX = 2048;                     // largest k whose index list is staged in LDS
-    static_assert(VP == 64, "one copy instruction per value part");
-    static_assert(TP == 8 && TI == 4 && TI % NW == 0, "8-piece tails, 8 rows per copy");
-};
-
-// chunk row held by S^T row slot m (a permutation of 0..31, see above)
-__device__ __forceinline__ constexpr int slot_row(int m)
-{
-    return (m & 16) | (((m >> 3) & 1) << 1) | ((m >> 2) & 1) | ((m & 3) << 2);
-}
-
 // FP8 latent rows (F8 = true): 656 bytes per token -- e4m3 codes of dims
 // 0..511, four fp32 power-of-two scales (one per 128 dims), and dims 512..575
 // in bf16.  The copies land in a staging area (codes, scales, rotary part),
@@ -862,17 +837,22 @@ hipError_t launch_bf16_w32(const AttnLaunch& a, hipStream_t s)
     const int cps = (nch + ns - 1) / ns;
     float* part_o = a.part;
     float* part_lse = ns > 1 ? a.part + (size_t)a.B * a.t_count * ns * a.H * DV : nullptr;
-    if (ns == 1) {
+    if (!F8 && DQK == 576 && DV == 512) {
+        // bf16 latent rows: the scheduled kernel of attn_mla.hip
+        hipError_t e = launch_sparse_attn_mla(a, s, ns, cps, part_o, part_lse);
+        if (e != hipSuccess || ns == 1) return e;
+    } else if (ns == 1) {
         hipLaunchKernelGGL((sparse_attn_bf16_w32_kernel<DQK, DV, NW, F8, false>), dim3(a.t_count, a.B, 1),
                            dim3(64 * NW), 0, s, (const uint16_t*)a.q, a.kv, a.idx, (uint16_t*)a.out, a.lse,
                            a.Lq, a.Lk, a.t_begin, a.H, a.k, a.idx_bstride, scale_log2, cps, part_o, part_lse);
         return hipGetLastError();
+    } else {
+        hipLaunchKernelGGL((sparse_attn_bf16_w32_kernel<DQK, DV, NW, F8, true>), dim3(a.t_count, a.B, ns),
+                           dim3(64 * NW), 0, s, (const uint16_t*)a.q, a.kv, a.idx, (uint16_t*)a.out, a.lse,
+                           a.Lq, a.Lk, a.t_begin, a.H, a.k, a.idx_bstride, scale_log2, cps, part_o, part_lse);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((sparse_attn_bf16_w32_kernel<DQK, DV, NW, F8, true>), dim3(a.t_count, a.B, ns), dim3(64 * NW),
-                       0, s, (const uint16_t*)a.q, a.kv, a.idx, (uint16_t*)a.out, a.lse,
-                       a.Lq, a.Lk, a.t_begin, a.H, a.k, a.idx_bstride, scale_log2, cps, part_o, part_lse);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
     const int64_t n_items = (int64_t)a.B * a.t_count * a.H * (DV / 4);
     hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)((n_items + kMergeThreads - 1) / kMergeThreads)),
                        dim3(kMergeThreads), 0, s, part_o, part_lse, (uint16_t*)a.out, a.lse, n_items, a.t_count,

@@ -203,14 +203,20 @@ def test_fp8kv_attention_matches_oracle(dsa, B, Lq, Lk, H, k):
 
 
 def test_fp8kv_attention_equals_bf16_attention_on_the_same_values(dsa):
-    """The FP8 path widens code * scale to bf16 exactly: over the unpacked rows
-    (as bf16) the bf16 attention kernel gives the same bits."""
+    """The FP8 path widens code * scale to bf16 exactly, so over the unpacked
+    rows (as bf16) the bf16 attention computes the same softmax-weighted sums;
+    the two kernels differ only in the order of their fp32 additions.  Their
+    outputs agree to within one bf16 step (the final rounding may fall either
+    side) and their log-sum-exps to fp32 rounding."""
     q, packed, idx = _fp8kv_case(dsa, 2, 300, 4000, 128, 2048, seed=5, short=False)
     kv_vals = torch.from_numpy(oracle.kv_unpack_fp8(packed.cpu())).to(torch.bfloat16).to(DEV)
     out8, lse8 = dsa.dsa_sparse_attn_fp8kv(q, packed, idx, 192 ** -0.5, q_pos0=4000 - 300)
     out16, lse16 = dsa.dsa_sparse_attn(q, kv_vals, idx, 512, 192 ** -0.5, q_pos0=4000 - 300)
     torch.cuda.synchronize()
-    assert torch.equal(out8.view(torch.int16), out16.view(torch.int16)) and torch.equal(lse8, lse16)
+    a, b = out8.float(), out16.float()
+    step = torch.maximum(a.abs(), b.abs()) * 2.0 ** -7 + 2.0 ** -133
+    assert bool(((a - b).abs() <= step).all()), float(((a - b).abs() / step).max())
+    assert float((lse8 - lse16).abs().max()) <= 1e-5
 
 
 def test_fp8kv_decode_batch_full_size(dsa):
