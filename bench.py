@@ -39,8 +39,8 @@ ORACLE_SAMPLE = {"tiny_fp32_L256": 256, "prefill_L4096": 128, HEADLINE: 384, "de
 # FETCH_SIZE / WRITE_SIZE runs scaled by a 1 GiB plain copy measured in the same
 # runs (fetch factor 2.0, write factor 1.0).  Valid only for the attention
 # source it was measured on; any other source reports null.
-ATTN_TRAFFIC = {"source_sha256_16": "d574ec853ebdf46f", "fetch_bytes": 55110908519.0,
-                "write_bytes": 5431578400.0}
+ATTN_TRAFFIC = {"source_sha256_16": "ddfbb2bfd6e2eebb", "fetch_bytes": 55121365232.6,
+                "write_bytes": 5890508320.0}
 
 
 def log(*a):
@@ -109,7 +109,7 @@ def stage_roofline(cfg, work, stages_ms):
 
 def attn_traffic_bytes():
     import hashlib
-    src = os.path.join(ROOT, "sparse_attention_04_amd", "csrc", "sparse_attn.hip")
+    src = os.path.join(ROOT, "sparse_attention_04_amd", "csrc", "attn_mla.hip")
     with open(src, "rb") as f:
         sha = hashlib.sha256(f.read()).hexdigest()[:16]
     if sha != ATTN_TRAFFIC["source_sha256_16"]:
@@ -483,7 +483,7 @@ def main():
         torch.cuda.empty_cache()
         roof, floor_s = stage_roofline(cfg, work, stages)
         att = roof["attention"]
-        res["roofline"] = {"bound": att["bound"], "kernel": "sparse_attn_bf16_w32", "achieved": att["achieved"],
+        res["roofline"] = {"bound": att["bound"], "kernel": "sparse_attn_mla_kernel", "achieved": att["achieved"],
                            "peak": att["peak"], "unit": att["unit"], "frac": att["frac"],
                            "traffic": attn_traffic_bytes() if cfg.name == HEADLINE else None}
         res["indexer_frac_fp8_peak"] = roof["indexer"]["frac"]
