@@ -231,15 +231,51 @@ dsa_status dsa_sparse_attn_bwd(const void* q, const void* kv, const int32_t* idx
                                float softmax_scale, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Bytes of device workspace dsa_forward needs for these sizes: one tile of
- * B * T * Lk fp32 scores (T = the query-tile rows), the selected sets of all
- * B * Lq rows (int32, k each), and the attention's split partials when
- * dsa_sparse_attn_workspace_size(B, Lq, ...) is non-zero.  q_tile_rows = 0
- * picks T automatically (the largest T whose score tile fits the automatic
- * tile budget, at most Lq).  Returns 0 for an empty problem.
+ * How dsa_forward finds each row's k largest scores.  Both routes give the
+ * same selected sets, bit for bit (the k largest scores, the lowest s first
+ * among equal ones); they differ in memory traffic.
+ *
+ * DSA_SELECT_SCORE_TILES: the indexer writes every row's scores (s <= t_pos)
+ *   in tiles of q_tile_rows query rows, and dsa_topk reads them back.
+ *
+ * DSA_SELECT_CANDIDATES: no row's full scores are written.  With R = 2^r,
+ *   r = max(0, floor(log2(k / 128))), the indexer first scores every R-th key
+ *   (s = 0, R, 2R, ...) of each row with t_pos + 1 > 2k; each such row takes
+ *   tau = the ceil(1.5 k / R)-th largest of those sample scores (about 1.5 k
+ *   of its keys score at least that), the other rows tau = -inf.  The indexer
+ *   then scores every key and keeps, per row, the list of keys scoring >= tau
+ *   (at most cap = 2k stored), and the k largest of the list are selected.
+ *   A list of at least k and at most 2k entries contains every key scoring at
+ *   least the row's k-th largest score, so this selection is the exact top k.
+ *   Rows whose list is shorter than k or longer than 2k are recomputed from
+ *   their full scores, in tiles of q_tile_rows rows, by the first route (only
+ *   those rows' scores are written).  Requires FP8 indexer inputs, Lq >= 8,
+ *   k <= 4096, and (Lk - 1) / R + 1 <= 16384.
+ *
+ * DSA_SELECT_AUTO: the route measured faster on MI355X, which in this version
+ *   is score tiles for every problem.
+ */
+typedef enum dsa_select {
+    DSA_SELECT_AUTO = 0,
+    DSA_SELECT_SCORE_TILES = 1,
+    DSA_SELECT_CANDIDATES = 2
+} dsa_select;
+
+/*
+ * Bytes of device workspace dsa_forward needs for these sizes and route, laid
+ * out in this order: one tile of B * T * Lk fp32 scores (T = the query-tile
+ * rows; at the start of the workspace), the selected sets
+ * of all B * Lq rows (int32, k each), the attention's split partials when
+ * dsa_sparse_attn_workspace_size(B, Lq, ...) is non-zero, and for the
+ * candidate route per row: the sample scores ((Lk - 1) / R + 1 fp32, padded
+ * to a multiple of 4), tau, the list (2k pairs of 4-byte words), its length and
+ * a flag.  q_tile_rows = 0 picks T automatically (the largest T whose score
+ * tile fits the automatic tile budget, at most Lq).  Returns 0 for an empty
+ * problem, for q_tile_rows < 0, and for DSA_SELECT_CANDIDATES on a problem the
+ * candidate route does not take (with any idx_dtype).
  */
 size_t dsa_forward_workspace_size(int B, int Lq, int Lk, int k, int n_heads, int d_qk, int d_v,
-                                  dsa_dtype io_dtype, int q_tile_rows);
+                                  dsa_dtype io_dtype, int q_tile_rows, dsa_select select);
 
 /*
  * The whole forward ("DeepseekV3.2 拆解", section 核心组件: the output u_t of
@@ -248,22 +284,27 @@ size_t dsa_forward_workspace_size(int B, int Lq, int Lk, int k, int n_heads, int
  *
  *   out[b,t] = dsa_sparse_attn(q, kv, dsa_topk(dsa_indexer_scores(...), k))[b,t]
  *
- * The scores are formed in tiles of q_tile_rows query rows, each tile's top-k
- * following at once, so that at most B * q_tile_rows * Lk scores exist at a time
- * (the full Lq x Lk score matrix is never held when q_tile_rows < Lq); the
- * attention then runs once over every row.  Rows with t_pos + 1 <= k select
- * every preceding token, so their scores are not computed.
+ * The selected sets come from the route `select` names (dsa_select above).
+ * With score tiles, the scores are formed in tiles of q_tile_rows query rows,
+ * each tile's top-k following at once, so that at most B * q_tile_rows * Lk
+ * scores exist at a time (the full Lq x Lk score matrix is never held when
+ * q_tile_rows < Lq).  With candidates, only the sample scores and the lists are
+ * written, and score tiles only for rows whose list misses.  The attention
+ * then runs once over every row.  Rows with t_pos + 1 <= k select every
+ * preceding token, so their scores are not computed.
  *
  * Results are identical, bit for bit, to calling dsa_indexer_scores, dsa_topk
  * and dsa_sparse_attn (with its workspace) in turn on the whole problem, for
- * every q_tile_rows.
+ * every q_tile_rows and route.
  *
  * Arguments are those of the three calls; idx_out [B,Lq,k] and lse may be
  * NULL (without idx_out the selected sets stay in the workspace).  workspace
  * must hold dsa_forward_workspace_size(B, Lq, Lk, k, n_heads, d_qk, d_v,
- * io_dtype, q_tile_rows) bytes, 256-byte aligned; its contents on entry do not
- * matter.  Errors: those of the three calls; DSA_ERR_WORKSPACE for a missing,
- * short or misaligned workspace; DSA_ERR_SHAPE for q_tile_rows < 0.
+ * io_dtype, q_tile_rows, select) bytes, 256-byte aligned; its contents on
+ * entry do not matter.  Errors: those of the three calls; DSA_ERR_WORKSPACE
+ * for a missing, short or misaligned workspace; DSA_ERR_SHAPE for
+ * q_tile_rows < 0 or an unknown route; DSA_ERR_UNSUPPORTED for
+ * DSA_SELECT_CANDIDATES on a problem it does not take.
  */
 dsa_status dsa_forward(const void* q_idx, const float* q_scale,
                        const void* k_idx, const float* k_scale, const float* w,
@@ -273,7 +314,7 @@ dsa_status dsa_forward(const void* q_idx, const float* q_scale,
                        float softmax_scale,
                        int B, int Lq, int Lk, int q_pos0, int k,
                        int32_t* idx_out, void* out, float* lse,
-                       int q_tile_rows, void* workspace, size_t workspace_bytes,
+                       int q_tile_rows, dsa_select select, void* workspace, size_t workspace_bytes,
                        void* stream);
 
 /*
@@ -284,7 +325,8 @@ dsa_status dsa_forward(const void* q_idx, const float* q_scale,
  * held from the first call on that GPU until the process ends.
  *
  * Arguments and results are those of dsa_forward (bit for bit the same
- * output): the query tile is the largest one whose workspace fits the array.
+ * output), by the score-tile route: the query tile is the largest one whose
+ * workspace fits the array.
  * Problems for which even a one-row tile does not fit (B * Lk * 4 bytes of
  * scores, plus B * Lq * k * 4 for the selected sets when idx_out is NULL,
  * plus the attention's split partials) return DSA_ERR_UNSUPPORTED before any

@@ -51,12 +51,12 @@ def _load() -> ctypes.CDLL:
     L.dsa_sparse_attn.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp, sz, vp]
     L.dsa_sparse_attn_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
     L.dsa_sparse_attn_workspace_size.restype = sz
-    L.dsa_forward_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i32]
+    L.dsa_forward_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i32, i32]
     L.dsa_forward_workspace_size.restype = sz
     L.dsa_forward.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32,
                               vp, vp, i32, i32, i32, i32, f32,
                               i32, i32, i32, i32, i32,
-                              vp, vp, vp, i32, vp, sz, vp]
+                              vp, vp, vp, i32, i32, vp, sz, vp]
     i64, f64 = ctypes.c_int64, ctypes.c_double
     L.dsa_forward_noalloc.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32,
                                       vp, vp, i32, i32, i32, i32, f32,
@@ -175,10 +175,15 @@ def dsa_sparse_attn(q, kv, idx, d_v: int, softmax_scale: float, q_pos0: int = 0,
     return out, lse
 
 
+# dsa_select: how the forward finds each row's k largest scores (include/dsa.h)
+SELECT_AUTO, SELECT_SCORE_TILES, SELECT_CANDIDATES = 0, 1, 2
+
+
 def dsa_forward_workspace_size(B: int, Lq: int, Lk: int, k: int, n_heads: int, d_qk: int, d_v: int,
-                               io_dtype: torch.dtype = torch.bfloat16, q_tile_rows: int = 0) -> int:
+                               io_dtype: torch.dtype = torch.bfloat16, q_tile_rows: int = 0,
+                               select: int = SELECT_AUTO) -> int:
     dt = DSA_BF16 if io_dtype == torch.bfloat16 else DSA_F32
-    return int(lib.dsa_forward_workspace_size(B, Lq, Lk, k, n_heads, d_qk, d_v, dt, q_tile_rows))
+    return int(lib.dsa_forward_workspace_size(B, Lq, Lk, k, n_heads, d_qk, d_v, dt, q_tile_rows, select))
 
 
 class Forward:
@@ -186,12 +191,14 @@ class Forward:
     then each call is one ``dsa_forward`` on the current stream."""
 
     def __init__(self, B, Lq, Lk, k, n_heads, d_v, io_dtype: torch.dtype, device,
-                 q_tile_rows: int = 0, want_idx: bool = True, want_lse: bool = True, d_qk: int = 576):
+                 q_tile_rows: int = 0, want_idx: bool = True, want_lse: bool = True, d_qk: int = 576,
+                 select: int = SELECT_AUTO):
         self.q_tile_rows = q_tile_rows
+        self.select = select
         self.out = torch.empty((B, Lq, n_heads, d_v), dtype=io_dtype, device=device)
         self.idx = torch.empty((B, Lq, k), dtype=torch.int32, device=device) if want_idx else None
         self.lse = torch.empty((B, Lq, n_heads), dtype=torch.float32, device=device) if want_lse else None
-        nbytes = dsa_forward_workspace_size(B, Lq, Lk, k, n_heads, d_qk, d_v, io_dtype, q_tile_rows)
+        nbytes = dsa_forward_workspace_size(B, Lq, Lk, k, n_heads, d_qk, d_v, io_dtype, q_tile_rows, select)
         self.workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
         self.k = k
 
@@ -199,7 +206,7 @@ class Forward:
                  q_pos0: int = 0, stream=None):
         dsa_forward(q_idx, q_scale, k_idx, k_scale, w, q, kv, self.k, softmax_scale, q_pos0,
                     out=self.out, idx=self.idx, lse=self.lse, q_tile_rows=self.q_tile_rows,
-                    workspace=self.workspace, stream=stream)
+                    select=self.select, workspace=self.workspace, stream=stream)
         return self.out, self.idx, self.lse
 
 
@@ -207,7 +214,8 @@ def dsa_forward(q_idx, q_scale, k_idx, k_scale, w, q, kv, k: int = 2048,
                 softmax_scale: Optional[float] = None, q_pos0: int = 0,
                 out: Optional[torch.Tensor] = None, idx: Optional[torch.Tensor] = None,
                 lse: Optional[torch.Tensor] = None, d_v: Optional[int] = None,
-                q_tile_rows: int = 0, workspace: Optional[torch.Tensor] = None, stream=None):
+                q_tile_rows: int = 0, workspace: Optional[torch.Tensor] = None, stream=None,
+                select: int = SELECT_AUTO):
     """Fused scores -> top-k -> attention.  Returns (out, idx, lse)."""
     B, Lq, HI, DI = q_idx.shape
     Lk = k_idx.shape[1]
@@ -218,13 +226,13 @@ def dsa_forward(q_idx, q_scale, k_idx, k_scale, w, q, kv, k: int = 2048,
         softmax_scale = 1.0 / math.sqrt(Dqk)
     if out is None:
         out = torch.empty((B, Lq, H, d_v), dtype=q.dtype, device=q.device)
-    nbytes = dsa_forward_workspace_size(B, Lq, Lk, k, H, Dqk, d_v, q.dtype, q_tile_rows)
+    nbytes = dsa_forward_workspace_size(B, Lq, Lk, k, H, Dqk, d_v, q.dtype, q_tile_rows, select)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
     _check("dsa_forward", lib.dsa_forward(
         _p(q_idx), _p(q_scale), _p(k_idx), _p(k_scale), _p(w), HI, DI, _idx_dtype(q_idx),
         _p(q), _p(kv), H, Dqk, d_v, _io_dtype(q), float(softmax_scale),
-        B, Lq, Lk, q_pos0, k, _p(idx), _p(out), _p(lse), q_tile_rows,
+        B, Lq, Lk, q_pos0, k, _p(idx), _p(out), _p(lse), q_tile_rows, select,
         _p(workspace), workspace.numel(), _stream(stream)))
     return out, idx, lse
 

@@ -22,6 +22,7 @@ SOURCES = [
     ("dsa_capi.cpp", []),
     ("indexer.hip", ["-mllvm", "-amdgpu-mfma-vgpr-form"]),
     ("topk.hip", []),
+    ("select.hip", []),
     ("sparse_attn.hip", []),
     ("attn_mla.hip", []),
     ("inputs.hip", []),

@@ -140,23 +140,76 @@ int auto_tile_rows(int B, int Lq, int Lk)
 
 size_t round256(size_t x) { return (x + 255u) & ~(size_t)255u; }
 
+// Parameters of the candidate route (dsa_select in dsa.h): sample every
+// 2^kshift-th key, tau = the need-th largest sample score, lists of at most
+// cap = 2k entries.  The sample is about k / 128 keys apart, so a row's need
+// is about 192 sample scores: the relative spread of the number of keys that
+// score >= tau is then about 1/sqrt(192), and 1.5 k sits 4.6 spreads from
+// both k and 2k.
+struct CandPlan {
+    int kshift, need, cap, Ls, Ls_pad;
+    bool applies;       // DSA_SELECT_CANDIDATES takes the problem
+    bool automatic;     // DSA_SELECT_AUTO picks it
+};
+
+CandPlan cand_plan(int B, int Lq, int Lk, int k, bool fp8)
+{
+    CandPlan c{};
+    while ((128 << (c.kshift + 1)) <= k) ++c.kshift;
+    const int R = 1 << c.kshift;
+    c.need = (3 * k + 2 * R - 1) / (2 * R);
+    c.cap = 2 * k;
+    c.Ls = ((Lk - 1) >> c.kshift) + 1;
+    c.Ls_pad = (c.Ls + 3) & ~3;
+    c.applies = fp8 && Lq >= 8 && k <= dsa::kSelectMaxCap / 2 && c.Ls <= dsa::kSelectMaxSample;
+    // AUTO keeps score tiles: at L = 32768 the candidate route measured
+    // 24.15-24.56 ms per forward against 24.07-24.11 ms (its filtered indexer
+    // pass, 3.5 ms, costs more than the score-writing one, and the sample,
+    // thresholds and selection, 0.8 ms, about what the top-k over full rows
+    // costs).
+    c.automatic = false;
+    return c;
+}
+
+// The route a call takes: 1 = score tiles, 2 = candidates, 0 = not taken
+// (candidates asked for where they do not apply), -1 = unknown value.
+int forward_route(int select, const CandPlan& c)
+{
+    switch (select) {
+    case DSA_SELECT_AUTO: return c.automatic ? 2 : 1;
+    case DSA_SELECT_SCORE_TILES: return 1;
+    case DSA_SELECT_CANDIDATES: return c.applies ? 2 : 0;
+    default: return -1;
+    }
+}
+
 // Workspace of the forward for query tiles of T rows: one tile of scores,
 // the selected sets of every row (the attention runs once over all rows
 // after the last tile), and the attention's split partials (decided by the
-// whole problem's rows, as dsa_sparse_attn decides).
+// whole problem's rows, as dsa_sparse_attn decides); for the candidate
+// route, per row the sample scores, tau, the list length, the flag and the
+// list.
 struct ForwardLayout {
-    size_t scores, idx, part, total;
+    size_t scores, idx, part, sample, tau, cnt, flag, cand, total;
 };
 
 ForwardLayout forward_layout(int B, int Lq, int Lk, int k, int n_heads, int d_qk, int d_v, dsa_dtype io_dtype,
-                             int T, bool idx_in_workspace = true)
+                             int T, bool idx_in_workspace = true, const CandPlan* cand = nullptr)
 {
     ForwardLayout L{};
     L.scores = round256((size_t)B * (size_t)T * (size_t)Lk * sizeof(float));
     L.idx = idx_in_workspace ? round256((size_t)B * (size_t)Lq * (size_t)k * sizeof(int32_t)) : 0;
     const int ns = dsa::sparse_attn_split((int64_t)B * Lq, n_heads, d_qk, d_v, k, io_dtype == DSA_BF16);
     L.part = round256(dsa::sparse_attn_split_bytes((int64_t)B * Lq, n_heads, d_v, ns));
-    L.total = L.scores + L.idx + L.part;
+    if (cand) {
+        const size_t rows = (size_t)B * (size_t)Lq;
+        L.sample = round256(rows * (size_t)cand->Ls_pad * sizeof(float));
+        L.tau = round256(rows * sizeof(float));
+        L.cnt = round256(rows * sizeof(int32_t));
+        L.flag = round256(rows * sizeof(int32_t));
+        L.cand = round256(rows * (size_t)cand->cap * 2 * sizeof(uint32_t));
+    }
+    L.total = L.scores + L.idx + L.part + L.sample + L.tau + L.cnt + L.flag + L.cand;
     return L;
 }
 
@@ -178,40 +231,81 @@ dsa_status check_forward(const char* fn, const void* q_idx, const float* q_scale
     return DSA_OK;
 }
 
-// The forward on checked arguments: per tile of T query rows the indexer
-// scores (no masked entries written; rows that select every preceding token
-// skipped) and the top-k into the selected sets of all rows; then one
+// The forward on checked arguments.  Score-tile route: per tile of T query
+// rows the indexer scores (no masked entries written; rows that select every
+// preceding token skipped) and the top-k into the selected sets of all rows.
+// Candidate route: the sample scores, the thresholds, the lists and the
+// selection over the whole problem, then the score tiles for the flagged rows
+// only (launches whose rows are all unflagged return at once).  Then one
 // attention launch over every row.  Nothing here allocates: `ws` holds
-// forward_layout(..., T).total bytes.
+// forward_layout(..., T, idx_out == nullptr, cand or nullptr).total bytes.
 dsa_status forward_run(const char* fn, const void* q_idx, const float* q_scale, const void* k_idx,
                        const float* k_scale, const float* w, int n_idx_heads, int idx_dim, dsa_dtype idx_dtype,
                        const void* q, const void* kv, int n_heads, int d_qk, int d_v, dsa_dtype io_dtype,
                        float softmax_scale, int B, int Lq, int Lk, int q_pos0, int k, int32_t* idx_out, void* out,
-                       float* lse, int T, void* ws, hipStream_t s)
+                       float* lse, int T, const CandPlan* cand, void* ws, hipStream_t s)
 {
-    const ForwardLayout L = forward_layout(B, Lq, Lk, k, n_heads, d_qk, d_v, io_dtype, T, idx_out == nullptr);
-    float* ws_scores = (float*)ws;
-    int32_t* idx_all = idx_out ? idx_out : (int32_t*)((char*)ws + L.scores);
-    float* ws_part = (float*)((char*)ws + L.scores + L.idx);
+    const ForwardLayout L = forward_layout(B, Lq, Lk, k, n_heads, d_qk, d_v, io_dtype, T, idx_out == nullptr, cand);
+    char* p = (char*)ws;
+    float* ws_scores = (float*)p;
+    p += L.scores;
+    int32_t* idx_all = idx_out ? idx_out : (int32_t*)p;
+    p += L.idx;
+    float* ws_part = (float*)p;
+    p += L.part;
+    float* ws_sample = (float*)p;
+    p += L.sample;
+    float* ws_tau = (float*)p;
+    p += L.tau;
+    int32_t* ws_cnt = (int32_t*)p;
+    p += L.cnt;
+    int32_t* ws_flag = (int32_t*)p;
+    p += L.flag;
+    uint32_t* ws_cand = (uint32_t*)p;
     const int64_t idx_bstride = (int64_t)Lq * k;
+
+    dsa::IndexerLaunch base{};
+    base.q = q_idx; base.q_scale = q_scale; base.k = k_idx; base.k_scale = k_scale; base.w = w;
+    base.B = B; base.Lq = Lq; base.Lk = Lk; base.q_pos0 = q_pos0;
+    base.H = n_idx_heads; base.D = idx_dim; base.fp8 = (idx_dtype == DSA_FP8_E4M3);
+    base.write_masked = false; base.skip_upto_k = k;
+    hipError_t e = hipSuccess;
+
+    if (cand) {
+        // sample scores of the rows with t_pos + 1 > cap, every 2^kshift-th key
+        dsa::IndexerLaunch sa = base;
+        sa.scores = ws_sample; sa.t_begin = 0; sa.t_count = Lq;
+        sa.sc_bstride = (int64_t)Lq * cand->Ls_pad; sa.sc_rstride = cand->Ls_pad;
+        sa.kshift = cand->kshift; sa.skip_upto_k = cand->cap;
+        if ((e = dsa::launch_indexer(sa, s)) != hipSuccess) return hip_status(fn, e);
+        dsa::SelectLaunch sl{};
+        sl.B = B; sl.Lq = Lq; sl.q_pos0 = q_pos0; sl.k = k;
+        sl.sample = ws_sample; sl.s_rstride = cand->Ls_pad; sl.kshift = cand->kshift; sl.need = cand->need;
+        sl.tau = ws_tau; sl.cand = ws_cand; sl.cand_cnt = ws_cnt; sl.cap = cand->cap;
+        sl.idx = idx_all; sl.idx_bstride = idx_bstride; sl.flag = ws_flag;
+        if ((e = dsa::launch_select_threshold(sl, s)) != hipSuccess) return hip_status(fn, e);
+        // every key's score against tau, the lists
+        dsa::IndexerLaunch fa = base;
+        fa.t_begin = 0; fa.t_count = Lq;
+        fa.tau = ws_tau; fa.cand = ws_cand; fa.cand_cnt = ws_cnt; fa.cap = cand->cap;
+        if ((e = dsa::launch_indexer(fa, s)) != hipSuccess) return hip_status(fn, e);
+        if ((e = dsa::launch_select_candidates(sl, s)) != hipSuccess) return hip_status(fn, e);
+    }
 
     for (int t0 = 0; t0 < Lq; t0 += T) {
         const int tc = (Lq - t0 < T) ? (Lq - t0) : T;
-        dsa::IndexerLaunch ia{};
-        ia.q = q_idx; ia.q_scale = q_scale; ia.k = k_idx; ia.k_scale = k_scale; ia.w = w;
-        ia.scores = ws_scores; ia.B = B; ia.Lq = Lq; ia.Lk = Lk; ia.q_pos0 = q_pos0;
-        ia.t_begin = t0; ia.t_count = tc; ia.sc_bstride = (int64_t)T * Lk; ia.sc_rstride = Lk;
-        ia.H = n_idx_heads; ia.D = idx_dim; ia.fp8 = (idx_dtype == DSA_FP8_E4M3);
-        ia.write_masked = false; ia.skip_upto_k = k;
-        hipError_t e = dsa::launch_indexer(ia, s);
-        if (e != hipSuccess) return hip_status(fn, e);
+        dsa::IndexerLaunch ia = base;
+        ia.scores = ws_scores; ia.t_begin = t0; ia.t_count = tc;
+        ia.sc_bstride = (int64_t)T * Lk; ia.sc_rstride = Lk;
+        ia.flag = cand ? ws_flag : nullptr;
+        if ((e = dsa::launch_indexer(ia, s)) != hipSuccess) return hip_status(fn, e);
 
         dsa::TopkLaunch ta{};
         ta.scores = ws_scores; ta.idx = idx_all + (int64_t)t0 * k; ta.B = B; ta.Lq = Lq; ta.Lk = Lk;
         ta.q_pos0 = q_pos0; ta.t_begin = t0; ta.t_count = tc; ta.sc_bstride = (int64_t)T * Lk; ta.sc_rstride = Lk;
         ta.idx_bstride = idx_bstride; ta.k = k;
-        e = dsa::launch_topk(ta, s);
-        if (e != hipSuccess) return hip_status(fn, e);
+        ta.flag = cand ? ws_flag : nullptr;
+        if ((e = dsa::launch_topk(ta, s)) != hipSuccess) return hip_status(fn, e);
     }
 
     dsa::AttnLaunch aa{};
@@ -460,11 +554,14 @@ dsa_status dsa_kv_pack_fp8(const void* kv, void* kv_fp8, int64_t n_tok, void* st
 }
 
 size_t dsa_forward_workspace_size(int B, int Lq, int Lk, int k, int n_heads, int d_qk, int d_v,
-                                  dsa_dtype io_dtype, int q_tile_rows)
+                                  dsa_dtype io_dtype, int q_tile_rows, dsa_select select)
 {
     if (B <= 0 || Lq <= 0 || Lk <= 0 || k <= 0 || q_tile_rows < 0) return 0;
+    const CandPlan c = cand_plan(B, Lq, Lk, k, true);
+    const int route = forward_route((int)select, c);
+    if (route <= 0) return 0;
     const int T = q_tile_rows > 0 ? (q_tile_rows < Lq ? q_tile_rows : Lq) : auto_tile_rows(B, Lq, Lk);
-    return forward_layout(B, Lq, Lk, k, n_heads, d_qk, d_v, io_dtype, T).total;
+    return forward_layout(B, Lq, Lk, k, n_heads, d_qk, d_v, io_dtype, T, true, route == 2 ? &c : nullptr).total;
 }
 
 dsa_status dsa_forward(const void* q_idx, const float* q_scale, const void* k_idx,
@@ -472,7 +569,8 @@ dsa_status dsa_forward(const void* q_idx, const float* q_scale, const void* k_id
                        dsa_dtype idx_dtype, const void* q, const void* kv, int n_heads, int d_qk,
                        int d_v, dsa_dtype io_dtype, float softmax_scale, int B, int Lq, int Lk,
                        int q_pos0, int k, int32_t* idx_out, void* out, float* lse,
-                       int q_tile_rows, void* workspace, size_t workspace_bytes, void* stream)
+                       int q_tile_rows, dsa_select select, void* workspace, size_t workspace_bytes,
+                       void* stream)
 {
     const char* fn = "dsa_forward";
     bool empty = false;
@@ -481,13 +579,22 @@ dsa_status dsa_forward(const void* q_idx, const float* q_scale, const void* k_id
                                   lse, &empty);
     if (st != DSA_OK || empty) return st == DSA_OK ? ok() : st;
     if (q_tile_rows < 0) return fail(DSA_ERR_SHAPE, "%s: q_tile_rows=%d must be >= 0", fn, q_tile_rows);
+    const CandPlan c = cand_plan(B, Lq, Lk, k, idx_dtype == DSA_FP8_E4M3);
+    const int route = forward_route((int)select, c);
+    if (route < 0) return fail(DSA_ERR_SHAPE, "%s: select=%d is not a dsa_select value", fn, (int)select);
+    if (route == 0)
+        return fail(DSA_ERR_UNSUPPORTED,
+                    "%s: the candidate route needs FP8 indexer inputs, Lq >= 8, k <= %d and (Lk - 1) / %d + 1 <= %d "
+                    "(Lq=%d, k=%d, Lk=%d)", fn, dsa::kSelectMaxCap / 2, 1 << c.kshift, dsa::kSelectMaxSample,
+                    Lq, k, Lk);
+    const CandPlan* cp = route == 2 ? &c : nullptr;
     const int T = q_tile_rows > 0 ? (q_tile_rows < Lq ? q_tile_rows : Lq) : auto_tile_rows(B, Lq, Lk);
-    const size_t need = forward_layout(B, Lq, Lk, k, n_heads, d_qk, d_v, io_dtype, T).total;
+    const size_t need = forward_layout(B, Lq, Lk, k, n_heads, d_qk, d_v, io_dtype, T, idx_out == nullptr, cp).total;
     if (workspace == nullptr || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0)
         return fail(DSA_ERR_WORKSPACE, "%s: workspace needs %zu bytes, 256-byte aligned (got %zu at %p)",
                     fn, need, workspace_bytes, workspace);
     return forward_run(fn, q_idx, q_scale, k_idx, k_scale, w, n_idx_heads, idx_dim, idx_dtype, q, kv, n_heads,
-                       d_qk, d_v, io_dtype, softmax_scale, B, Lq, Lk, q_pos0, k, idx_out, out, lse, T, workspace,
+                       d_qk, d_v, io_dtype, softmax_scale, B, Lq, Lk, q_pos0, k, idx_out, out, lse, T, cp, workspace,
                        (hipStream_t)stream);
 }
 
@@ -520,7 +627,7 @@ dsa_status dsa_forward_noalloc(const void* q_idx, const float* q_scale, const vo
     st = scratch_address(fn, &ws);
     if (st != DSA_OK) return st;
     return forward_run(fn, q_idx, q_scale, k_idx, k_scale, w, n_idx_heads, idx_dim, idx_dtype, q, kv, n_heads,
-                       d_qk, d_v, io_dtype, softmax_scale, B, Lq, Lk, q_pos0, k, idx_out, out, lse, T, ws,
+                       d_qk, d_v, io_dtype, softmax_scale, B, Lq, Lk, q_pos0, k, idx_out, out, lse, T, nullptr, ws,
                        (hipStream_t)stream);
 }
 

@@ -160,6 +160,17 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int /*lane*/)
     return v;
 }
 
+// Inclusive prefix sum within each 16-lane row of the wave (the first four
+// steps of wave_incl_scan).
+__device__ __forceinline__ uint32_t row16_incl_scan(uint32_t v)
+{
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false);   // row_shr:1
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false);   // row_shr:2
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false);   // row_shr:4
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false);   // row_shr:8
+    return v;
+}
+
 // Value of lane 63 (e.g. the total of an inclusive scan), wave-uniform.
 __device__ __forceinline__ uint32_t wave_last(uint32_t v) { return __builtin_amdgcn_readlane(v, 63); }
 

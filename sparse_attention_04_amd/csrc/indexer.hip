@@ -53,12 +53,34 @@ __device__ __forceinline__ int ktile_off(int r, int c) { return r * kD + ((c ^ (
 // Round to bf16 (nearest even) and return the rounded value as fp32.
 __device__ __forceinline__ float round_bf16(float x) { return bf16_bits_to_f32(pack_bf16x2(x, 0.f) & 0xFFFFu); }
 
+// The block kernel's other modes (rows indexed b * Lq + t):
+//  - kshift > 0: the sample pass.  Key j of the launch is key s = j << kshift
+//    of the sequence, row t takes j <= t_pos >> kshift, and the score of key
+//    j goes to column j;
+//  - flag non-null: the block runs only if one of its rows has flag != 0;
+//  - CAND: no scores are stored.  The keys of a row whose score is >= tau[row]
+//    are appended to the row's list in ascending s, as (score bits, s) pairs,
+//    the first cap of them stored, and cand_cnt[row] gets their number.  A
+//    row's keys must all be in one workgroup (no split over blockIdx.z): the
+//    position of a group's entries is the row's running count, kept by every
+//    thread of the row, plus the count of the group's lower keys.
+struct IdxExt {
+    int kshift;
+    const int32_t* flag;
+    const float* tau;
+    uint32_t* cand;
+    int32_t* cand_cnt;
+    int cap;
+};
+
+template <bool CAND>
 __global__ __launch_bounds__(kThreads)
 void indexer_fp8_kernel(const uint8_t* __restrict__ q8, const float* __restrict__ q_scale,
                         const uint8_t* __restrict__ k8, const float* __restrict__ k_scale,
                         const float* __restrict__ w, float* __restrict__ scores,
                         int Lq, int Lk, int q_pos0, int t_begin, int t_count,
-                        int64_t sc_bstride, int64_t sc_rstride, int write_masked, int skip_upto_k, int gps)
+                        int64_t sc_bstride, int64_t sc_rstride, int write_masked, int skip_upto_k, int gps,
+                        IdxExt x)
 {
     __shared__ __attribute__((aligned(16))) uint8_t ktile[2][kKG * kD];
     __shared__ __attribute__((aligned(16))) v4f red[2][4][4][kWave];     // [buffer][wave][tile][lane]
@@ -72,10 +94,17 @@ void indexer_fp8_kernel(const uint8_t* __restrict__ q8, const float* __restrict_
     const int tpos_last = q_pos0 + t0 + rows_here - 1;
     if (!write_masked && skip_upto_k > 0 && tpos_last + 1 <= skip_upto_k)
         return;
+    if (x.flag) {
+        int any = 0;
+        for (int r = 0; r < rows_here; ++r) any |= x.flag[(int64_t)b * Lq + t0 + r];
+        if (!any) return;
+    }
+    const int kshift = x.kshift;
+    const int Lks = ((Lk - 1) >> kshift) + 1;          // keys of the launch (all of them when kshift = 0)
     // Key groups of this block: [g0, g1) of the ngroups its rows need (split
     // over blockIdx.z when there are few row blocks); a split past the
     // block's keys has nothing to do.
-    const int ngroups = (tpos_last + 1 + kKG - 1) / kKG;
+    const int ngroups = ((tpos_last >> kshift) + 1 + kKG - 1) / kKG;
     const int g0 = (int)blockIdx.z * gps;
     const int g1 = min(g0 + gps, ngroups);
     if (g0 >= g1)
@@ -164,8 +193,8 @@ void indexer_fp8_kernel(const uint8_t* __restrict__ q8, const float* __restrict_
         for (int n = 0; n < 2; ++n) {
             const int p = n * kThreads + tid;
             const int r = p >> 3, c = (p & 7) ^ ((r >> 1) & 7);
-            const int s = min(g * kKG + r, Lk - 1);
-            const uint8_t* src = k8 + ((int64_t)b * Lk + s) * kD + c * 16;
+            const int s = min(g * kKG + r, Lks - 1);
+            const uint8_t* src = k8 + ((int64_t)b * Lk + ((int64_t)s << kshift)) * kD + c * 16;
             const uint32_t dst = ktile_lds + slot * (kKG * kD) + (n * kThreads + wave * kWave) * 16;
             global_to_lds16_async(src, __builtin_amdgcn_readfirstlane(dst));
         }
@@ -181,6 +210,19 @@ void indexer_fp8_kernel(const uint8_t* __restrict__ q8, const float* __restrict_
         cb[p] = as_bf8(*(const u32x4*)&cpart[p][col][(32 * grp + 8 * wave) / 2]);
     const int lin_chunk = 2 * grp + (wave >> 1), lin_byte = 8 * (wave & 1);
 
+    // After each group's barrier, thread (wave, lane) finishes row
+    // er = 4 wave + lane / 16 of the block at keys s0 + 4 eq .. + 3, eq =
+    // lane % 16: a row's 64 keys lie in one 16-lane row of one wave, in
+    // ascending s, so its scores leave as one 256-byte run and its
+    // candidates are counted by a scan within the 16 lanes.
+    const int er = 4 * wave + (lane >> 4), eq = lane & 15;
+    // CAND: this thread's row, its threshold and its entries so far (the same
+    // count in all 16 threads of the row).
+    const int64_t crow = (int64_t)b * Lq + t0 + er;
+    const bool cact = CAND && er < rows_here && q_pos0 + t0 + er + 1 > skip_upto_k;
+    const float ctau = cact ? x.tau[crow] : INFINITY;
+    uint32_t crun = 0;
+
     // Per group: the copy of group g+1 into the other tile slot runs while g
     // is computed; one wait + barrier publishes both the next key tile and
     // this group's partial sums (the reduction buffer is double-buffered too).
@@ -191,10 +233,10 @@ void indexer_fp8_kernel(const uint8_t* __restrict__ q8, const float* __restrict_
         if (g + 1 < g1) issue_keys(g + 1, kb ^ 1);
         // key scales of the four keys this thread finishes after the barrier,
         // fetched now so the epilogue does not wait on memory
-        const int sb = s0 + wave * 16 + grp * 4;
+        const int sb = s0 + 4 * eq;
         float ksc[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) ksc[r] = k_scale[(int64_t)b * Lk + min(sb + r, Lk - 1)];
+        for (int r = 0; r < 4; ++r) ksc[r] = k_scale[(int64_t)b * Lk + ((int64_t)min(sb + r, Lks - 1) << kshift)];
         // key fragments of tile i: the linear part's 8 bytes and the 32-byte
         // MFMA operand; those of tile i + 1 are read while tile i computes
         auto load_frag = [&](int i, u32x2& kk_, v8i& af_) {
@@ -244,11 +286,13 @@ void indexer_fp8_kernel(const uint8_t* __restrict__ q8, const float* __restrict_
         }
         wait_vmcnt0();
         __syncthreads();
-        // thread (wave = tile i, lane): sum the four waves' partials
-        v4f sum = red[kb][0][wave][lane];
+        // sum the four waves' partials of row er, keys sb .. sb + 3 (tile
+        // eq / 4, written by lane er + 16 (eq % 4) of each wave)
+        const int rl = er + 16 * (eq & 3), rt = eq >> 2;
+        v4f sum = red[kb][0][rt][rl];
 #pragma unroll
         for (int ww = 1; ww < 4; ++ww) {
-            const v4f x = red[kb][ww][wave][lane];
+            const v4f x = red[kb][ww][rt][rl];
             sum[0] += x[0]; sum[1] += x[1]; sum[2] += x[2]; sum[3] += x[3];
         }
         if (write_masked) {
@@ -263,9 +307,31 @@ void indexer_fp8_kernel(const uint8_t* __restrict__ q8, const float* __restrict_
                 }
             }
         }
-        if (col < rows_here) {
-            const int t = t0 + col;
-            const int tpos = q_pos0 + t;
+        if constexpr (CAND) {
+            const int tpos = q_pos0 + t0 + er;
+            float v[4];
+            uint32_t m = 0;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                v[r] = sum[r] * ksc[r];
+                m |= (cact && sb + r <= tpos && v[r] >= ctau) ? (1u << r) : 0u;
+            }
+            const uint32_t c = (uint32_t)__builtin_popcount(m);
+            const uint32_t incl = row16_incl_scan(c);
+            const uint32_t total = (uint32_t)__shfl((int)incl, lane | 15, kWave);
+            uint32_t pos = crun + incl - c;
+            uint32_t* dst = x.cand + (size_t)crow * (size_t)x.cap * 2;
+            while (m) {
+                const int r = __builtin_ctz(m);
+                m &= m - 1;
+                if (pos < (uint32_t)x.cap)
+                    *(u32x2*)(dst + 2 * (size_t)pos) = u32x2{__float_as_uint(v[r]), (uint32_t)(sb + r)};
+                ++pos;
+            }
+            crun += total;
+        } else if (er < rows_here) {
+            const int t = t0 + er;
+            const int tpos = (q_pos0 + t) >> kshift;
             float* dst = scores + (int64_t)b * sc_bstride + (int64_t)(t - t_begin) * sc_rstride + sb;
             float v[4];
 #pragma unroll
@@ -274,16 +340,21 @@ void indexer_fp8_kernel(const uint8_t* __restrict__ q8, const float* __restrict_
                 v[r] = (s <= tpos) ? sum[r] * ksc[r] : -INFINITY;
             }
             const bool vec_ok = ((uintptr_t)dst & 15u) == 0;
-            if (vec_ok && sb + 3 < Lk && (write_masked || sb + 3 <= tpos)) {
+            if (vec_ok && sb + 3 < Lks && (write_masked || sb + 3 <= tpos)) {
                 *(v4f*)dst = v4f{v[0], v[1], v[2], v[3]};
             } else {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int s = sb + r;
-                    if (s < Lk && (write_masked || s <= tpos)) dst[r] = v[r];
+                    if (s < Lks && (write_masked || s <= tpos)) dst[r] = v[r];
                 }
             }
         }
+    }
+
+    if constexpr (CAND) {
+        if (eq == 0 && er < rows_here) x.cand_cnt[crow] = cact ? (int32_t)crun : 0;
+        return;
     }
 
     if (write_masked && g1 == ngroups) {
@@ -484,15 +555,20 @@ hipError_t launch_indexer(const IndexerLaunch& a, hipStream_t s)
         // about 1024 workgroups run and the longest block's chain of key
         // groups is cut (splits past a block's keys return at once).
         const int nqb = (a.t_count + kQB - 1) / kQB;
-        const int gmax = (int)(((int64_t)a.q_pos0 + a.t_begin + a.t_count + kKG - 1) / kKG);
+        const int64_t tpos_end = (int64_t)a.q_pos0 + a.t_begin + a.t_count;   // largest t_pos + 1
+        const int gmax = (int)((((tpos_end - 1) >> a.kshift) + kKG) / kKG);
         const int64_t blocks = (int64_t)nqb * a.B;
-        int nz = blocks >= kMinBlocks ? 1 : (int)std::min<int64_t>((kMinBlocks + blocks - 1) / blocks, gmax);
+        const bool cand = a.tau != nullptr;
+        int nz = (blocks >= kMinBlocks || cand) ? 1
+                 : (int)std::min<int64_t>((kMinBlocks + blocks - 1) / blocks, gmax);
         const int gps = (gmax + nz - 1) / nz;
         nz = (gmax + gps - 1) / gps;
-        hipLaunchKernelGGL(indexer_fp8_kernel, dim3(nqb, a.B, nz), dim3(kThreads), 0, s,
+        const IdxExt x{a.kshift, a.flag, a.tau, a.cand, a.cand_cnt, a.cap};
+        hipLaunchKernelGGL(cand ? indexer_fp8_kernel<true> : indexer_fp8_kernel<false>, dim3(nqb, a.B, nz),
+                           dim3(kThreads), 0, s,
                            (const uint8_t*)a.q, a.q_scale, (const uint8_t*)a.k, a.k_scale, a.w,
                            a.scores, a.Lq, a.Lk, a.q_pos0, a.t_begin, a.t_count,
-                           a.sc_bstride, a.sc_rstride, (int)a.write_masked, a.skip_upto_k, gps);
+                           a.sc_bstride, a.sc_rstride, (int)a.write_masked, a.skip_upto_k, gps, x);
     } else {
         const size_t shm = sizeof(float) * ((size_t)a.H * a.D + a.H);
         hipLaunchKernelGGL(indexer_f32_kernel, dim3(a.t_count, a.B), dim3(kF32Threads), shm, s,

@@ -21,6 +21,17 @@ struct IndexerLaunch {
     bool fp8;
     bool write_masked;      // write -inf for t_pos < s < Lk
     int skip_upto_k;        // > 0: skip query blocks whose rows all have t_pos + 1 <= this
+    // FP8 block kernel only (B * Lq rows indexed b * Lq + t):
+    int kshift = 0;         // > 0: sample pass over keys s = j << kshift; score column j, j <= t_pos >> kshift
+    const int32_t* flag = nullptr;   // non-null: only query blocks holding a row with flag != 0 run
+    // Candidate pass (tau non-null; no scores stored, keys not split over
+    // workgroups): the keys of row (b, t) with score >= tau[row] are appended,
+    // in ascending s, to cand + 2 * row * cap as (score bits, s) pairs, the
+    // first cap of them stored; cand_cnt[row] gets their number.
+    const float* tau = nullptr;
+    uint32_t* cand = nullptr;
+    int32_t* cand_cnt = nullptr;
+    int cap = 0;
 };
 
 struct TopkLaunch {
@@ -30,6 +41,30 @@ struct TopkLaunch {
     int t_begin, t_count;
     int64_t sc_bstride, sc_rstride, idx_bstride;
     int k;
+    const int32_t* flag = nullptr;   // non-null: only rows with flag[b * Lq + t] != 0 run
+};
+
+// Selection over per-row candidate lists (select.hip), rows [0, Lq) of every
+// batch entry, row (b, t) at index b * Lq + t.
+struct SelectLaunch {
+    int B, Lq, q_pos0, k;
+    // thresholds: rows with t_pos + 1 <= cap get tau = -inf (every key is a
+    // candidate); the others the need-th largest of their (t_pos >> kshift) + 1
+    // sample scores, row (b, t) at sample + (b * Lq + t) * s_rstride
+    const float* sample;
+    int64_t s_rstride;
+    int kshift, need;
+    float* tau;
+    // selection: the k entries of the row's list with the largest scores
+    // (lowest s among equal scores), written in ascending s to
+    // idx + b * idx_bstride + t * k; flag[row] = 1 when the list cannot
+    // hold them (fewer than k entries, or more than cap), else 0
+    const uint32_t* cand;
+    const int32_t* cand_cnt;
+    int cap;
+    int32_t* idx;
+    int64_t idx_bstride;
+    int32_t* flag;
 };
 
 struct AttnLaunch {
@@ -98,6 +133,11 @@ struct RopeLaunch {
 
 hipError_t launch_indexer(const IndexerLaunch& a, hipStream_t s);
 hipError_t launch_topk(const TopkLaunch& a, hipStream_t s);
+hipError_t launch_select_threshold(const SelectLaunch& a, hipStream_t s);
+hipError_t launch_select_candidates(const SelectLaunch& a, hipStream_t s);
+// largest sample row and list the selection kernels take
+constexpr int kSelectMaxSample = 16384;
+constexpr int kSelectMaxCap = 8192;
 hipError_t launch_sparse_attn(const AttnLaunch& a, hipStream_t s);
 // bf16 576/512 rows, 32/64/128 heads, k <= 2048 (attn_mla.hip): ns splits
 // of cps chunks each (ns > 1: partials to part_o / part_lse for the merge)

@@ -151,7 +151,7 @@ template <bool IN_REGS>
 __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(8)))
 void topk_radix_kernel(const float* __restrict__ scores, int32_t* __restrict__ idx,
                        int q_pos0, int t_begin, int row0, int64_t sc_bstride, int64_t sc_rstride,
-                       int64_t idx_bstride, int k)
+                       int64_t idx_bstride, int k, const int32_t* __restrict__ flag, int Lq)
 {
     __shared__ TopkShared sh;
 
@@ -159,6 +159,8 @@ void topk_radix_kernel(const float* __restrict__ scores, int32_t* __restrict__ i
     const int row = row0 + (int)(gridDim.x - 1 - blockIdx.x), b = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int t = t_begin + row;
+    if (flag && flag[(int64_t)b * Lq + t] == 0)    // only the flagged rows run
+        return;
     const int n = q_pos0 + t + 1;                  // candidates s = 0 .. t_pos
     int32_t* out = idx + (int64_t)b * idx_bstride + (int64_t)row * k;
     if (n <= k) {
@@ -619,7 +621,7 @@ hipError_t launch_topk(const TopkLaunch& a, hipStream_t s)
     auto rows = [&](auto kernel, int r0, int r1) {
         if (r1 > r0)
             hipLaunchKernelGGL(kernel, dim3(r1 - r0, a.B), dim3(kT), 0, s, a.scores, a.idx, a.q_pos0, a.t_begin, r0,
-                               a.sc_bstride, a.sc_rstride, a.idx_bstride, a.k);
+                               a.sc_bstride, a.sc_rstride, a.idx_bstride, a.k, a.flag, a.Lq);
     };
     rows(topk_radix_kernel<false>, 0, r_lo);
     rows(topk_radix_kernel<true>, r_lo, r_hi);

@@ -136,28 +136,59 @@ def test_attention_split_workspace(L):
 
 
 AUTO_TILE_BYTES = 4 << 30      # the forward's automatic query tile: score tile cap
+SEL_AUTO, SEL_TILES, SEL_CAND = 0, 1, 2
+
+
+def _r256(x):
+    return (x + 255) // 256 * 256
+
+
+def _cand_extra(B, Lq, Lk, k):
+    """Candidate-route workspace beyond the score-tile route's: per row the
+    sample scores (every 2^r-th key, r = max(0, floor(log2(k / 128))), padded
+    to 4), tau, the list length, the flag and the list of 2k (score, s) pairs."""
+    r = 0
+    while (128 << (r + 1)) <= k:
+        r += 1
+    ls_pad = ((((Lk - 1) >> r) + 1) + 3) // 4 * 4
+    rows = B * Lq
+    return _r256(rows * ls_pad * 4) + 3 * _r256(rows * 4) + _r256(rows * 2 * k * 8)
 
 
 def test_forward_workspace(L):
-    ws = lambda B, Lq, Lk, k, T: L.dsa_forward_workspace_size(B, Lq, Lk, k, 128, 576, 512, BF16, T)
-    # one tile of scores plus the selected sets of every row (the attention
-    # runs once over all rows after the last tile)
+    ws = lambda B, Lq, Lk, k, T, sel=SEL_TILES: L.dsa_forward_workspace_size(B, Lq, Lk, k, 128, 576, 512, BF16,
+                                                                            T, sel)
+    # score tiles: one tile of scores plus the selected sets of every row (the
+    # attention runs once over all rows after the last tile)
     assert ws(1, 32768, 32768, 2048, 1024) == 1024 * 32768 * 4 + 32768 * 2048 * 4
     assert ws(1, 131072, 131072, 2048, 4096) == 4096 * 131072 * 4 + 131072 * 2048 * 4
     # auto tile: the largest score tile within AUTO_TILE_BYTES
     for Lk in (4096, 32768, 131072):
         T = min(Lk, AUTO_TILE_BYTES // (Lk * 4))
-        assert ws(1, Lk, Lk, 2048, 0) == T * Lk * 4 + Lk * 2048 * 4
+        tiles = T * Lk * 4 + Lk * 2048 * 4
+        assert ws(1, Lk, Lk, 2048, 0) == tiles
+        # candidates on top of the fallback tiles
+        assert ws(1, Lk, Lk, 2048, 0, SEL_CAND) == tiles + _cand_extra(1, Lk, Lk, 2048)
+        # AUTO takes score tiles
+        assert ws(1, Lk, Lk, 2048, 0, SEL_AUTO) == tiles
+    assert ws(1, 32768, 32768, 512, 0, SEL_AUTO) == ws(1, 32768, 32768, 512, 0)      # k < 1024: tiles
+    assert ws(1, 300, 300, 64, 0, SEL_CAND) == ws(1, 300, 300, 64, 0) + _cand_extra(1, 300, 300, 64)
     # decode batch: scores, indices and the attention's split partials (4 splits)
     assert ws(64, 1, 65536, 2048, 0) == 64 * 65536 * 4 + 64 * 2048 * 4 + 64 * 4 * 128 * 513 * 4
+    assert ws(64, 1, 65536, 2048, 0, SEL_AUTO) == ws(64, 1, 65536, 2048, 0)
+    # routes that do not take the problem, and unknown routes
+    assert ws(64, 1, 65536, 2048, 0, SEL_CAND) == 0                 # Lq < 8
+    assert ws(1, 8192, 8192, 5000, 0, SEL_CAND) == 0                # k > 4096
+    assert ws(1, 1 << 16, 1 << 16, 64, 0, SEL_CAND) == 0            # a sample of 65536 keys
+    assert ws(1, 8, 8, 4, 0, 3) == 0 and ws(1, 8, 8, 4, -1) == 0
     assert ws(0, 1, 1, 1, 0) == 0
     need = ws(1, 8, 8, 4, 0)
 
     def fwd(workspace, nbytes, **kw):
-        a = dict(H=64, D=128, dt=FP8, Hq=128, dqk=576, dv=512, io=BF16, k=4, T=0)
+        a = dict(H=64, D=128, dt=FP8, Hq=128, dqk=576, dv=512, io=BF16, k=4, T=0, sel=SEL_AUTO)
         a.update(kw)
         return L.dsa_forward(A, A, A, A, A, a["H"], a["D"], a["dt"], A, A, a["Hq"], a["dqk"], a["dv"],
-                             a["io"], 0.1, 1, 8, 8, 0, a["k"], None, A, None, a["T"], workspace,
+                             a["io"], 0.1, 1, 8, 8, 0, a["k"], None, A, None, a["T"], a["sel"], workspace,
                              nbytes, None)
 
     assert fwd(None, need) == WS
@@ -167,6 +198,11 @@ def test_forward_workspace(L):
     assert fwd(A, need, T=-1) == SHAPE
     assert fwd(A, need, H=16) == UNSUP
     assert fwd(A, need, io=FP8) == DTYPE
+    assert fwd(A, need, sel=3) == SHAPE
+    assert fwd(A, need, sel=SEL_CAND) == WS                 # the candidate route needs more
+    # the candidate route on fp32 indexer inputs (no scales)
+    assert L.dsa_forward(A, None, A, None, A, 4, 32, F32, A, A, 128, 576, 512, BF16, 0.1, 1, 8, 8, 0, 4, None, A,
+                         None, 0, SEL_CAND, A, ws(1, 8, 8, 4, 0, SEL_CAND), None) == UNSUP
 
 
 def test_quantize_validation(L):

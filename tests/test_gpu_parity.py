@@ -99,18 +99,28 @@ def _run_case(dsa, cfg, rows_by_b, seed=0, check_forward=True, q_tile_rows=0, mi
         stats["attn_err"] = max(stats["attn_err"], check_attention(g_o, o_ref, g_l, l_ref, io == BF16))
 
     if check_forward:
-        # fused forward == the three calls, bit for bit
-        fwd_idx = torch.empty_like(idx)
-        fwd_lse = torch.empty_like(lse)
-        fwd_out, _, _ = dsa.dsa_forward(inp["q_idx"], inp.get("q_scale"), inp["k_idx"], inp.get("k_scale"),
-                                        inp["w"], inp["q"], inp["kv"], k=cfg.k,
-                                        softmax_scale=cfg.softmax_scale, q_pos0=cfg.q_pos0,
-                                        idx=fwd_idx, lse=fwd_lse, d_v=cfg.d_v, q_tile_rows=q_tile_rows)
-        torch.cuda.synchronize()
-        assert torch.equal(fwd_idx, idx), "forward idx != top-k call"
-        assert torch.equal(fwd_out.view(torch.int16) if fwd_out.dtype == torch.bfloat16 else fwd_out,
-                           out.view(torch.int16) if out.dtype == torch.bfloat16 else out), "forward out differs"
-        assert torch.equal(fwd_lse, lse), "forward lse differs"
+        # fused forward == the three calls, bit for bit, by every route that
+        # takes the problem (AUTO, score tiles, candidate lists)
+        routes = [dsa.SELECT_AUTO, dsa.SELECT_SCORE_TILES]
+        if fp8 and dsa.dsa_forward_workspace_size(cfg.B, cfg.Lq, cfg.Lk, cfg.k, cfg.n_heads, cfg.d_qk, cfg.d_v,
+                                                  inp["q"].dtype, q_tile_rows, dsa.SELECT_CANDIDATES) > 0:
+            routes.append(dsa.SELECT_CANDIDATES)
+        for route in routes:
+            fwd_idx = torch.empty_like(idx)
+            fwd_lse = torch.empty_like(lse)
+            fwd_out, _, _ = dsa.dsa_forward(inp["q_idx"], inp.get("q_scale"), inp["k_idx"], inp.get("k_scale"),
+                                            inp["w"], inp["q"], inp["kv"], k=cfg.k,
+                                            softmax_scale=cfg.softmax_scale, q_pos0=cfg.q_pos0,
+                                            idx=fwd_idx, lse=fwd_lse, d_v=cfg.d_v, q_tile_rows=q_tile_rows,
+                                            select=route)
+            torch.cuda.synchronize()
+            assert torch.equal(fwd_idx, idx), f"forward idx != top-k call (route {route})"
+            assert torch.equal(fwd_out.view(torch.int16) if fwd_out.dtype == torch.bfloat16 else fwd_out,
+                               out.view(torch.int16) if out.dtype == torch.bfloat16 else out), \
+                f"forward out differs (route {route})"
+            assert torch.equal(fwd_lse, lse), f"forward lse differs (route {route})"
+            del fwd_idx, fwd_lse, fwd_out
+        print(f"  [{cfg.name}] forward routes {routes} equal to the three calls", flush=True)
     frac_plain = stats["n_plain"] / max(stats["n_valid"], 1)
     print(f"  [{cfg.name}] score err/tol {stats['score_err_ratio']:.3g} (err/mass {stats['err_over_mass']:.3g}), "
           f"plain 1e-3 rel {frac_plain:.4f} of {stats['n_valid']} (all {stats['n_big']} >= 2.5% of row max), "
