@@ -60,7 +60,12 @@ void sparse_attn_mla_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
 {
     using S = W32Shape<576, 512, NW>;
     constexpr int NC = S::NC;
-    constexpr int NBUF = 3;                                   // ring slots
+    // ring slots: three for many rows; four when each row's set is split
+    // over workgroups (few rows: the gathers come from HBM, and a deeper ring
+    // keeps more of them in flight; the wait counter, 6 bits, must hold two
+    // chunks' copies)
+    constexpr int NBUF = (SPLIT && 2 * S::SPW < 64) ? 4 : 3;
+    constexpr int AHEAD = NBUF - 1;                           // chunks copied ahead
     constexpr int SPW = S::SPW;                               // copy instructions per wave per chunk
     constexpr int TPW = S::TI / NW;                           // of which tails
     __shared__ __attribute__((aligned(16))) uint8_t ring[NBUF][S::BUF_BYTES];
@@ -167,17 +172,26 @@ void sparse_attn_mla_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
     float m_seen = -INFINITY;                                // this half-wave's largest logit (log2 domain)
     for (int pass = 0; pass < 2; ++pass) {
         bool overflow = false;
-        if (nchunks > 0) issue_chunk(c0);
-        if (nchunks > 1) issue_chunk(c0 + 1);
+#pragma unroll
+        for (int i = 0; i < AHEAD; ++i)
+            if (nchunks > i) issue_chunk(c0 + i);
         for (int it = 0; it < nchunks; ++it) {
-            if (it + 1 < nchunks) wait_vmcnt<SPW>();         // chunk it landed; chunk it+1 may be in flight
-            else wait_vmcnt0();
+            // chunk it landed; the up to AHEAD - 1 chunks after it may be in flight
+            const int later = min(AHEAD - 1, nchunks - 1 - it);
+            if constexpr (AHEAD >= 3) {
+                if (later >= 2) wait_vmcnt<2 * SPW>();
+                else if (later == 1) wait_vmcnt<SPW>();
+                else wait_vmcnt0();
+            } else {
+                if (later == 1) wait_vmcnt<SPW>();
+                else wait_vmcnt0();
+            }
             __syncthreads();                                 // ... for every wave; chunk it-1 consumed
             const int c = c0 + it;
             const uint8_t* cur = ring[c % NBUF];
-            const bool copies = it + 2 < nchunks;            // chunk it+2 goes into chunk it-1's slot
+            const bool copies = it + AHEAD < nchunks;        // chunk it+AHEAD goes into chunk it-1's slot
             CopySrc cs;
-            if (copies) cs = copy_src(c + 2);
+            if (copies) cs = copy_src(c + AHEAD);
 
             // S^T (32 rows x 32 heads).  Step c2 < 32 reads value-part piece
             // 2*c2 + hi of row slot_row(col); later steps read the tail.  Copy
@@ -202,7 +216,7 @@ void sparse_attn_mla_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
                     sacc = mfma_bf16_32x32x16(as_bf8(kf[c2 % (kPre + 1)]), qf[c2], sacc);
 #pragma unroll
                     for (int j = 0; j < SPW; ++j)
-                        if (c2 == (j * S::QC) / SPW && copies) issue_copy(cs, c + 2, j);
+                        if (c2 == (j * S::QC) / SPW && copies) issue_copy(cs, c + AHEAD, j);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
