@@ -262,13 +262,38 @@ def training_side(cfg, dev, stream, steps):
     return res
 
 
-def forward_runner(cfg, inp, dev, stream):
+def forward_runner(cfg, inp, dev, stream, select=0):
     import sparse_attention_04_amd as dsa
     fwd = dsa.Forward(cfg.B, cfg.Lq, cfg.Lk, cfg.k, cfg.n_heads, cfg.d_v, inp["q"].dtype, dev, d_qk=cfg.d_qk,
-                      q_tile_rows=cfg.q_tile_rows)
+                      q_tile_rows=cfg.q_tile_rows, select=select)
     run = lambda: fwd(inp["q_idx"], inp.get("q_scale"), inp["k_idx"], inp.get("k_scale"), inp["w"], inp["q"],
                       inp["kv"], cfg.softmax_scale, q_pos0=cfg.q_pos0, stream=stream)
     return fwd, run
+
+
+def route_times(cfg, inp, dev, stream, steps):
+    """The forward by each selection route that takes the workload (score
+    tiles; candidate lists, which keep full score rows out of memory), median
+    ms, and the route the default (AUTO) takes: the one whose workspace size
+    it asks for."""
+    import torch
+    import sparse_attention_04_amd as dsa
+    ws = lambda sel: dsa.dsa_forward_workspace_size(cfg.B, cfg.Lq, cfg.Lk, cfg.k, cfg.n_heads, cfg.d_qk, cfg.d_v,
+                                                    inp["q"].dtype, cfg.q_tile_rows, sel)
+    out = {}
+    routes = {"score_tiles": dsa.SELECT_SCORE_TILES}
+    if cfg.idx_dtype == "fp8" and ws(dsa.SELECT_CANDIDATES) > 0:
+        routes["candidates"] = dsa.SELECT_CANDIDATES
+    for name, sel in routes.items():
+        fwd, run = forward_runner(cfg, inp, dev, stream, sel)
+        run()
+        torch.cuda.synchronize()
+        out[name] = median_ms(run, steps, stream)
+        del fwd, run
+        torch.cuda.empty_cache()
+    auto = "candidates" if ("candidates" in routes and ws(dsa.SELECT_AUTO) == ws(dsa.SELECT_CANDIDATES)) \
+        else "score_tiles"
+    return out, auto
 
 
 def time_stages(cfg, inp, fwd, dev, stream, steps):
@@ -386,6 +411,7 @@ def bench_workload(cfg, dev, stream, steps, warmup, want_oracle):
     ms = median_ms(run, steps, stream)
     tokens = cfg.B * cfg.Lq
     log(f"[bench] {cfg.name}: forward {ms:.3f} ms -> {tokens / (ms * 1e-3):.4g} tokens/s")
+    routes, route = route_times(cfg, inp, dev, stream, steps)
     stages = time_stages(cfg, inp, fwd, dev, stream, steps)
     roof, floor_s = stage_roofline(cfg, work, stages)
     res = {"tokens_per_s": tokens / (ms * 1e-3), "ms_per_step": ms, "steps": steps, "tokens": tokens,
@@ -393,6 +419,7 @@ def bench_workload(cfg, dev, stream, steps, warmup, want_oracle):
                       "n_idx_heads": cfg.n_idx_heads, "idx_dim": cfg.idx_dim, "idx_dtype": cfg.idx_dtype,
                       "n_heads": cfg.n_heads, "d_qk": cfg.d_qk, "d_v": cfg.d_v, "io_dtype": cfg.io_dtype,
                       "q_tile_rows": cfg.q_tile_rows},
+           "routes_ms": routes, "route": route,
            "stages_ms": stages, "stage_roofline": roof, "floor_ms": floor_s * 1e3,
            "e2e_frac_of_floor": floor_s / (ms * 1e-3)}
     if want_oracle:
@@ -479,6 +506,8 @@ def main():
                    "d_qk": cfg.d_qk, "d_v": cfg.d_v, "q_tile_rows": cfg.q_tile_rows},
     }
     if not args.no_stages:
+        res["routes_ms"], res["route"] = route_times(cfg, inp, dev, stream, max(1, args.steps))
+        log(f"[bench] routes {res['routes_ms']} (default: {res['route']})")
         stages = time_stages(cfg, inp, fwd, dev, stream, max(1, args.steps))
         torch.cuda.empty_cache()
         roof, floor_s = stage_roofline(cfg, work, stages)

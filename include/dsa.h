@@ -250,10 +250,12 @@ dsa_status dsa_sparse_attn_bwd(const void* q, const void* kv, const int32_t* idx
  *   Rows whose list is shorter than k or longer than 2k are recomputed from
  *   their full scores, in tiles of q_tile_rows rows, by the first route (only
  *   those rows' scores are written).  Requires FP8 indexer inputs, Lq >= 8,
- *   k <= 4096, and (Lk - 1) / R + 1 <= 16384.
+ *   k <= 2048, and (Lk - 1) / R + 1 <= 8192.
  *
- * DSA_SELECT_AUTO: the route measured faster on MI355X, which in this version
- *   is score tiles for every problem.
+ * DSA_SELECT_AUTO: candidates when they apply, k >= 1024 (the sample is then
+ *   at most 1/8 of the keys) and the problem has at least 1024 blocks of 16
+ *   query rows (B * ceil(Lq / 16)); score tiles otherwise.  For the workspace
+ *   size, AUTO assumes FP8 inputs.
  */
 typedef enum dsa_select {
     DSA_SELECT_AUTO = 0,

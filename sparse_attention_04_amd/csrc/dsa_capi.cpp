@@ -162,12 +162,11 @@ CandPlan cand_plan(int B, int Lq, int Lk, int k, bool fp8)
     c.Ls = ((Lk - 1) >> c.kshift) + 1;
     c.Ls_pad = (c.Ls + 3) & ~3;
     c.applies = fp8 && Lq >= 8 && k <= dsa::kSelectMaxCap / 2 && c.Ls <= dsa::kSelectMaxSample;
-    // AUTO keeps score tiles: at L = 32768 the candidate route measured
-    // 24.15-24.56 ms per forward against 24.07-24.11 ms (its filtered indexer
-    // pass, 3.5 ms, costs more than the score-writing one, and the sample,
-    // thresholds and selection, 0.8 ms, about what the top-k over full rows
-    // costs).
-    c.automatic = false;
+    // AUTO: candidates where the sample is at most 1/8 of the keys and the
+    // list pass fills the GPU without splitting keys over workgroups (at least
+    // 1024 blocks of 16 rows).  At L = 32768 they measured 23.39 ms per forward
+    // against 23.81 ms by score tiles.
+    c.automatic = c.applies && k >= 1024 && (int64_t)B * ((Lq + 15) / 16) >= 1024;
     return c;
 }
 

@@ -319,14 +319,14 @@ void indexer_fp8_kernel(const uint8_t* __restrict__ q8, const float* __restrict_
             const uint32_t c = (uint32_t)__builtin_popcount(m);
             const uint32_t incl = row16_incl_scan(c);
             const uint32_t total = (uint32_t)__shfl((int)incl, lane | 15, kWave);
-            uint32_t pos = crun + incl - c;
+            // entry positions past cap are clamped to the last slot: such a
+            // row overflows, its list is never read
+            const uint32_t pos = crun + incl - c;
             uint32_t* dst = x.cand + (size_t)crow * (size_t)x.cap * 2;
-            while (m) {
-                const int r = __builtin_ctz(m);
-                m &= m - 1;
-                if (pos < (uint32_t)x.cap)
-                    *(u32x2*)(dst + 2 * (size_t)pos) = u32x2{__float_as_uint(v[r]), (uint32_t)(sb + r)};
-                ++pos;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const uint32_t pr = min(pos + (uint32_t)__builtin_popcount(m & ((1u << r) - 1u)), (uint32_t)x.cap - 1u);
+                if (m & (1u << r)) *(u32x2*)(dst + 2 * (size_t)pr) = u32x2{__float_as_uint(v[r]), (uint32_t)(sb + r)};
             }
             crun += total;
         } else if (er < rows_here) {

@@ -136,8 +136,8 @@ hipError_t launch_topk(const TopkLaunch& a, hipStream_t s);
 hipError_t launch_select_threshold(const SelectLaunch& a, hipStream_t s);
 hipError_t launch_select_candidates(const SelectLaunch& a, hipStream_t s);
 // largest sample row and list the selection kernels take
-constexpr int kSelectMaxSample = 16384;
-constexpr int kSelectMaxCap = 8192;
+constexpr int kSelectMaxSample = 8192;
+constexpr int kSelectMaxCap = 4096;
 hipError_t launch_sparse_attn(const AttnLaunch& a, hipStream_t s);
 // bf16 576/512 rows, 32/64/128 heads, k <= 2048 (attn_mla.hip): ns splits
 // of cps chunks each (ns > 1: partials to part_o / part_lse for the merge)

@@ -169,8 +169,8 @@ def test_forward_workspace(L):
         assert ws(1, Lk, Lk, 2048, 0) == tiles
         # candidates on top of the fallback tiles
         assert ws(1, Lk, Lk, 2048, 0, SEL_CAND) == tiles + _cand_extra(1, Lk, Lk, 2048)
-        # AUTO takes score tiles
-        assert ws(1, Lk, Lk, 2048, 0, SEL_AUTO) == tiles
+        # AUTO takes candidates from 1024 blocks of 16 rows up (not at L = 4096)
+        assert ws(1, Lk, Lk, 2048, 0, SEL_AUTO) == (tiles if Lk == 4096 else tiles + _cand_extra(1, Lk, Lk, 2048))
     assert ws(1, 32768, 32768, 512, 0, SEL_AUTO) == ws(1, 32768, 32768, 512, 0)      # k < 1024: tiles
     assert ws(1, 300, 300, 64, 0, SEL_CAND) == ws(1, 300, 300, 64, 0) + _cand_extra(1, 300, 300, 64)
     # decode batch: scores, indices and the attention's split partials (4 splits)
@@ -178,8 +178,9 @@ def test_forward_workspace(L):
     assert ws(64, 1, 65536, 2048, 0, SEL_AUTO) == ws(64, 1, 65536, 2048, 0)
     # routes that do not take the problem, and unknown routes
     assert ws(64, 1, 65536, 2048, 0, SEL_CAND) == 0                 # Lq < 8
-    assert ws(1, 8192, 8192, 5000, 0, SEL_CAND) == 0                # k > 4096
-    assert ws(1, 1 << 16, 1 << 16, 64, 0, SEL_CAND) == 0            # a sample of 65536 keys
+    assert ws(1, 8192, 8192, 3000, 0, SEL_CAND) == 0                # k > 2048
+    assert ws(1, 1 << 14, 1 << 14, 64, 0, SEL_CAND) == 0            # a sample of 16384 keys
+    assert ws(1, 131072, 131072, 2048, 4096, SEL_CAND) > 0         # a sample of 8192 keys
     assert ws(1, 8, 8, 4, 0, 3) == 0 and ws(1, 8, 8, 4, -1) == 0
     assert ws(0, 1, 1, 1, 0) == 0
     need = ws(1, 8, 8, 4, 0)
