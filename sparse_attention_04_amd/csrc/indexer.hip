@@ -83,7 +83,11 @@ void indexer_fp8_kernel(const uint8_t* __restrict__ q8, const float* __restrict_
                         IdxExt x)
 {
     __shared__ __attribute__((aligned(16))) uint8_t ktile[2][kKG * kD];
-    __shared__ __attribute__((aligned(16))) v4f red[2][4][4][kWave];     // [buffer][wave][tile][lane]
+    // [buffer][wave][row r * 16 + (quad e ^ r)]: wave w's partial sums of block
+    // row r at keys 4e .. 4e+3 of the group; the XOR makes both the writes (16
+    // rows at one quad) and the reads (one row, 16 quads) hit 16 distinct
+    // 16-byte bank groups
+    __shared__ __attribute__((aligned(16))) v4f red[2][4][16 * kQB];
     __shared__ __attribute__((aligned(16))) uint32_t cpart[3][kQB][kD / 2]; // bf16 pairs: hi, mid, lo
 
     const int nqb = (t_count + kQB - 1) / kQB;
@@ -278,7 +282,7 @@ void indexer_fp8_kernel(const uint8_t* __restrict__ q8, const float* __restrict_
                 d = d1;
                 d1 = d2;
             }
-            red[kb][wave][i][lane] = acc;
+            red[kb][wave][col * 16 + ((4 * i + grp) ^ col)] = acc;
             if (i + 1 < 4) {
                 kk = kk_next;
                 af = af_next;
@@ -286,13 +290,12 @@ void indexer_fp8_kernel(const uint8_t* __restrict__ q8, const float* __restrict_
         }
         wait_vmcnt0();
         __syncthreads();
-        // sum the four waves' partials of row er, keys sb .. sb + 3 (tile
-        // eq / 4, written by lane er + 16 (eq % 4) of each wave)
-        const int rl = er + 16 * (eq & 3), rt = eq >> 2;
-        v4f sum = red[kb][0][rt][rl];
+        // sum the four waves' partials of row er, keys sb .. sb + 3
+        const int rs = er * 16 + (eq ^ er);
+        v4f sum = red[kb][0][rs];
 #pragma unroll
         for (int ww = 1; ww < 4; ++ww) {
-            const v4f x = red[kb][ww][rt][rl];
+            const v4f x = red[kb][ww][rs];
             sum[0] += x[0]; sum[1] += x[1]; sum[2] += x[2]; sum[3] += x[3];
         }
         if (write_masked) {
@@ -318,7 +321,8 @@ void indexer_fp8_kernel(const uint8_t* __restrict__ q8, const float* __restrict_
             }
             const uint32_t c = (uint32_t)__builtin_popcount(m);
             const uint32_t incl = row16_incl_scan(c);
-            const uint32_t total = (uint32_t)__shfl((int)incl, lane | 15, kWave);
+            // the row's count: lane 15 of the 16-lane row, broadcast (DPP row_newbcast)
+            const uint32_t total = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)incl, 0x15F, 0xF, 0xF, false);
             // entry positions past cap are clamped to the last slot: such a
             // row overflows, its list is never read
             const uint32_t pos = crun + incl - c;
