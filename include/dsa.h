@@ -219,11 +219,15 @@ dsa_status dsa_indexer_kl(const void* q, const void* kv, const float* scores, fl
  *   q [B,Lq,n_heads,576] bf16; kv [B,Lk,576] bf16; idx [B,Lq,k] int32
  *   out, dout [B,Lq,n_heads,512] bf16; lse [B,Lq,n_heads] fp32
  *   dq [B,Lq,n_heads,576] fp32 (output); dkv [B,Lk,576] fp32 (output, overwritten)
- * P and dZ pass through the workspace in bf16 (the MFMA operand precision);
- * dkv is accumulated with fp32 atomics, so its last bits vary between runs.
- * Supported: (d_qk, d_v) = (576, 512), n_heads in {16, 32, 64, 128}, k <= 2048.
+ * P and dZ pass through the workspace in bf16 (the MFMA operand precision).
+ * dkv: each entry's 576 fp32 contributions go to a slot of a key-major buffer
+ * in the workspace (B * Lq * k slots of 2304 bytes), and each key's slots are
+ * summed in slot order.  An entry's slot among its key's comes from an atomic
+ * counter, so dkv's last bits vary between runs; dq is deterministic.
+ * Supported: (d_qk, d_v) = (576, 512), n_heads in {16, 32, 64, 128}, k <= 2048,
+ * B * Lq * k and B * Lk below 2^31.
  */
-size_t dsa_sparse_attn_bwd_workspace_size(int B, int Lq, int n_heads, int k);
+size_t dsa_sparse_attn_bwd_workspace_size(int B, int Lq, int Lk, int n_heads, int k);
 
 dsa_status dsa_sparse_attn_bwd(const void* q, const void* kv, const int32_t* idx, const void* out,
                                const float* lse, const void* dout, float* dq, float* dkv,

@@ -66,7 +66,7 @@ def _load() -> ctypes.CDLL:
     L.dsa_rope_assemble.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, f64, vp]
     L.dsa_kv_pack_fp8.argtypes = [vp, vp, i64, vp]
     L.dsa_indexer_kl.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, vp]
-    L.dsa_sparse_attn_bwd_workspace_size.argtypes = [i32, i32, i32, i32]
+    L.dsa_sparse_attn_bwd_workspace_size.argtypes = [i32, i32, i32, i32, i32]
     L.dsa_sparse_attn_bwd_workspace_size.restype = sz
     L.dsa_sparse_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, f32,
                                       vp, sz, vp]
@@ -374,7 +374,7 @@ def dsa_sparse_attn_bwd(q, kv, idx, out, lse, dout, softmax_scale: float, q_pos0
     if dkv is None:
         dkv = torch.empty((B, Lk, Dqk), dtype=torch.float32, device=q.device)
     if workspace is None:
-        n = int(lib.dsa_sparse_attn_bwd_workspace_size(B, Lq, H, k))
+        n = int(lib.dsa_sparse_attn_bwd_workspace_size(B, Lq, Lk, H, k))
         workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=q.device)
     _check("dsa_sparse_attn_bwd", lib.dsa_sparse_attn_bwd(
         _p(q), _p(kv), _p(idx), _p(out), _p(lse), _p(dout), _p(dq), _p(dkv), B, Lq, Lk, q_pos0, H, Dqk, Dv, k,

@@ -17,12 +17,17 @@
 //     LDS transpose reads.  P and dZ are also written (bf16, keys-major) for 2.
 //  2. dkv: one workgroup per (row, 6 of the 18 column tiles of 32), one wave
 //     per 2 tiles.  A tile of the first 512 columns takes both products,
-//     scale dZ q and P dO, into one accumulator (one atomic per element, not
-//     two); the last 2 tiles take scale dZ q only.  The B operands (q and dO,
-//     heads along K) stay in registers for the whole row; per chunk the 32 x H
-//     weights (P and scale dZ) come through LDS and each 32 x 32 tile is added
-//     to the selected rows with fp32 atomics (so dkv's summation order varies
-//     between runs).
+//     scale dZ q and P dO, into one accumulator; the last 2 tiles take scale
+//     dZ q only.  The B operands (q and dO, heads along K) stay in registers
+//     for the whole row; per chunk the 32 x H weights (P and scale dZ) come
+//     through LDS, and each entry's 576 contributions are stored (fp32) to
+//     its slot of a key-major buffer: key s owns the slots [off[s], off[s] +
+//     count[s]), and an entry's place among them is the rank an atomic
+//     counter gave it in a pass over idx.
+//  3. dkv[s] = the sum of key s's slots, in slot order, one wave per (key, 64
+//     columns); keys no entry selects get 0.  Plain stores and streaming
+//     reads replace one fp32 atomic per (entry, column); the slot order, and
+//     so dkv's last bits, vary between runs.
 #include "hw.h"
 #include "launch.h"
 
@@ -274,7 +279,8 @@ template <int KS>                                                       // K ste
 __global__ __launch_bounds__(kDkvThreads, 2)                            // two workgroups per CU
 void attn_bwd_dkv_kernel(const uint16_t* __restrict__ q, const int32_t* __restrict__ idx,
                          const uint16_t* __restrict__ dout, const uint16_t* __restrict__ wsP,
-                         const uint16_t* __restrict__ wsZ, float* __restrict__ dkv, int Lq, int Lk, int k,
+                         const uint16_t* __restrict__ wsZ, const int32_t* __restrict__ rank,
+                         const int32_t* __restrict__ off, float* __restrict__ contrib, int Lq, int Lk, int k,
                          float scale)
 {
     constexpr int H = 16 * KS;
@@ -283,6 +289,7 @@ void attn_bwd_dkv_kernel(const uint16_t* __restrict__ q, const int32_t* __restri
     constexpr int WPER = (WTOT + kDkvThreads - 1) / kDkvThreads;        // per thread (the last round partial)
     __shared__ __attribute__((aligned(16))) uint16_t W[2][2][kBNC * WP];  // [buffer][P | dZ][key][head]
     __shared__ __attribute__((aligned(16))) int32_t sel[kBKMax];           // the row's index list (-1 padded)
+    __shared__ __attribute__((aligned(16))) int32_t slot[kBKMax];          // each entry's slot (-1: none)
     __shared__ int wlast[kDkvWaves];
     const int t = blockIdx.x, b = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -323,6 +330,7 @@ void attn_bwd_dkv_kernel(const uint16_t* __restrict__ q, const int32_t* __restri
         const int s = (i < k) ? irow[i] : -1;
         const bool ok = s >= 0 && s < Lk;
         sel[i] = ok ? s : -1;
+        slot[i] = ok ? off[(int64_t)b * Lk + s] + rank[qrow * k + i] : -1;
         last = ok ? i : last;
     }
 #pragma unroll
@@ -359,7 +367,6 @@ void attn_bwd_dkv_kernel(const uint16_t* __restrict__ q, const int32_t* __restri
             *(u32x4*)(&W[c & 1][which][kk * WP + 8 * cc]) = in ? wr[e] : u32x4{0u, 0u, 0u, 0u};
         }
     };
-    float* dkvb = dkv + (int64_t)b * Lk * kBQK;
     u32x4 wr[WPER];
     if (nch > 0) {
         load_w(0, wr);
@@ -370,10 +377,6 @@ void attn_bwd_dkv_kernel(const uint16_t* __restrict__ q, const int32_t* __restri
         const int cn = min(ch + 1, nch - 1);                            // the last chunk reloads itself
         __syncthreads();                                                // W of ch complete; the other buffer free
         load_w(cn, wr);
-        // an entry that is not a row (zero weights) adds 0 to the chunk's first
-        // row, so that every atomic instruction is issued
-        const uint64_t vm = __ballot(lane < kBNC && sel[c0 + (lane & 31)] >= 0);
-        const int s_any = __builtin_amdgcn_readfirstlane(vm ? sel[c0 + __builtin_ctzll(vm)] : 0);
 #pragma unroll
         for (int j = 0; j < kTilesPerWave; ++j) {
             const int T = tile0 + j;
@@ -393,12 +396,80 @@ void attn_bwd_dkv_kernel(const uint16_t* __restrict__ q, const int32_t* __restri
             const int d = 32 * T + n;
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const int s = sel[c0 + 8 * (v >> 2) + 4 * hs + (v & 3)];
-                unsafeAtomicAdd(dkvb + (int64_t)(s >= 0 ? s : s_any) * kBQK + d, acc[v]);
+                const int sl = slot[c0 + 8 * (v >> 2) + 4 * hs + (v & 3)];
+                if (sl >= 0) contrib[(int64_t)sl * kBQK + d] = acc[v];
             }
         }
         store_w(cn, wr);
     }
+}
+
+// ---------------------------------------------------------------- slots and the per-key sums
+
+// rank[b, t, i] = this entry's place among the entries of its key (from an
+// atomic counter, so the order among one key's entries varies between runs);
+// count[b, s] ends as the number of entries of key s.  Entries that are not a
+// row get -1.
+__global__ __launch_bounds__(256)
+void bwd_rank_kernel(const int32_t* __restrict__ idx, int32_t* __restrict__ rank, int32_t* __restrict__ count,
+                     int64_t n_entries, int per_b, int Lk)
+{
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= n_entries) return;
+    const int s = idx[e];
+    const int b = (int)(e / per_b);
+    rank[e] = (s >= 0 && s < Lk) ? atomicAdd(&count[(int64_t)b * Lk + s], 1) : -1;
+}
+
+// off[j] = count[0] + ... + count[j - 1] over j < n (one workgroup of 1024
+// threads: each scans a contiguous run, a block scan orders the runs).
+__global__ __launch_bounds__(1024)
+void bwd_offsets_kernel(const int32_t* __restrict__ count, int32_t* __restrict__ off, int64_t n)
+{
+    __shared__ uint32_t wsum[16];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t per = (n + 1023) / 1024;
+    const int64_t j0 = min((int64_t)tid * per, n), j1 = min(j0 + per, n);
+    uint32_t local = 0;
+    for (int64_t j = j0; j < j1; ++j) local += (uint32_t)count[j];
+    const uint32_t incl = wave_incl_scan(local, lane);
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    uint32_t base = incl - local;
+    for (int w = 0; w < wave; ++w) base += wsum[w];
+    for (int64_t j = j0; j < j1; ++j) {
+        off[j] = (int32_t)base;
+        base += (uint32_t)count[j];
+    }
+}
+
+// dkv[b, s, 64 c + lane] = the sum of column 64 c + lane over key s's slots,
+// in slot order; one wave per (key, 64 columns), eight slots in flight.  Keys
+// are visited in ascending s, the longest segments of a causal problem first.
+constexpr int kRedCols = kBQK / 64;                                     // 9 column blocks
+__global__ __launch_bounds__(256)
+void bwd_key_sum_kernel(const float* __restrict__ contrib, const int32_t* __restrict__ off,
+                        const int32_t* __restrict__ count, float* __restrict__ dkv, int64_t n_keys)
+{
+    const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (w >= n_keys * kRedCols) return;                                 // whole waves leave
+    const int lane = threadIdx.x & 63;
+    const int64_t j = w / kRedCols;                                     // key (b * Lk + s)
+    const int c = (int)(w % kRedCols);
+    const int64_t r0 = off[j];
+    const int cnt = count[j];
+    const float* src = contrib + r0 * kBQK + 64 * c + lane;
+    float acc = 0.f;
+    int r = 0;
+    for (; r + 8 <= cnt; r += 8) {
+        float x[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) x[u] = src[(int64_t)(r + u) * kBQK];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc += x[u];
+    }
+    for (; r < cnt; ++r) acc += src[(int64_t)r * kBQK];
+    dkv[j * kBQK + 64 * c + lane] = acc;
 }
 
 __global__ __launch_bounds__(256)
@@ -410,20 +481,53 @@ void fill_zero_kernel(float* __restrict__ p, int64_t n4)
 
 }  // namespace
 
-size_t attn_bwd_workspace_bytes(int B, int Lq, int H, int k)
+// Workspace: P and dZ (bf16, [B, Lq, k, H] each), the entries' ranks
+// ([B, Lq, k] int32), the per-key counts and offsets ([B, Lk] int32 each) and
+// the key-major contributions (one 576-float slot per entry of idx), each part
+// 256-byte aligned.
+struct BwdLayout {
+    size_t p, rank, count, off, contrib, total;
+};
+
+BwdLayout bwd_layout(int B, int Lq, int Lk, int H, int k)
 {
-    return 2 * (size_t)B * Lq * k * H * sizeof(uint16_t);
+    auto r256 = [](size_t x) { return (x + 255u) & ~(size_t)255u; };
+    const size_t entries = (size_t)B * Lq * k;
+    BwdLayout L{};
+    L.p = r256(2 * entries * H * sizeof(uint16_t));
+    L.rank = r256(entries * sizeof(int32_t));
+    L.count = r256((size_t)B * Lk * sizeof(int32_t));
+    L.off = r256((size_t)B * Lk * sizeof(int32_t));
+    L.contrib = r256(entries * kBQK * sizeof(float));
+    L.total = L.p + L.rank + L.count + L.off + L.contrib;
+    return L;
+}
+
+size_t attn_bwd_workspace_bytes(int B, int Lq, int Lk, int H, int k)
+{
+    return bwd_layout(B, Lq, Lk, H, k).total;
 }
 
 hipError_t launch_attn_bwd(const AttnBwdLaunch& a, hipStream_t s)
 {
     if (a.B == 0 || a.Lq == 0) return hipSuccess;
-    uint16_t* wsP = (uint16_t*)a.workspace;
+    const BwdLayout Lw = bwd_layout(a.B, a.Lq, a.Lk, a.H, a.k);
+    char* wp = (char*)a.workspace;
+    uint16_t* wsP = (uint16_t*)wp;
     uint16_t* wsZ = wsP + (size_t)a.B * a.Lq * a.k * a.H;
-    // dkv = 0 (a kernel, not a memset, so the sequence can be captured in a graph)
-    const int64_t n4 = (int64_t)a.B * a.Lk * kBQK / 4;
-    hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)std::min<int64_t>((n4 + 255) / 256, 65536)), dim3(256), 0, s,
-                       a.dkv, n4);
+    int32_t* rank = (int32_t*)(wp + Lw.p);
+    int32_t* count = (int32_t*)(wp + Lw.p + Lw.rank);
+    int32_t* off = (int32_t*)(wp + Lw.p + Lw.rank + Lw.count);
+    float* contrib = (float*)(wp + Lw.p + Lw.rank + Lw.count + Lw.off);
+    // counts = 0 (a kernel, not a memset, so the sequence can be captured in a graph)
+    const int64_t n_keys = (int64_t)a.B * a.Lk;
+    const int64_t c4 = (n_keys + 3) / 4;                                // the count region is 256-byte padded
+    hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)std::min<int64_t>((c4 + 255) / 256, 65536)), dim3(256), 0, s,
+                       (float*)count, c4);
+    const int64_t n_entries = (int64_t)a.B * a.Lq * a.k;
+    hipLaunchKernelGGL(bwd_rank_kernel, dim3((unsigned)((n_entries + 255) / 256)), dim3(256), 0, s, a.idx, rank, count,
+                       n_entries, a.Lq * a.k, a.Lk);
+    hipLaunchKernelGGL(bwd_offsets_kernel, dim3(1), dim3(1024), 0, s, (const int32_t*)count, off, n_keys);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int nw = a.H >= 64 ? 4 : a.H / 16;
@@ -444,7 +548,8 @@ hipError_t launch_attn_bwd(const AttnBwdLaunch& a, hipStream_t s)
     const dim3 g2(a.Lq, a.B, (kDkvTiles + kTilesPerGroup - 1) / kTilesPerGroup);
 #define DSA_DKV(KS)                                                                                           \
     hipLaunchKernelGGL(attn_bwd_dkv_kernel<KS>, g2, dim3(kDkvThreads), 0, s, (const uint16_t*)a.q, a.idx,     \
-                       (const uint16_t*)a.dout, wsP, wsZ, a.dkv, a.Lq, a.Lk, a.k, a.scale)
+                       (const uint16_t*)a.dout, wsP, wsZ, (const int32_t*)rank, (const int32_t*)off, contrib,   \
+                       a.Lq, a.Lk, a.k, a.scale)
     switch (a.H / 16) {
     case 1: DSA_DKV(1); break;
     case 2: DSA_DKV(2); break;
@@ -453,6 +558,11 @@ hipError_t launch_attn_bwd(const AttnBwdLaunch& a, hipStream_t s)
     default: return hipErrorInvalidValue;
     }
 #undef DSA_DKV
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t waves = n_keys * kRedCols;
+    hipLaunchKernelGGL(bwd_key_sum_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, (const float*)contrib,
+                       (const int32_t*)off, (const int32_t*)count, a.dkv, n_keys);
     return hipGetLastError();
 }
 

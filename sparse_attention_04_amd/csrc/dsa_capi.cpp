@@ -499,10 +499,10 @@ dsa_status dsa_indexer_kl(const void* q, const void* kv, const float* scores, fl
     return hip_status(fn, dsa::launch_indexer_kl(a, (hipStream_t)stream));
 }
 
-size_t dsa_sparse_attn_bwd_workspace_size(int B, int Lq, int n_heads, int k)
+size_t dsa_sparse_attn_bwd_workspace_size(int B, int Lq, int Lk, int n_heads, int k)
 {
-    if (B <= 0 || Lq <= 0 || n_heads <= 0 || k <= 0) return 0;
-    return round256(dsa::attn_bwd_workspace_bytes(B, Lq, n_heads, k));
+    if (B <= 0 || Lq <= 0 || Lk <= 0 || n_heads <= 0 || k <= 0) return 0;
+    return round256(dsa::attn_bwd_workspace_bytes(B, Lq, Lk, n_heads, k));
 }
 
 dsa_status dsa_sparse_attn_bwd(const void* q, const void* kv, const int32_t* idx, const void* out,
@@ -529,7 +529,9 @@ dsa_status dsa_sparse_attn_bwd(const void* q, const void* kv, const int32_t* idx
     if (k < 1 || k > 2048) return fail(DSA_ERR_UNSUPPORTED, "%s: k=%d outside [1, 2048]", fn, k);
     if (!(std::isfinite(softmax_scale) && softmax_scale > 0.f))
         return fail(DSA_ERR_SHAPE, "%s: softmax_scale must be finite and > 0", fn);
-    const size_t need = dsa_sparse_attn_bwd_workspace_size(B, Lq, n_heads, k);
+    if ((int64_t)B * Lq * k >= ((int64_t)1 << 31) || (int64_t)B * Lk >= ((int64_t)1 << 31))
+        return fail(DSA_ERR_UNSUPPORTED, "%s: B * Lq * k and B * Lk must be below 2^31", fn);
+    const size_t need = dsa_sparse_attn_bwd_workspace_size(B, Lq, Lk, n_heads, k);
     if (workspace == nullptr || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0)
         return fail(DSA_ERR_WORKSPACE, "%s: workspace needs %zu bytes, 256-byte aligned (got %zu at %p)", fn, need,
                     workspace_bytes, workspace);

@@ -103,7 +103,7 @@ struct AttnBwdLaunch {
     const void* dout;       // [B, Lq, H, 512] bf16
     float* dq;              // [B, Lq, H, 576]
     float* dkv;             // [B, Lk, 576]
-    void* workspace;        // attn_bwd_workspace_bytes(B, Lq, H, k)
+    void* workspace;        // attn_bwd_workspace_bytes(B, Lq, Lk, H, k)
     int B, Lq, Lk, H, k;
     float scale;
 };
@@ -148,7 +148,7 @@ hipError_t launch_rope_assemble(const RopeLaunch& a, hipStream_t s);
 hipError_t launch_kv_pack_fp8(const KvPackLaunch& a, hipStream_t s);
 hipError_t launch_indexer_kl(const KlLaunch& a, hipStream_t s);
 hipError_t launch_attn_bwd(const AttnBwdLaunch& a, hipStream_t s);
-size_t attn_bwd_workspace_bytes(int B, int Lq, int H, int k);
+size_t attn_bwd_workspace_bytes(int B, int Lq, int Lk, int H, int k);
 
 // Split factor for the selected set when few query rows are attended (1 = no
 // split), and the bytes of partial results it needs.
