@@ -25,6 +25,7 @@ SOURCES = [
     ("select.hip", []),
     ("sparse_attn.hip", []),
     ("attn_mla.hip", []),
+    ("attn_mqa.hip", []),
     ("inputs.hip", []),
     ("kl.hip", []),
     ("attn_bwd.hip", []),

@@ -38,18 +38,6 @@ namespace dsa {
 
 namespace {
 
-// Asynchronous 16-byte copy global -> LDS with a wave-uniform 64-bit base in
-// SGPRs and a 32-bit per-lane byte offset (the saddr form, no per-lane 64-bit
-// address arithmetic).  Lane l's 16 bytes land at lds_byte_addr + 16 l; the
-// wave fences it itself (s_waitcnt vmcnt + a barrier before the slot is read).
-__device__ __forceinline__ void global_to_lds16_saddr(const void* sbase, uint32_t voff, uint32_t lds_byte_addr)
-{
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-                 :
-                 : "v"(voff), "s"(sbase), "s"(lds_byte_addr)
-                 : "memory");
-}
-
 template <int NW, bool SPLIT>
 __global__ __launch_bounds__(64 * NW)
 void sparse_attn_mla_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
@@ -141,10 +129,7 @@ void sparse_attn_mla_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
             const int r = wave * S::RPW + j;
             const int sr = __builtin_amdgcn_readlane(cs.vrl, j);
             // the row's address as a wave-uniform (scalar) 64-bit base
-            const uint64_t ga = (uint64_t)(uintptr_t)(kvb + (int64_t)sr * 576);
-            const uint32_t glo = __builtin_amdgcn_readfirstlane((uint32_t)ga);
-            const uint32_t ghi = __builtin_amdgcn_readfirstlane((uint32_t)(ga >> 32));
-            global_to_lds16_saddr((const void*)(uintptr_t)(((uint64_t)ghi << 32) | glo), (uint32_t)lane * 16u,
+            global_to_lds16_saddr(wave_uniform_ptr(kvb + (int64_t)sr * 576), (uint32_t)lane * 16u,
                                   __builtin_amdgcn_readfirstlane(base + (uint32_t)r * S::VPITCH));
         } else {
             const int jj = j - S::RPW;

@@ -73,6 +73,27 @@ __device__ __forceinline__ void global_to_lds16_async(const void* gptr, uint32_t
                  : "memory");
 }
 
+// A pointer every lane of the wave holds, made wave-uniform (SGPRs): each
+// half goes through readfirstlane, which returns a signed int, so the halves
+// are taken as uint32_t before they are put together.
+__device__ __forceinline__ const void* wave_uniform_ptr(const void* p)
+{
+    const uint64_t a = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+    return (const void*)(uintptr_t)(((uint64_t)hi << 32) | (uint64_t)lo);
+}
+
+// The same copy with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane
+// byte offset (the saddr form, no per-lane 64-bit address arithmetic).
+__device__ __forceinline__ void global_to_lds16_saddr(const void* sbase, uint32_t voff, uint32_t lds_byte_addr)
+{
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(sbase), "s"(lds_byte_addr)
+                 : "memory");
+}
+
 // 4-byte variant: lane l's 4 bytes land at lds_byte_addr + 4*l.
 __device__ __forceinline__ void global_to_lds4_async(const void* gptr, uint32_t lds_byte_addr)
 {

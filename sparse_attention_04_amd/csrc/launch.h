@@ -143,6 +143,11 @@ hipError_t launch_sparse_attn(const AttnLaunch& a, hipStream_t s);
 // of cps chunks each (ns > 1: partials to part_o / part_lse for the merge)
 hipError_t launch_sparse_attn_mla(const AttnLaunch& a, hipStream_t s, int ns, int cps, float* part_o,
                                   float* part_lse);
+// bf16 rows of D = d_qk = d_v in {64, 128}, H / 16 waves (1, 2, 4 or 8 and
+// dividing D / 16), k <= 2048, rows addressable by 32-bit byte offsets
+// (attn_mqa.hip)
+bool sparse_attn_mqa_supported(int H, int D, int k, int Lk);
+hipError_t launch_sparse_attn_mqa(const AttnLaunch& a, hipStream_t s);
 hipError_t launch_quantize_e4m3(const QuantLaunch& a, hipStream_t s);
 hipError_t launch_rope_assemble(const RopeLaunch& a, hipStream_t s);
 hipError_t launch_kv_pack_fp8(const KvPackLaunch& a, hipStream_t s);

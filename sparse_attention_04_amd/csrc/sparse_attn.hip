@@ -510,8 +510,10 @@ void sparse_attn_bf16_w32_kernel(const uint16_t* __restrict__ q, const void* __r
     }
 }
 
-// bf16 kernel for rows of D = d_qk = d_v in {64, 128} (the MQA shapes): one
-// workgroup per query row, one wave per 16 heads, v_mfma_f32_16x16x32_bf16.
+// bf16 kernel for rows of D = d_qk = d_v in {64, 128} (the MQA shapes) with
+// the head counts attn_mqa.hip does not take (H / 16 waves not 1, 2, 4 or 8,
+// or not dividing D / 16): one workgroup per query row, one wave per 16
+// heads, v_mfma_f32_16x16x32_bf16.
 //  - The query's index list (k <= 2048) is staged in LDS once; the selected
 //    rows stream through a two-slot LDS ring of 32 rows, copied
 //    asynchronously one chunk ahead, 1 KB (1024 / 2D rows) per copy
@@ -898,6 +900,8 @@ hipError_t launch_sparse_attn(const AttnLaunch& a, hipStream_t s)
         if (a.Dqk == 576 && a.Dv == 512) e = launch_bf16_w32_any<576, 512>(a, s, &handled);
         if (handled) return e;
     }
+    if (a.bf16 && a.Dqk == a.Dv && sparse_attn_mqa_supported(a.H, a.Dqk, a.k, a.Lk))
+        return launch_sparse_attn_mqa(a, s);
     if (a.bf16 && a.k <= 2048 && a.Dqk == a.Dv && (a.Dqk == 128 || a.Dqk == 64)) {
         const float scale_log2 = a.scale * 1.4426950408889634f;
 #define DSA_W16(D, NW)                                                                                          \
