@@ -177,6 +177,7 @@ void sparse_attn_mla_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
             const bool copies = it + AHEAD < nchunks;        // chunk it+AHEAD goes into chunk it-1's slot
             CopySrc cs;
             if (copies) cs = copy_src(c + AHEAD);
+            const uint32_t vmask = valid_mask(c);            // read ahead of Q.K, off the softmax's path
 
             // S^T (32 rows x 32 heads).  Step c2 < 32 reads value-part piece
             // 2*c2 + hi of row slot_row(col); later steps read the tail.  Copy
@@ -206,7 +207,6 @@ void sparse_attn_mla_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
                 }
             }
 
-            const uint32_t vmask = valid_mask(c);
             if (vmask == 0u) continue;                       // nothing selected here (uniform)
             if (vmask != 0xFFFFFFFFu) {
                 // element v holds chunk row slot_row(8 (v/4) + 4 hi + v%4) = hi + rv(v)
