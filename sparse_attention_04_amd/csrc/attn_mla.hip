@@ -181,8 +181,8 @@ void sparse_attn_mla_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
 
             // S^T (32 rows x 32 heads).  Step c2 < 32 reads value-part piece
             // 2*c2 + hi of row slot_row(col); later steps read the tail.  Copy
-            // j of chunk it+2 is issued after MFMA 36 j / SPW (every step has one
-            // when a wave copies 36 pieces per chunk).
+            // j of chunk it+AHEAD is issued after MFMA min(36 j / SPW + 2, 35)
+            // (two MFMAs in, so the LDS reads of its sources have landed).
             v16f sacc;
 #pragma unroll
             for (int v = 0; v < 16; ++v) sacc[v] = 0.f;
@@ -202,10 +202,28 @@ void sparse_attn_mla_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
                     sacc = mfma_bf16_32x32x16(as_bf8(kf[c2 % (kPre + 1)]), qf[c2], sacc);
 #pragma unroll
                     for (int j = 0; j < SPW; ++j)
-                        if (c2 == (j * S::QC) / SPW && copies) issue_copy(cs, c + AHEAD, j);
+                        if (c2 == min((j * S::QC) / SPW + 2, S::QC - 1) && copies) issue_copy(cs, c + AHEAD, j);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
+
+            // The first V^T fragments of P.V, read before the softmax so that
+            // their LDS latency runs under it.  K slot (a, j) of lane group hi
+            // is S^T row slot 16*tt + 8a + 4*hi + j, i.e. chunk row
+            // 16*tt + 2a + hi + 4j; the lane reads dims dt*32 + 16*g2 + 4*qs ..
+            // +3 of its source row.
+            const uint8_t* vb = cur + 32 * g2 + 8 * qs;
+            auto vfrag = [&](int s) -> u32x4 {
+                const int tt = s >> 4, dt = s & 15;
+                const int r0 = 16 * tt + hi + 4 * js;
+                const u32x2 a = __builtin_bit_cast(u32x2, lds_read_tr16(vb + r0 * S::VPITCH + 64 * dt));
+                const u32x2 bq = __builtin_bit_cast(u32x2, lds_read_tr16(vb + (r0 + 2) * S::VPITCH + 64 * dt));
+                return u32x4{a[0], a[1], bq[0], bq[1]};
+            };
+            u32x4 vf[kPvPre + 1];
+#pragma unroll
+            for (int i = 0; i < kPvPre; ++i) vf[i] = vfrag(i);
+            __builtin_amdgcn_sched_barrier(0);
 
             if (vmask == 0u) continue;                       // nothing selected here (uniform)
             if (vmask != 0xFFFFFFFFu) {
@@ -238,22 +256,9 @@ void sparse_attn_mla_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
 #pragma unroll
             for (int v = 0; v < 8; ++v) soft(v);
 
-            // O^T += V^T . P^T, two 16-row K steps (step s = 16 tt + dt).  K
-            // slot (a, j) of lane group hi is S^T row slot 16*tt + 8a + 4*hi + j,
-            // i.e. chunk row 16*tt + 2a + hi + 4j; the lane reads dims
-            // dt*32 + 16*g2 + 4*qs .. +3 of its source row.  The softmax of
-            // elements 8..15 runs between the first eight MFMAs.
-            const uint8_t* vb = cur + 32 * g2 + 8 * qs;
-            auto vfrag = [&](int s) -> u32x4 {
-                const int tt = s >> 4, dt = s & 15;
-                const int r0 = 16 * tt + hi + 4 * js;
-                const u32x2 a = __builtin_bit_cast(u32x2, lds_read_tr16(vb + r0 * S::VPITCH + 64 * dt));
-                const u32x2 bq = __builtin_bit_cast(u32x2, lds_read_tr16(vb + (r0 + 2) * S::VPITCH + 64 * dt));
-                return u32x4{a[0], a[1], bq[0], bq[1]};
-            };
-            u32x4 vf[kPvPre + 1];
-#pragma unroll
-            for (int i = 0; i < kPvPre; ++i) vf[i] = vfrag(i);
+            // O^T += V^T . P^T, two 16-row K steps (step s = 16 tt + dt), the
+            // first V^T fragments read above.  The softmax of elements 8..15
+            // runs between the first eight MFMAs.
 #pragma unroll
             for (int s = 0; s < 2 * S::DT; ++s) {
                 if (s + kPvPre < 2 * S::DT) vf[(s + kPvPre) % (kPvPre + 1)] = vfrag(s + kPvPre);
