@@ -35,7 +35,8 @@ namespace {
 
 constexpr int kT = 1024;           // threads per row
 constexpr int kWaves = kT / kWave;
-constexpr int kNV = 8;             // register-resident steps of 4 keys per thread
+constexpr int kNV = 8;             // register-resident steps of 4 keys per thread (rows up to kRegRow)
+constexpr int kNVLong = 16;        // the same for rows up to 2 kRegRow
 constexpr int kTile = kT * 4;      // positions per vector step
 constexpr int kRegRow = kTile * kNV;
 constexpr int kCopies = 4;
@@ -46,7 +47,7 @@ constexpr int kSelCap = 2048;      // k up to this is assembled in LDS
 struct TopkShared {
     uint32_t hist[kBins * kCopies];   // [bin][copy]
     uint32_t wsum[kWaves];            // per-wave totals of a scan
-    uint32_t wtot[kNV][kWaves];
+    uint32_t wtot[kNVLong][kWaves];
     uint32_t cand[kCand];
     int32_t sel[kSelCap];
     uint32_t trash[kWave];            // target of the stores of lanes with nothing to store
@@ -143,12 +144,13 @@ __device__ __forceinline__ uint32_t radix_select(TopkShared& sh, uint32_t& need,
 }
 
 // Two rows per CU: 8 waves per SIMD (64 VGPRs) and under 80 KB of LDS each.
-// IN_REGS: every row of the launch has n <= kRegRow and either n >= 4 or
+// IN_REGS: every row of the launch has n <= NV * kTile and either n >= 4 or
 // n <= k, starts 16-byte aligned and is held in registers (a separate
-// instance, so that the registers of the streaming path do not crowd the 32
-// register-resident keys).  Block x handles row row0 + x.
-template <bool IN_REGS>
-__global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(8)))
+// instance, so that the registers of the streaming path do not crowd the
+// 4 NV register-resident keys; NV = kNVLong holds rows up to 2 kRegRow at
+// one row per CU, 128 VGPRs).  Block x handles row row0 + x.
+template <bool IN_REGS, int NV>
+__global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(NV > kNV ? 4 : 8)))
 void topk_radix_kernel(const float* __restrict__ scores, int32_t* __restrict__ idx,
                        int q_pos0, int t_begin, int row0, int64_t sc_bstride, int64_t sc_rstride,
                        int64_t idx_bstride, int k, const int32_t* __restrict__ flag, int Lq)
@@ -169,6 +171,9 @@ void topk_radix_kernel(const float* __restrict__ scores, int32_t* __restrict__ i
     }
     const float* src = scores + (int64_t)b * sc_bstride + (int64_t)row * sc_rstride;
     constexpr bool in_regs = IN_REGS;
+    static_assert(NV == kNV || (IN_REGS && NV == kNVLong), "register steps");
+    // rows longer than kRegRow take a two-digit lower bound from 2048 samples
+    constexpr bool two_digits = !IN_REGS || NV > kNV;
     const bool vec = IN_REGS || ((uintptr_t)src & 15u) == 0;
     if (tid == 0) {                                // published by the first barrier below
         sh.ncand = 0;
@@ -184,12 +189,12 @@ void topk_radix_kernel(const float* __restrict__ scores, int32_t* __restrict__ i
     //    list, takes its first two digits (22 bits) from 2048 samples.
     const int64_t target = 2 * (int64_t)k;
     const bool sampled = target < n;
-    const int ns = in_regs ? kT : 2 * kT;
+    const int ns = two_digits ? 2 * kT : kT;
     uint32_t sraw[2] = {0u, 0u};                   // sample scores, raw bits
     if (sampled) {
 #pragma unroll
         for (int e = 0; e < 2; ++e)
-            if (e == 0 || !in_regs) sraw[e] = __float_as_uint(src[(int)(((int64_t)(tid + e * kT) * n) / ns)]);
+            if (e == 0 || two_digits) sraw[e] = __float_as_uint(src[(int)(((int64_t)(tid + e * kT) * n) / ns)]);
     }
 
     // keys of positions s0..s0+3 (0 past the row)
@@ -211,18 +216,18 @@ void topk_radix_kernel(const float* __restrict__ scores, int32_t* __restrict__ i
     // one partial group (n % 4 != 0) is read with scalar loads and patched in.
     // All loads are issued before the first conversion, so they are in flight
     // together.
-    uint32_t key[kNV][4];
+    uint32_t key[NV][4];
     if (in_regs) {
         const int last4 = (n - 4) & ~3;            // start of the last whole aligned group
 #pragma unroll
-        for (int v = 0; v < kNV; ++v) {
+        for (int v = 0; v < NV; ++v) {
             if (v * kTile >= n) break;
             const u32x4 x = *(const u32x4*)(src + min(v * kTile + tid * 4, last4));
 #pragma unroll
             for (int e = 0; e < 4; ++e) key[v][e] = x[e];
         }
 #pragma unroll
-        for (int v = 0; v < kNV; ++v) {
+        for (int v = 0; v < NV; ++v) {
             if (v * kTile >= n) break;
             const uint32_t keep = (v * kTile + tid * 4 <= last4) ? ~0u : 0u;
 #pragma unroll
@@ -235,7 +240,7 @@ void topk_radix_kernel(const float* __restrict__ scores, int32_t* __restrict__ i
             for (int e = 0; e < 3; ++e) px[e] = (sp + e < n) ? score_key(src[sp + e]) : 0u;
             const bool own = tid == (sp % kTile) / 4;
 #pragma unroll
-            for (int v = 0; v < kNV; ++v)
+            for (int v = 0; v < NV; ++v)
                 if (v == sp / kTile)
 #pragma unroll
                     for (int e = 0; e < 3; ++e) key[v][e] = own ? px[e] : key[v][e];
@@ -276,7 +281,7 @@ void topk_radix_kernel(const float* __restrict__ scores, int32_t* __restrict__ i
     auto for_each_step = [&](auto&& fn) {
         if (in_regs) {
 #pragma unroll
-            for (int v = 0; v < kNV; ++v)
+            for (int v = 0; v < NV; ++v)
                 if (v * kTile < n) fn(v * kTile + tid * 4, key[v]);
         } else {
             stream_steps(fn);
@@ -292,18 +297,18 @@ void topk_radix_kernel(const float* __restrict__ scores, int32_t* __restrict__ i
         for (int e = 0; e < 2; ++e) sample[e] = score_key(__uint_as_float(sraw[e]));
         // the largest sample: the top of the candidate list's histogram range
         // (published by the barriers below)
-        uint32_t smax = in_regs ? sample[0] : max(sample[0], sample[1]);
+        uint32_t smax = two_digits ? max(sample[0], sample[1]) : sample[0];
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) smax = max(smax, (uint32_t)__shfl_xor((int)smax, o, kWave));
         if (lane == 0) atomicMax(&sh.cmax, smax);
         auto each_sample = [&](auto&& fn) {
             fn(sample[0]);
-            if (!in_regs) fn(sample[1]);
+            if (two_digits) fn(sample[1]);
         };
         radix_step<11>(sh, 21, 0u, 0u, j, each_sample);
         const uint32_t b1 = sh.bin;
         lbound = b1 << 21;
-        if (!in_regs) {
+        if (two_digits) {
             const uint32_t above = sh.above;
             __syncthreads();                       // sh.bin / sh.above are rewritten below
             radix_step<11>(sh, 10, b1 << 21, 0x7FFu << 21, j - above, each_sample);
@@ -337,14 +342,14 @@ void topk_radix_kernel(const float* __restrict__ scores, int32_t* __restrict__ i
         uint32_t c = 0, rmax = 0;
         if (sampled) {
 #pragma unroll
-            for (int v = 0; v < kNV; ++v)
+            for (int v = 0; v < NV; ++v)
                 if (v * kTile < n)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) c += key[v][e] >= lb1;
         } else {
             // no samples: the list's range ends at the row's largest key
 #pragma unroll
-            for (int v = 0; v < kNV; ++v)
+            for (int v = 0; v < NV; ++v)
                 if (v * kTile < n)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
@@ -360,7 +365,7 @@ void topk_radix_kernel(const float* __restrict__ scores, int32_t* __restrict__ i
         uint32_t* trash = &sh.trash[lane];
         auto store = [&](bool guard) {
 #pragma unroll
-            for (int v = 0; v < kNV; ++v)
+            for (int v = 0; v < NV; ++v)
                 if (v * kTile < n)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
@@ -506,17 +511,22 @@ void topk_radix_kernel(const float* __restrict__ scores, int32_t* __restrict__ i
         // All steps at once.  Usually every key equal to T is taken (eqT ==
         // need) and T >= 1, so the selection is simply key >= T (positions
         // past the row hold key 0).  Per lane, the counts of selected keys of
-        // the 8 steps (at most 4 each) are packed three to a word in 10-bit
-        // fields, so three wave scans give every in-wave prefix (at most 256)
-        // and the wave totals; the (step, wave) totals in ascending-s order
-        // (step-major), two per lane, get one exclusive scan that every wave
-        // evaluates, and each wave reads its own prefixes with uniform lane
-        // reads.  Lanes write unselected positions to their own trash word.
-        static_assert(kNV == 8 && kNV * kWaves == 2 * kWave, "three packed scans; two (step, wave) totals per lane");
+        // the NV steps (at most 4 each) are packed three to a word in 10-bit
+        // fields, so NW3 wave scans give every in-wave prefix (at most 256)
+        // and the wave totals; the NV * kWaves (step, wave) totals in
+        // ascending-s order (step-major), EPL consecutive ones per lane, get
+        // one exclusive scan that every wave evaluates, and each wave reads
+        // its own prefixes with uniform lane reads.  Lanes write unselected
+        // positions to their own trash word.
+        constexpr int NW3 = (NV + 2) / 3;
+        constexpr int EPL = NV * kWaves / kWave;   // (step, wave) totals per lane
+        static_assert(EPL * kWave == NV * kWaves && kWaves % EPL == 0, "whole totals per lane, a wave's own slot");
         if (eqT == need && T > 0u && to_lds) {
-            uint32_t cw[3] = {0u, 0u, 0u};
+            uint32_t cw[NW3];
 #pragma unroll
-            for (int v = 0; v < kNV; ++v) {
+            for (int i = 0; i < NW3; ++i) cw[i] = 0u;
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
                 uint32_t c = 0;
                 if (v * kTile < n) {
 #pragma unroll
@@ -524,27 +534,34 @@ void topk_radix_kernel(const float* __restrict__ scores, int32_t* __restrict__ i
                 }
                 cw[v / 3] |= c << (10 * (v % 3));
             }
-            uint32_t ci[3];
+            uint32_t ci[NW3];
 #pragma unroll
-            for (int i = 0; i < 3; ++i) ci[i] = wave_incl_scan(cw[i], lane);
-            uint32_t* w3 = &sh.wtot[0][0];         // [wave][3] wave totals
+            for (int i = 0; i < NW3; ++i) ci[i] = wave_incl_scan(cw[i], lane);
+            uint32_t* w3 = &sh.wtot[0][0];         // [wave][NW3] wave totals
+            static_assert(kWaves * NW3 <= kNVLong * kWaves, "room for the packed wave totals");
             if (lane == 63) {
 #pragma unroll
-                for (int i = 0; i < 3; ++i) w3[wave * 3 + i] = ci[i];
+                for (int i = 0; i < NW3; ++i) w3[wave * NW3 + i] = ci[i];
             }
             __syncthreads();
-            // entries 2 lane, 2 lane + 1: step lane / 8, waves 2 (lane % 8) and 2 (lane % 8) + 1
-            const int sv = lane >> 3, sw = 2 * (lane & 7);
-            const uint32_t x0 = (w3[sw * 3 + sv / 3] >> (10 * (sv % 3))) & 0x3FFu;
-            const uint32_t x1 = (w3[(sw + 1) * 3 + sv / 3] >> (10 * (sv % 3))) & 0x3FFu;
-            const uint32_t e0 = wave_incl_scan(x0 + x1, lane) - (x0 + x1);   // before entry 2*lane
-            const uint32_t ew = (wave & 1) ? e0 + x0 : e0;                   // before entry 2*lane + (wave & 1)
+            // entries EPL lane + i: step (EPL lane + i) / kWaves, wave (EPL lane + i) % kWaves
+            uint32_t x[EPL], sum = 0;
+#pragma unroll
+            for (int i = 0; i < EPL; ++i) {
+                const int ent = EPL * lane + i, sv = ent / kWaves, sw = ent % kWaves;
+                x[i] = (w3[sw * NW3 + sv / 3] >> (10 * (sv % 3))) & 0x3FFu;
+                sum += x[i];
+            }
+            // before entry EPL lane + (wave % EPL): this wave's slot in each lane
+            uint32_t ew = wave_incl_scan(sum, lane) - sum;
+#pragma unroll
+            for (int i = 0; i + 1 < EPL; ++i) ew += (i < wave % EPL) ? x[i] : 0u;
             uint32_t* trash = &sh.trash[lane];
 #pragma unroll
-            for (int v = 0; v < kNV; ++v) {
+            for (int v = 0; v < NV; ++v) {
                 if (v * kTile >= n) break;         // workgroup-uniform
                 const int f = 10 * (v % 3);
-                uint32_t pos = __builtin_amdgcn_readlane(ew, (v * kWaves + wave) >> 1) +
+                uint32_t pos = __builtin_amdgcn_readlane(ew, (v * kWaves + wave) / EPL) +
                                ((ci[v / 3] >> f) & 0x3FFu) - ((cw[v / 3] >> f) & 0x3FFu);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -560,19 +577,25 @@ void topk_radix_kernel(const float* __restrict__ scores, int32_t* __restrict__ i
             // per-step scans are recomputed after the barrier rather than
             // kept.
 #pragma unroll
-            for (int v = 0; v < kNV; ++v) {
+            for (int v = 0; v < NV; ++v) {
                 const uint32_t incl = (v * kTile < n) ? wave_incl_scan(counts(v * kTile + tid * 4, key[v]), lane) : 0u;
                 if (lane == 63) sh.wtot[v][wave] = incl;
             }
             __syncthreads();
             const uint32_t* flat = &sh.wtot[0][0];
-            const uint32_t x0 = flat[2 * lane], x1 = flat[2 * lane + 1];
-            const uint32_t e0 = wave_incl_scan(x0 + x1, lane) - (x0 + x1);   // before entry 2*lane
-            const uint32_t ew = (wave & 1) ? e0 + x0 : e0;                   // before entry 2*lane + (wave & 1)
+            uint32_t x[EPL], sum = 0;
 #pragma unroll
-            for (int v = 0; v < kNV; ++v) {
+            for (int i = 0; i < EPL; ++i) {
+                x[i] = flat[EPL * lane + i];
+                sum += x[i];
+            }
+            uint32_t ew = wave_incl_scan(sum, lane) - sum;    // before entry EPL lane + (wave % EPL)
+#pragma unroll
+            for (int i = 0; i + 1 < EPL; ++i) ew += (i < wave % EPL) ? x[i] : 0u;
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
                 if (v * kTile >= n) break;         // workgroup-uniform
-                const uint32_t base = __builtin_amdgcn_readlane(ew, (v * kWaves + wave) >> 1);
+                const uint32_t base = __builtin_amdgcn_readlane(ew, (v * kWaves + wave) / EPL);
                 const uint32_t pk = counts(v * kTile + tid * 4, key[v]);
                 const uint32_t pre = base + wave_incl_scan(pk, lane) - pk;
                 place(v * kTile + tid * 4, key[v], pre >> 16, pre & 0xFFFFu);
@@ -612,7 +635,8 @@ hipError_t launch_topk(const TopkLaunch& a, hipStream_t s)
     // Row r (t = t_begin + r) has n = q_pos0 + t_begin + r + 1 candidates, so
     // with aligned rows the register-resident instance takes the rows with
     // n <= kRegRow and either n >= 4 or n <= k (those only write 0..n-1), a
-    // contiguous range [r_lo, r_hi); the others stream.
+    // contiguous range [r_lo, r_hi), and its long-row instance the rows with
+    // kRegRow < n <= 2 kRegRow, [r_hi, r_2); the others stream.
     const bool aligned = ((uintptr_t)a.scores & 15u) == 0 && a.sc_bstride % 4 == 0 && a.sc_rstride % 4 == 0;
     const int64_t n0 = (int64_t)a.q_pos0 + a.t_begin + 1;                 // n of row 0
     const int64_t n_lo = a.k >= 3 ? 1 : 4;                                 // smallest n the instance takes
@@ -623,9 +647,11 @@ hipError_t launch_topk(const TopkLaunch& a, hipStream_t s)
             hipLaunchKernelGGL(kernel, dim3(r1 - r0, a.B), dim3(kT), 0, s, a.scores, a.idx, a.q_pos0, a.t_begin, r0,
                                a.sc_bstride, a.sc_rstride, a.idx_bstride, a.k, a.flag, a.Lq);
     };
-    rows(topk_radix_kernel<false>, 0, r_lo);
-    rows(topk_radix_kernel<true>, r_lo, r_hi);
-    rows(topk_radix_kernel<false>, r_hi, a.t_count);
+    const int r_2 = aligned ? (int)std::max<int64_t>(std::min<int64_t>(2 * kRegRow - n0 + 1, a.t_count), r_hi) : a.t_count;
+    rows(topk_radix_kernel<false, kNV>, 0, r_lo);
+    rows(topk_radix_kernel<true, kNV>, r_lo, r_hi);
+    rows(topk_radix_kernel<true, kNVLong>, r_hi, r_2);
+    rows(topk_radix_kernel<false, kNV>, r_2, a.t_count);
     return hipGetLastError();
 }
 

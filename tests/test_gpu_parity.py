@@ -350,13 +350,30 @@ def test_topk_routes_bit_exact(dsa, n):
     _topk_exact(dsa, s.to(dev).contiguous(), 2048, q_pos0=n - 1)
 
 
+@pytest.mark.parametrize("n0", [32769, 40001, 65533])
+def test_topk_long_register_rows(dsa, n0):
+    """Rows of 32769 to 65536 candidates held in registers at one row per CU
+    (16 steps of 4 keys per thread): rows n0, n0 + 1, n0 + 2 of an aligned
+    65536-wide score array (partial last groups of 4 and partial last steps),
+    every score pattern, exactly against the oracle."""
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device="cpu").manual_seed(n0)
+    Lk = 65536
+    pats = ["normal", "ties", "const", "cluster_outlier", "ulp_cluster", "sample_trap"]
+    s = torch.full((len(pats), 3, Lk), -7.0)
+    for i, p in enumerate(pats):
+        for r in range(3):
+            s[i, r, : n0 + r] = _topk_pattern_row(p, n0 + r, g)
+    _topk_exact(dsa, s.to(dev).contiguous(), 2048, q_pos0=n0 - 1)
+
+
 @pytest.mark.parametrize("k", [2047, 3000, 4096])
 def test_topk_k_beyond_lds_assembly(dsa, k):
     """k around and above the 2048 positions assembled in LDS (written to
     memory directly past that), on register-resident and long rows."""
     dev = torch.device("cuda:0")
     g = torch.Generator(device="cpu").manual_seed(k)
-    for n in (20000, 70001):
+    for n in (20000, 50000, 70001):
         s = torch.stack([_topk_pattern_row(p, n, g) for p in ("normal", "ties", "cluster_outlier")])[:, None, :]
         _topk_exact(dsa, s.to(dev).contiguous(), k, q_pos0=n - 1)
 
