@@ -18,7 +18,8 @@
 // the threshold bin; otherwise the radix select runs over the whole row.  Rows
 // of up to 32768 scores are read from memory once (each thread keeps the keys
 // of positions 4096 v + 4 tid + e in registers, in a kernel instance of its
-// own); longer rows are read again in each pass.  Selected positions are
+// own), and so are rows of up to 65536 (twice the registers, one row per CU);
+// longer rows are read again in each pass.  Selected positions are
 // assembled in LDS and written out in one coalesced pass.  The histogram is
 // kept in four copies (lane % 4 picks one) so that lanes hitting the same bin
 // in one atomic instruction mostly hit different LDS words; its bins are
@@ -143,7 +144,7 @@ __device__ __forceinline__ uint32_t radix_select(TopkShared& sh, uint32_t& need,
     return prefix;
 }
 
-// Two rows per CU: 8 waves per SIMD (64 VGPRs) and under 80 KB of LDS each.
+// Two rows per CU (NV = kNV): 8 waves per SIMD (64 VGPRs) and under 80 KB of LDS each.
 // IN_REGS: every row of the launch has n <= NV * kTile and either n >= 4 or
 // n <= k, starts 16-byte aligned and is held in registers (a separate
 // instance, so that the registers of the streaming path do not crowd the
