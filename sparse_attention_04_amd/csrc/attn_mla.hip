@@ -67,10 +67,22 @@ void sparse_attn_mla_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
     const int col = lane & 31, hi = lane >> 5;
     const int h = wave * 32 + col;
 
+    // The query's loads, then every load of the index list before any of
+    // them is used (one memory round trip instead of one per entry); the
+    // list's staging then waits on both.  Entries past k read entry k - 1
+    // (k >= 1) and are dropped.
     const uint16_t* qrow = q + (((int64_t)b * Lq + t) * H + h) * 576;
     v8bf qf[S::QC];
 #pragma unroll
     for (int c = 0; c < S::QC; ++c) qf[c] = as_bf8(*(const u32x4*)(qrow + c * 16 + hi * 8));
+    __builtin_amdgcn_sched_barrier(0);
+
+    const int32_t* irow = idx + (int64_t)b * idx_bstride + (int64_t)row * k;
+    constexpr int SPL = S::KMAX / (64 * NW);                 // list entries per lane
+    int sv[SPL];
+#pragma unroll
+    for (int j = 0; j < SPL; ++j) sv[j] = irow[min(tid + j * 64 * NW, k - 1)];
+    __builtin_amdgcn_sched_barrier(0);
 
     v16f o[S::DT];
 #pragma unroll
@@ -78,13 +90,14 @@ void sparse_attn_mla_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
 #pragma unroll
         for (int v = 0; v < 16; ++v) o[i][v] = 0.f;
 
-    const int32_t* irow = idx + (int64_t)b * idx_bstride + (int64_t)row * k;
     const uint16_t* kvb = kv + (int64_t)b * Lk * 576;
     // Stage the index list; entries that cannot be read become -1.  Chunks
     // past the last valid entry (a short row's -1 padding) are not visited.
     int last = -1;
-    for (int i = tid; i < S::KMAX; i += 64 * NW) {
-        const int sidx = (i < k) ? irow[i] : -1;
+#pragma unroll
+    for (int j = 0; j < SPL; ++j) {
+        const int i = tid + j * 64 * NW;
+        const int sidx = (i < k) ? sv[j] : -1;
         const bool ok = sidx >= 0 && sidx < Lk;
         sel[i] = ok ? sidx : -1;
         last = ok ? i : last;
@@ -302,15 +315,23 @@ void sparse_attn_mla_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
             }
         if (hi == 0) part_lse[pr * H + h] = lse_row;
     } else {
+        // Element 4g + e of o[dt] is dim dt*32 + 8g + 4hi + e of head h.  One
+        // swap of the half-waves gives lane hi = 0 all eight dims of group
+        // 2p and lane hi = 1 those of group 2p + 1, so each lane stores 16
+        // bytes and a head's two lanes 32 contiguous bytes.
         uint16_t* orow = out + (((int64_t)b * Lq + t) * H + h) * 512;
 #pragma unroll
         for (int dt = 0; dt < S::DT; ++dt)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int d0 = dt * 32 + 8 * g + 4 * hi;
-                const uint32_t w0 = pack_bf16x2(o[dt][4 * g] * inv, o[dt][4 * g + 1] * inv);
-                const uint32_t w1 = pack_bf16x2(o[dt][4 * g + 2] * inv, o[dt][4 * g + 3] * inv);
-                *(u32x2*)(orow + d0) = u32x2{w0, w1};
+            for (int p = 0; p < 2; ++p) {
+                const int ga = 2 * p, gb = 2 * p + 1;
+                const uint32_t a0 = pack_bf16x2(o[dt][4 * ga] * inv, o[dt][4 * ga + 1] * inv);
+                const uint32_t a1 = pack_bf16x2(o[dt][4 * ga + 2] * inv, o[dt][4 * ga + 3] * inv);
+                const uint32_t b0 = pack_bf16x2(o[dt][4 * gb] * inv, o[dt][4 * gb + 1] * inv);
+                const uint32_t b1 = pack_bf16x2(o[dt][4 * gb + 2] * inv, o[dt][4 * gb + 3] * inv);
+                const auto s0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
+                const auto s1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
+                *(u32x4*)(orow + dt * 32 + 16 * p + 8 * hi) = u32x4{s0[0], s1[0], s0[1], s1[1]};
             }
         if (lse != nullptr && hi == 0)
             lse[((int64_t)b * Lq + t) * H + h] = lse_row;

@@ -246,12 +246,22 @@ void sparse_attn_bf16_w32_kernel(const uint16_t* __restrict__ q, const void* __r
     const uint8_t* kv8b = (const uint8_t*)kv + (F8 ? (int64_t)b * Lk * kF8Row : 0);
     // Stage the index list; entries that cannot be read become -1.  Chunks
     // past the last valid entry (a short row's -1 padding) are not visited.
+    // Every load is issued before any is used (one memory round trip);
+    // entries past k read entry k - 1 (k >= 1) and are dropped.
     int last = -1;
-    for (int i = tid; i < S::KMAX; i += 64 * NW) {
-        const int sidx = (i < k) ? irow[i] : -1;
-        const bool ok = sidx >= 0 && sidx < Lk;
-        sel[i] = ok ? sidx : -1;
-        last = ok ? i : last;
+    {
+        constexpr int EPT = S::KMAX / (64 * NW);     // list entries per thread
+        static_assert(S::KMAX % (64 * NW) == 0, "whole list entries per thread");
+        int32_t ent[EPT];
+#pragma unroll
+        for (int m = 0; m < EPT; ++m) ent[m] = irow[min(tid + 64 * NW * m, k - 1)];
+#pragma unroll
+        for (int m = 0; m < EPT; ++m) {
+            const int i = tid + 64 * NW * m;
+            const bool ok = i < k && ent[m] >= 0 && ent[m] < Lk;
+            sel[i] = ok ? ent[m] : -1;
+            last = ok ? i : last;
+        }
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) last = max(last, __shfl_xor(last, o, kWave));
@@ -561,12 +571,23 @@ void sparse_attn_bf16_w16_kernel(const uint16_t* __restrict__ q, const uint16_t*
     for (int c = 0; c < D / 32; ++c) qf[c] = as_bf8(*(const u32x4*)(qrow + 32 * c + 8 * g));
 
     const int32_t* irow = idx + (int64_t)b * idx_bstride + (int64_t)row * k;
+    // Every load is issued before any is used (one memory round trip);
+    // entries past k read entry k - 1 (k >= 1) and are dropped.
     int last = -1;
-    for (int i = tid; i < KMAX; i += 64 * NW) {
-        const int sidx = (i < k) ? irow[i] : -1;
-        const bool ok = sidx >= 0 && sidx < Lk;
-        sel[i] = ok ? sidx : -1;
-        last = ok ? i : last;
+    {
+        constexpr int EPT = (KMAX + 64 * NW - 1) / (64 * NW);   // list entries per thread
+        int32_t ent[EPT];
+#pragma unroll
+        for (int m = 0; m < EPT; ++m) ent[m] = irow[min(tid + 64 * NW * m, k - 1)];
+#pragma unroll
+        for (int m = 0; m < EPT; ++m) {
+            const int i = tid + 64 * NW * m;
+            if (i < KMAX) {
+                const bool ok = i < k && ent[m] >= 0 && ent[m] < Lk;
+                sel[i] = ok ? ent[m] : -1;
+                last = ok ? i : last;
+            }
+        }
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) last = max(last, __shfl_xor(last, o, kWave));
