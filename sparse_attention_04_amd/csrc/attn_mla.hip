@@ -317,24 +317,41 @@ void sparse_attn_mla_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
     } else {
         // Element 4g + e of o[dt] is dim dt*32 + 8g + 4hi + e of head h.  One
         // swap of the half-waves gives lane hi = 0 all eight dims of group
-        // 2p and lane hi = 1 those of group 2p + 1, so each lane stores 16
-        // bytes and a head's two lanes 32 contiguous bytes.
-        uint16_t* orow = out + (((int64_t)b * Lq + t) * H + h) * 512;
+        // 2p and lane hi = 1 those of group 2p + 1 (16 bytes each).  The
+        // wave's 32 rows then go through LDS (the ring is free: every wave
+        // has passed the last barrier) in two halves of the value dims, so
+        // each store instruction writes two heads' 512-byte runs.  Piece j
+        // of staged row r sits at slot j ^ r (conflict-free row reads).
+        static_assert(NBUF * S::BUF_BYTES >= NW * 16384, "staging fits the ring");
+        uint8_t* stage = &ring[0][0] + wave * 16384;
+        uint16_t* owave = (uint16_t*)wave_uniform_ptr(out + (((int64_t)b * Lq + t) * H + wave * 32) * 512);
 #pragma unroll
-        for (int dt = 0; dt < S::DT; ++dt)
+        for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
-            for (int p = 0; p < 2; ++p) {
-                const int ga = 2 * p, gb = 2 * p + 1;
-                const uint32_t a0 = pack_bf16x2(o[dt][4 * ga] * inv, o[dt][4 * ga + 1] * inv);
-                const uint32_t a1 = pack_bf16x2(o[dt][4 * ga + 2] * inv, o[dt][4 * ga + 3] * inv);
-                const uint32_t b0 = pack_bf16x2(o[dt][4 * gb] * inv, o[dt][4 * gb + 1] * inv);
-                const uint32_t b1 = pack_bf16x2(o[dt][4 * gb + 2] * inv, o[dt][4 * gb + 3] * inv);
-                const auto s0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
-                const auto s1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
-                *(u32x4*)(orow + dt * 32 + 16 * p + 8 * hi) = u32x4{s0[0], s1[0], s0[1], s1[1]};
+            for (int d8 = 0; d8 < 8; ++d8) {
+                const int dt = 8 * hh + d8;
+#pragma unroll
+                for (int p = 0; p < 2; ++p) {
+                    const int ga = 2 * p, gb = 2 * p + 1;
+                    const uint32_t a0 = pack_bf16x2(o[dt][4 * ga] * inv, o[dt][4 * ga + 1] * inv);
+                    const uint32_t a1 = pack_bf16x2(o[dt][4 * ga + 2] * inv, o[dt][4 * ga + 3] * inv);
+                    const uint32_t b0 = pack_bf16x2(o[dt][4 * gb] * inv, o[dt][4 * gb + 1] * inv);
+                    const uint32_t b1 = pack_bf16x2(o[dt][4 * gb + 2] * inv, o[dt][4 * gb + 3] * inv);
+                    const auto s0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
+                    const auto s1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
+                    const int piece = 4 * d8 + 2 * p + hi;
+                    *(u32x4*)(stage + col * 512 + ((piece ^ col) << 4)) = u32x4{s0[0], s1[0], s0[1], s1[1]};
+                }
             }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int r = 2 * i + hi;
+                const u32x4 v = *(const u32x4*)(stage + r * 512 + ((col ^ r) << 4));
+                *(u32x4*)(owave + (int64_t)r * 512 + hh * 256 + col * 8) = v;
+            }
+        }
         if (lse != nullptr && hi == 0)
-            lse[((int64_t)b * Lq + t) * H + h] = lse_row;
+            ((float*)wave_uniform_ptr(lse + ((int64_t)b * Lq + t) * H + wave * 32))[col] = lse_row;
     }
 }
 
