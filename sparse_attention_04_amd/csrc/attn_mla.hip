@@ -209,7 +209,10 @@ void sparse_attn_mla_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
                 u32x4 kf[kPre + 1];
 #pragma unroll
                 for (int i = 0; i < kPre; ++i) kf[i] = kfrag(i);
-#pragma unroll
+                // fully unrolled for every wave count: with one wave (36 copies
+                // per chunk) the default heuristic kept the loop, and the query
+                // fragments, indexed at run time, went to scratch memory
+#pragma clang loop unroll(full)
                 for (int c2 = 0; c2 < S::QC; ++c2) {
                     if (c2 + kPre < S::QC) kf[(c2 + kPre) % (kPre + 1)] = kfrag(c2 + kPre);
                     sacc = mfma_bf16_32x32x16(as_bf8(kf[c2 % (kPre + 1)]), qf[c2], sacc);

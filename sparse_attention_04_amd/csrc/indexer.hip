@@ -381,14 +381,15 @@ void indexer_fp8_kernel(const uint8_t* __restrict__ q8, const float* __restrict_
 }
 
 // FP8 kernel for few query rows per sequence (decode): one workgroup per
-// (query row, range of kRowKeys keys).  The MFMA's N dimension carries 16
+// (query row, range of row_keys keys).  The MFMA's N dimension carries 16
 // heads instead of 16 queries, so no work is spent on absent query rows:
 // per 16-key tile a wave runs four v_mfma_f32_16x16x128_f8f6f4 (64 heads),
 // folds ReLU and the head weights into four fp32 partial sums per lane, and
 // sums them over the 16 lanes that hold the 16 heads of a key.  Keys are read
 // straight from memory into the A operand, kTileAhead tiles ahead; the four
 // waves take alternate tiles and need no workgroup synchronisation.
-constexpr int kRowKeys = 2048;     // keys per workgroup
+constexpr int kRowKeysMax = 8192;  // keys per workgroup at most (the LDS score row)
+constexpr int kRowKeysMin = 2048;
 constexpr int kTileAhead = 8;      // key tiles in flight per wave
 
 // Sum over each 16-lane row of the wave (every lane of the row gets it): DPP
@@ -407,15 +408,16 @@ void indexer_fp8_row_kernel(const uint8_t* __restrict__ q8, const float* __restr
                             const uint8_t* __restrict__ k8, const float* __restrict__ k_scale,
                             const float* __restrict__ w, float* __restrict__ scores,
                             int Lq, int Lk, int q_pos0, int t_begin,
-                            int64_t sc_bstride, int64_t sc_rstride, int write_masked, int skip_upto_k)
+                            int64_t sc_bstride, int64_t sc_rstride, int write_masked, int skip_upto_k,
+                            int row_keys)
 {
     const int t = t_begin + blockIdx.x;
     const int b = blockIdx.y;
     const int tpos = q_pos0 + t;
     if (skip_upto_k > 0 && tpos + 1 <= skip_upto_k)
         return;
-    const int s_begin = blockIdx.z * kRowKeys;
-    const int s_stop = min(s_begin + kRowKeys, Lk);           // this workgroup's key range
+    const int s_begin = blockIdx.z * row_keys;
+    const int s_stop = min(s_begin + row_keys, Lk);           // this workgroup's key range
     const int s_end = min(s_stop, tpos + 1);                  // keys that get a score
     float* dst = scores + (int64_t)b * sc_bstride + (int64_t)(t - t_begin) * sc_rstride;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -446,7 +448,7 @@ void indexer_fp8_row_kernel(const uint8_t* __restrict__ q8, const float* __restr
     // (past the last one: the last one again) and the scores go to LDS, so
     // the number of memory instructions per step is fixed and the compiler's
     // waits keep kTileAhead tiles in flight; the row is stored at the end.
-    __shared__ __attribute__((aligned(16))) float sc_lds[kRowKeys];
+    __shared__ __attribute__((aligned(16))) float sc_lds[kRowKeysMax];
     struct Tile {
         v8i a;
         float ks[4];
@@ -548,12 +550,19 @@ hipError_t launch_indexer(const IndexerLaunch& a, hipStream_t s)
     // whole-problem call gives it, whatever the size of its tile.
     if (a.fp8 && a.Lq < kQB / 2) {
         // few query rows per sequence: split the keys instead of blocking queries
+        // Longer key ranges per workgroup while at least 512 workgroups (two
+        // per CU) remain: each wave's prefetch ramp and drain are paid once
+        // per range, and the launch fits in one round (64 x 65536 keys: 8192
+        // keys per workgroup, 14% faster than 2048).  The partition does not
+        // change any score.
         const int last = a.write_masked ? a.Lk : min(a.Lk, a.q_pos0 + a.t_begin + a.t_count);
-        const int nz = (last + kRowKeys - 1) / kRowKeys;
+        int rk = kRowKeysMax;
+        while (rk > kRowKeysMin && (int64_t)a.t_count * a.B * ((last + rk - 1) / rk) < 512) rk /= 2;
+        const int nz = (last + rk - 1) / rk;
         hipLaunchKernelGGL(indexer_fp8_row_kernel, dim3(a.t_count, a.B, nz), dim3(kThreads), 0, s,
                            (const uint8_t*)a.q, a.q_scale, (const uint8_t*)a.k, a.k_scale, a.w,
                            a.scores, a.Lq, a.Lk, a.q_pos0, a.t_begin,
-                           a.sc_bstride, a.sc_rstride, (int)a.write_masked, a.skip_upto_k);
+                           a.sc_bstride, a.sc_rstride, (int)a.write_masked, a.skip_upto_k, rk);
     } else if (a.fp8) {
         // With fewer than 1024 row blocks the keys are split as well, so that
         // about 1024 workgroups run and the longest block's chain of key

@@ -176,13 +176,25 @@ def test_head_dim_64(dsa):
 @pytest.mark.parametrize("where", ["decode", "chunk_edge", "short_rows"])
 def test_few_query_rows_split_keys(dsa, Lq, where):
     """Fewer than 8 query rows per sequence: the FP8 indexer splits each row's
-    keys over workgroups of 2048.  Lk = 5003 leaves a ragged last chunk (not a
+    keys over workgroups (of 2048 keys at these sizes).  Lk = 5003 leaves a ragged last chunk (not a
     multiple of 16); rows that end before Lk - 1 leave whole chunks masked."""
     Lk = 5003
     q_pos0 = {"decode": Lk - Lq, "chunk_edge": 4094, "short_rows": 2045}[where]
     cfg = CONFIGS["decode_B64_ctx65536"].with_(name=f"rows{Lq}_{where}", B=2, Lq=Lq, Lk=Lk, q_pos0=q_pos0,
                                                n_heads=16)
     _run_case(dsa, cfg, {b: np.arange(cfg.Lq) for b in range(cfg.B)}, seed=Lq)
+
+
+@pytest.mark.parametrize("Lk", [40003, 70001])
+def test_few_query_rows_long_key_ranges(dsa, Lk):
+    """64 query rows in sequences of 4: the FP8 indexer gives each
+    workgroup 4096 (Lk = 40003) or 8192 (Lk = 70001) keys, the longest range
+    that still leaves 512 workgroups, and the last range of every row is
+    ragged.  Scores, top-k and attention of two sequences against the
+    oracle."""
+    cfg = CONFIGS["decode_B64_ctx65536"].with_(name=f"rows4_Lk{Lk}", B=16, Lq=4, Lk=Lk, q_pos0=Lk - 4,
+                                               n_heads=16)
+    _run_case(dsa, cfg, {b: np.arange(cfg.Lq) for b in (0, 15)}, seed=Lk)
 
 
 # ------------------------------------------------------------------ full-size workloads, sampled rows
