@@ -16,8 +16,11 @@ OBJ_DIR = os.path.join(HERE, "_build")
 ARCH = "gfx950"
 # Per-source extra flags.  The indexer's MFMA results are consumed by vector
 # fmas at once, so its MFMAs are built in the VGPR-destination form (an AGPR
-# destination would need a copy-out instruction per element); the attention
-# kernel keeps its accumulators in AGPRs.
+# destination would need a copy-out instruction per element).  So are the
+# 64/128-wide attention kernel's: its accumulators fit the VGPRs, and in AGPRs
+# the compiler moved two O tiles out and back around every chunk's Q.K (4.5%
+# of the kernel).  The 576/512 attention kernels keep their 256 accumulators
+# in AGPRs.
 SOURCES = [
     ("dsa_capi.cpp", []),
     ("indexer.hip", ["-mllvm", "-amdgpu-mfma-vgpr-form"]),
@@ -25,7 +28,7 @@ SOURCES = [
     ("select.hip", []),
     ("sparse_attn.hip", []),
     ("attn_mla.hip", []),
-    ("attn_mqa.hip", []),
+    ("attn_mqa.hip", ["-mllvm", "-amdgpu-mfma-vgpr-form"]),
     ("inputs.hip", []),
     ("kl.hip", []),
     ("attn_bwd.hip", []),
