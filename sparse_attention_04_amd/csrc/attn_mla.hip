@@ -10,7 +10,8 @@
 // layout of attn_layout.h (value parts at a 1040-byte pitch, tails packed 8
 // rows per 1 KB, S^T row slot m holding chunk row slot_row(m)):
 //  - S^T[32 rows x 32 heads] = K_chunk . Q^T with the query operand (36 steps
-//    of 32 heads x 16 dims) in registers for the whole row;
+//    of 32 heads x 16 dims) in registers for the whole row, accumulated in
+//    VGPRs (inline MFMAs) while O^T fills the 256 AGPRs;
 //  - softmax in fp32 (exp2 domain) against a per-head reference maximum m
 //    fixed at the first chunk holding a valid row, so O is never rescaled; a
 //    logit more than 64 (log2 units) above m makes the workgroup recompute
@@ -197,8 +198,6 @@ void sparse_attn_mla_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
             // j of chunk it+AHEAD is issued after MFMA min(36 j / SPW + 2, 35)
             // (two MFMAs in, so the LDS reads of its sources have landed).
             v16f sacc;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) sacc[v] = 0.f;
             {
                 const uint8_t* vrow = cur + krow_i * S::VPITCH + hi * 16;
                 const uint8_t* trw = cur + S::VBYTES + krow_i * (S::TP * 16);
@@ -215,7 +214,19 @@ void sparse_attn_mla_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
 #pragma clang loop unroll(full)
                 for (int c2 = 0; c2 < S::QC; ++c2) {
                     if (c2 + kPre < S::QC) kf[(c2 + kPre) % (kPre + 1)] = kfrag(c2 + kPre);
-                    sacc = mfma_bf16_32x32x16(as_bf8(kf[c2 % (kPre + 1)]), qf[c2], sacc);
+                    // S^T accumulates in VGPRs: the 256 AGPRs hold O^T, and
+                    // the compiler (one MFMA register form per function) would
+                    // otherwise move an O^T tile out and back every chunk.  The
+                    // chain accumulates in place (no wait states needed); its
+                    // operands come from LDS and global loads only, which the
+                    // compiler's waits cover; the wait states before the
+                    // first VALU read of S^T follow the chain.
+                    if (c2 == 0)
+                        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0"
+                                     : "=&v"(sacc) : "v"(as_bf8(kf[0])), "v"(qf[0]));
+                    else
+                        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                                     : "+v"(sacc) : "v"(as_bf8(kf[c2 % (kPre + 1)])), "v"(qf[c2]));
 #pragma unroll
                     for (int j = 0; j < SPW; ++j)
                         if (c2 == min((j * S::QC) / SPW + 2, S::QC - 1) && copies) issue_copy(cs, c + AHEAD, j);
@@ -242,10 +253,13 @@ void sparse_attn_mla_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
             __builtin_amdgcn_sched_barrier(0);
 
             if (vmask == 0u) continue;                       // nothing selected here (uniform)
-            // S^T out of the accumulator registers once, into plain registers
-            // (the empty asm pins the copy; left to itself the compiler read
-            // the accumulators afresh for the mask, the maximum and the
-            // softmax, about 47 more moves per chunk, 5% of the kernel)
+            // 20 wait states between the last S^T MFMA (8 passes) and any
+            // VALU access to its result registers, more than the hardware's
+            // required count for an 8-pass MFMA result
+            asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(sacc));
+            // S^T pinned in plain registers for the mask, the maximum and the
+            // softmax (with S^T in AGPRs the compiler had read them afresh for
+            // each, about 47 more moves per chunk)
             float z[16];
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
