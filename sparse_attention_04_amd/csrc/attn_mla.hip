@@ -31,6 +31,8 @@
 //    checks its own logits against m;
 //  - the second half of the softmax (rows of the second 16-key step) runs
 //    between the MFMAs of the first P.V step.
+#include <type_traits>
+
 #include "attn_layout.h"
 #include "hw.h"
 #include "launch.h"
@@ -198,7 +200,9 @@ void sparse_attn_mla_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
             // j of chunk it+AHEAD is issued after MFMA min(36 j / SPW + 2, 35)
             // (two MFMAs in, so the LDS reads of its sources have landed).
             v16f sacc;
-            {
+            // kMode 1: this chunk issues copies, 0: it does not, 2: as copies says
+            auto qk = [&](auto mode_tag) {
+                constexpr int kMode = decltype(mode_tag)::value;
                 const uint8_t* vrow = cur + krow_i * S::VPITCH + hi * 16;
                 const uint8_t* trw = cur + S::VBYTES + krow_i * (S::TP * 16);
                 auto kfrag = [&](int c2) -> u32x4 {
@@ -229,9 +233,20 @@ void sparse_attn_mla_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
                                      : "+v"(sacc) : "v"(as_bf8(kf[c2 % (kPre + 1)])), "v"(qf[c2]));
 #pragma unroll
                     for (int j = 0; j < SPW; ++j)
-                        if (c2 == min((j * S::QC) / SPW + 2, S::QC - 1) && copies) issue_copy(cs, c + AHEAD, j);
+                        if ((kMode == 1 || (kMode == 2 && copies)) && c2 == min((j * S::QC) / SPW + 2, S::QC - 1))
+                            issue_copy(cs, c + AHEAD, j);
                     __builtin_amdgcn_sched_barrier(0);
                 }
+            };
+            // Two copies of the loop, with and without the chunk's copies, take
+            // the branch around each copy out of the MFMA sequence (2.7% at
+            // 128 heads); the instances for 32 heads or split sets keep one
+            // loop, which needs no scratch memory.
+            if constexpr (!SPLIT && NW > 1) {
+                if (copies) qk(std::integral_constant<int, 1>{});
+                else qk(std::integral_constant<int, 0>{});
+            } else {
+                qk(std::integral_constant<int, 2>{});
             }
 
             // The first V^T fragments of P.V, read before the softmax so that
@@ -350,6 +365,10 @@ void sparse_attn_mla_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
         // each store instruction writes two heads' 512-byte runs.  Piece j
         // of staged row r sits at slot j ^ r (conflict-free row reads).
         static_assert(NBUF * S::BUF_BYTES >= NW * 16384, "staging fits the ring");
+        // the lane's position, computed afresh (kept from the start of the
+        // kernel it would hold a register through the chunk loop)
+        const int lane_e = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+        const int col_e = lane_e & 31, hi_e = lane_e >> 5;
         uint8_t* stage = &ring[0][0] + wave * 16384;
         uint16_t* owave = (uint16_t*)wave_uniform_ptr(out + (((int64_t)b * Lq + t) * H + wave * 32) * 512);
 #pragma unroll
@@ -366,19 +385,19 @@ void sparse_attn_mla_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
                     const uint32_t b1 = pack_bf16x2(o[dt][4 * gb + 2] * inv, o[dt][4 * gb + 3] * inv);
                     const auto s0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
                     const auto s1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
-                    const int piece = 4 * d8 + 2 * p + hi;
-                    *(u32x4*)(stage + col * 512 + ((piece ^ col) << 4)) = u32x4{s0[0], s1[0], s0[1], s1[1]};
+                    const int piece = 4 * d8 + 2 * p + hi_e;
+                    *(u32x4*)(stage + col_e * 512 + ((piece ^ col_e) << 4)) = u32x4{s0[0], s1[0], s0[1], s1[1]};
                 }
             }
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const int r = 2 * i + hi;
-                const u32x4 v = *(const u32x4*)(stage + r * 512 + ((col ^ r) << 4));
-                *(u32x4*)(owave + (int64_t)r * 512 + hh * 256 + col * 8) = v;
+                const int r = 2 * i + hi_e;
+                const u32x4 v = *(const u32x4*)(stage + r * 512 + ((col_e ^ r) << 4));
+                *(u32x4*)(owave + (int64_t)r * 512 + hh * 256 + col_e * 8) = v;
             }
         }
-        if (lse != nullptr && hi == 0)
-            ((float*)wave_uniform_ptr(lse + ((int64_t)b * Lq + t) * H + wave * 32))[col] = lse_row;
+        if (lse != nullptr && hi_e == 0)
+            ((float*)wave_uniform_ptr(lse + ((int64_t)b * Lq + t) * H + wave * 32))[col_e] = lse_row;
     }
 }
 
