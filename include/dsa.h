@@ -128,13 +128,20 @@ dsa_status dsa_topk(const float* scores, int32_t* idx,
  *            (d_qk, d_v) in {(576,512), (128,128), (64,64)};
  *            F32 with d_qk <= 1024, d_v <= d_qk, n_heads <= 256.
  *
- * Few query rows (decode): when dsa_sparse_attn_workspace_size() is non-zero
- * and `workspace` (256-byte aligned) holds that many bytes, each row's
- * selected set is split over several workgroups whose normalised partial
- * outputs and log-sum-exps are merged in fp32 (in a fixed order, so the
- * result is deterministic).  With workspace NULL or too small the rows run
- * unsplit; the two results agree within fp32 rounding before the bf16
- * rounding of out.  The workspace's contents on entry do not matter.
+ * Workspace (bf16 576/512 rows with 32, 64 or 128 heads and k <= 2048): when
+ * dsa_sparse_attn_workspace_size() is non-zero and `workspace` (256-byte
+ * aligned) holds that many bytes,
+ *  - few query rows (decode): each row's selected set is split over several
+ *    workgroups whose normalised partial outputs and log-sum-exps are merged
+ *    in fp32 (in a fixed order, so the result is deterministic).  Unsplit
+ *    (workspace NULL or too small) the result agrees within fp32 rounding
+ *    before the bf16 rounding of out;
+ *  - many query rows: the workspace holds a counter from which workgroups
+ *    take their rows in turn, so the GPU's dies share the rows by speed.  The
+ *    result is the same bit for bit as without the workspace (one workgroup
+ *    per row, fixed).
+ * The workspace's contents on entry do not matter.  Calls that share a
+ * workspace must not run at the same time.
  */
 dsa_status dsa_sparse_attn(const void* q, const void* kv, const int32_t* idx,
                            void* out, float* lse,
@@ -144,10 +151,10 @@ dsa_status dsa_sparse_attn(const void* q, const void* kv, const int32_t* idx,
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Bytes of workspace with which dsa_sparse_attn splits the selected sets
- * (0: these sizes run unsplit).  The split applies to the bf16 576/512 rows
- * with 32, 64 or 128 heads, k <= 2048, and fewer than 128 query rows
- * (B * Lq) in all.
+ * Bytes of workspace dsa_sparse_attn can use (0: none).  For the bf16 576/512
+ * rows with 32, 64 or 128 heads and k <= 2048: with fewer than 128 query rows
+ * (B * Lq) in all, the split partials; otherwise 256 bytes for the row
+ * counter.
  */
 size_t dsa_sparse_attn_workspace_size(int B, int Lq, int n_heads, int d_qk, int d_v, int k,
                                       dsa_dtype io_dtype);
@@ -271,8 +278,9 @@ typedef enum dsa_select {
  * Bytes of device workspace dsa_forward needs for these sizes and route, laid
  * out in this order: one tile of B * T * Lk fp32 scores (T = the query-tile
  * rows; at the start of the workspace), the selected sets
- * of all B * Lq rows (int32, k each), the attention's split partials when
- * dsa_sparse_attn_workspace_size(B, Lq, ...) is non-zero, and for the
+ * of all B * Lq rows (int32, k each), the attention's workspace (split
+ * partials or row counter) when dsa_sparse_attn_workspace_size(B, Lq, ...)
+ * is non-zero, and for the
  * candidate route per row: the sample scores ((Lk - 1) / R + 1 fp32, padded
  * to a multiple of 4), tau, the list (2k pairs of 4-byte words), its length and
  * a flag.  q_tile_rows = 0 picks T automatically (the largest T whose score

@@ -47,7 +47,8 @@ void sparse_attn_mla_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
                             const int32_t* __restrict__ idx, uint16_t* __restrict__ out,
                             float* __restrict__ lse, int Lq, int Lk, int t_begin, int H, int k,
                             int64_t idx_bstride, float scale_log2, int cps,
-                            float* __restrict__ part_o, float* __restrict__ part_lse)
+                            float* __restrict__ part_o, float* __restrict__ part_lse,
+                            int* __restrict__ row_ctr, int t_count, int n_seq)
 {
     using S = W32Shape<576, 512, NW>;
     constexpr int NC = S::NC;
@@ -63,7 +64,23 @@ void sparse_attn_mla_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
     __shared__ __attribute__((aligned(16))) int32_t sel[S::KMAX];   // the query's index list (-1 padded)
     __shared__ int wlast[NW];                                       // per wave: last valid list position
 
-    const int row = blockIdx.x, b = blockIdx.y;
+    // Unsplit with a row counter: each workgroup takes the next of the
+    // n_seq * t_count rows from the counter (the grid has about 1/8 more
+    // workgroups than rows; the late ones find none and leave), so dies that
+    // run faster take more rows.  Which workgroup computes a row does not
+    // change its result.  Otherwise: one workgroup per row, fixed.
+    int row = blockIdx.x, b = blockIdx.y;
+    if (!SPLIT && row_ctr != nullptr) {
+        __shared__ int s_item;
+        if (threadIdx.x == 0) s_item = atomicAdd(row_ctr, 1);
+        __syncthreads();
+        const int item = s_item;
+        if (item >= n_seq * t_count) return;                 // uniform over the workgroup
+        b = item / t_count;
+        row = item - b * t_count;
+        b = __builtin_amdgcn_readfirstlane(b);
+        row = __builtin_amdgcn_readfirstlane(row);
+    }
     const int t = t_begin + row;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
@@ -402,18 +419,38 @@ void sparse_attn_mla_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
 }
 
 
+__global__ void zero_counter_kernel(int* __restrict__ p)
+{
+    if (threadIdx.x == 0) *p = 0;
+}
+
 template <int NW>
 hipError_t launch_mla(const AttnLaunch& a, hipStream_t s, int ns, int cps, float* part_o, float* part_lse)
 {
     const float scale_log2 = a.scale * 1.4426950408889634f;
-    if (ns == 1)
+    if (ns == 1 && a.row_ctr != nullptr) {
+        // the counter is cleared by a kernel (not a memset), so the pair can
+        // be captured in a graph; a one-dimensional grid takes rows (b, t)
+        // numbered b * t_count + t
+        hipLaunchKernelGGL(zero_counter_kernel, dim3(1), dim3(64), 0, s, a.row_ctr);
+        const int64_t items = (int64_t)a.B * a.t_count;
+        const int64_t grid = items + items / 8 + 64;
+        if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((sparse_attn_mla_kernel<NW, false>), dim3((unsigned)grid, 1, 1), dim3(64 * NW), 0, s,
+                           (const uint16_t*)a.q, (const uint16_t*)a.kv, a.idx, (uint16_t*)a.out, a.lse, a.Lq,
+                           a.Lk, a.t_begin, a.H, a.k, a.idx_bstride, scale_log2, cps, part_o, part_lse, a.row_ctr,
+                           a.t_count, a.B);
+    } else if (ns == 1) {
         hipLaunchKernelGGL((sparse_attn_mla_kernel<NW, false>), dim3(a.t_count, a.B, 1), dim3(64 * NW), 0, s,
                            (const uint16_t*)a.q, (const uint16_t*)a.kv, a.idx, (uint16_t*)a.out, a.lse, a.Lq,
-                           a.Lk, a.t_begin, a.H, a.k, a.idx_bstride, scale_log2, cps, part_o, part_lse);
-    else
+                           a.Lk, a.t_begin, a.H, a.k, a.idx_bstride, scale_log2, cps, part_o, part_lse, nullptr,
+                           a.t_count, a.B);
+    } else {
         hipLaunchKernelGGL((sparse_attn_mla_kernel<NW, true>), dim3(a.t_count, a.B, ns), dim3(64 * NW), 0, s,
                            (const uint16_t*)a.q, (const uint16_t*)a.kv, a.idx, (uint16_t*)a.out, a.lse, a.Lq,
-                           a.Lk, a.t_begin, a.H, a.k, a.idx_bstride, scale_log2, cps, part_o, part_lse);
+                           a.Lk, a.t_begin, a.H, a.k, a.idx_bstride, scale_log2, cps, part_o, part_lse, nullptr,
+                           a.t_count, a.B);
+    }
     return hipGetLastError();
 }
 

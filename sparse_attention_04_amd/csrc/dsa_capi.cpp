@@ -199,7 +199,10 @@ ForwardLayout forward_layout(int B, int Lq, int Lk, int k, int n_heads, int d_qk
     L.scores = round256((size_t)B * (size_t)T * (size_t)Lk * sizeof(float));
     L.idx = idx_in_workspace ? round256((size_t)B * (size_t)Lq * (size_t)k * sizeof(int32_t)) : 0;
     const int ns = dsa::sparse_attn_split((int64_t)B * Lq, n_heads, d_qk, d_v, k, io_dtype == DSA_BF16);
-    L.part = round256(dsa::sparse_attn_split_bytes((int64_t)B * Lq, n_heads, d_v, ns));
+    // the attention's split partials, or (unsplit) its row counter
+    L.part = round256(ns > 1 ? dsa::sparse_attn_split_bytes((int64_t)B * Lq, n_heads, d_v, ns)
+                             : dsa::sparse_attn_counter_bytes((int64_t)B * Lq, n_heads, d_qk, d_v, k,
+                                                              io_dtype == DSA_BF16));
     if (cand) {
         const size_t rows = (size_t)B * (size_t)Lq;
         L.sample = round256(rows * (size_t)cand->Ls_pad * sizeof(float));
@@ -314,6 +317,8 @@ dsa_status forward_run(const char* fn, const void* q_idx, const float* q_scale, 
     aa.bf16 = (io_dtype == DSA_BF16);
     aa.nsplit = dsa::sparse_attn_split((int64_t)B * Lq, n_heads, d_qk, d_v, k, aa.bf16);
     aa.part = aa.nsplit > 1 ? ws_part : nullptr;
+    if (aa.nsplit == 1 && dsa::sparse_attn_counter_bytes((int64_t)B * Lq, n_heads, d_qk, d_v, k, aa.bf16) > 0)
+        aa.row_ctr = (int*)ws_part;
     return hip_status(fn, dsa::launch_sparse_attn(aa, s));
 }
 
@@ -413,8 +418,10 @@ size_t dsa_sparse_attn_workspace_size(int B, int Lq, int n_heads, int d_qk, int 
 {
     if (B <= 0 || Lq <= 0 || n_heads <= 0 || d_v <= 0 || k <= 0) return 0;
     const int64_t rows = (int64_t)B * Lq;
-    const int ns = dsa::sparse_attn_split(rows, n_heads, d_qk, d_v, k, io_dtype == DSA_BF16);
-    const size_t bytes = dsa::sparse_attn_split_bytes(rows, n_heads, d_v, ns);
+    const bool bf16 = io_dtype == DSA_BF16;
+    const int ns = dsa::sparse_attn_split(rows, n_heads, d_qk, d_v, k, bf16);
+    const size_t bytes = ns > 1 ? dsa::sparse_attn_split_bytes(rows, n_heads, d_v, ns)
+                                : dsa::sparse_attn_counter_bytes(rows, n_heads, d_qk, d_v, k, bf16);
     return bytes ? round256(bytes) : 0;
 }
 
@@ -436,13 +443,15 @@ dsa_status dsa_sparse_attn(const void* q, const void* kv, const int32_t* idx, vo
     a.B = B; a.Lq = Lq; a.Lk = Lk; a.t_begin = 0; a.t_count = Lq; a.idx_bstride = (int64_t)Lq * k;
     a.H = n_heads; a.Dqk = d_qk; a.Dv = d_v; a.k = k; a.scale = softmax_scale;
     a.bf16 = (io_dtype == DSA_BF16);
-    // the split over the selected set runs only with a large enough workspace
+    // the split over the selected set (few rows) or the row counter (many)
+    // runs only with a large enough workspace
     const size_t need = dsa_sparse_attn_workspace_size(B, Lq, n_heads, d_qk, d_v, k, io_dtype);
     if (need > 0 && workspace != nullptr && workspace_bytes >= need) {
         if (((uintptr_t)workspace & 255u) != 0)
             return fail(DSA_ERR_ALIGN, "%s: workspace must be 256-byte aligned", fn);
         a.nsplit = dsa::sparse_attn_split((int64_t)B * Lq, n_heads, d_qk, d_v, k, a.bf16);
-        a.part = (float*)workspace;
+        if (a.nsplit > 1) a.part = (float*)workspace;
+        else a.row_ctr = (int*)workspace;
     }
     return hip_status(fn, dsa::launch_sparse_attn(a, (hipStream_t)stream));
 }
@@ -472,7 +481,7 @@ dsa_status dsa_sparse_attn_fp8kv(const void* q, const void* kv_fp8, const int32_
         if (((uintptr_t)workspace & 255u) != 0)
             return fail(DSA_ERR_ALIGN, "%s: workspace must be 256-byte aligned", fn);
         a.nsplit = dsa::sparse_attn_split((int64_t)B * Lq, n_heads, 576, 512, k, true);
-        a.part = (float*)workspace;
+        if (a.nsplit > 1) a.part = (float*)workspace;     // the FP8-row kernel takes no row counter
     }
     return hip_status(fn, dsa::launch_sparse_attn(a, (hipStream_t)stream));
 }

@@ -82,6 +82,8 @@ struct AttnLaunch {
     bool kv_fp8;            // kv holds 656-byte FP8 rows (576/512 rows, 32-head kernel only)
     int nsplit;             // > 1: split each row's selected set (32-head kernel only)
     float* part;            // split partials, sparse_attn_split_bytes(B * t_count, H, Dv, nsplit) bytes
+    int* row_ctr = nullptr; // unsplit 576/512 rows: a device counter (zeroed by the launch) from which
+                            // workgroups take their rows in turn; null: one workgroup per row, fixed
 };
 
 struct QuantLaunch {
@@ -159,6 +161,9 @@ size_t attn_bwd_workspace_bytes(int B, int Lq, int Lk, int H, int k);
 // split), and the bytes of partial results it needs.
 int sparse_attn_split(int64_t rows, int H, int Dqk, int Dv, int k, bool bf16);
 size_t sparse_attn_split_bytes(int64_t rows, int H, int Dv, int nsplit);
+// Bytes of the row counter the unsplit 576/512 kernel takes its rows from
+// (0 where that kernel does not run unsplit).
+size_t sparse_attn_counter_bytes(int64_t rows, int H, int Dqk, int Dv, int k, bool bf16);
 
 // Which (Dqk, Dv) pairs the bf16 attention kernel is instantiated for.
 bool sparse_attn_bf16_supported(int Dqk, int Dv);

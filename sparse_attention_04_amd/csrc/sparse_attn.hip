@@ -840,6 +840,12 @@ int sparse_attn_split(int64_t rows, int H, int Dqk, int Dv, int k, bool bf16)
     return ns > 1 ? ns : 1;
 }
 
+size_t sparse_attn_counter_bytes(int64_t rows, int H, int Dqk, int Dv, int k, bool bf16)
+{
+    if (!bf16 || (H != 32 && H != 64 && H != 128) || Dqk != 576 || Dv != 512 || k > 2048 || rows <= 0) return 0;
+    return sparse_attn_split(rows, H, Dqk, Dv, k, bf16) == 1 ? 256 : 0;
+}
+
 size_t sparse_attn_split_bytes(int64_t rows, int H, int Dv, int nsplit)
 {
     if (nsplit <= 1) return 0;

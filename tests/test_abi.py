@@ -126,8 +126,8 @@ def test_attention_split_workspace(L):
     assert ws(1, 8, 128, 576, 512, 2048, BF16) == part(8, 8)          # at most 8 splits
     assert ws(1, 8, 32, 576, 512, 2048, BF16) == part(8, 8, H=32)
     assert ws(1, 8, 128, 576, 512, 256, BF16) == part(8, 2)           # at least 4 chunks of 32 per split
-    assert ws(1, 128, 128, 576, 512, 2048, BF16) == 0                 # enough rows: no split
-    assert ws(1, 8, 128, 576, 512, 64, BF16) == 0
+    assert ws(1, 128, 128, 576, 512, 2048, BF16) == 256               # enough rows: no split, the row counter
+    assert ws(1, 8, 128, 576, 512, 64, BF16) == 256                   # too few chunks to split
     assert ws(1, 8, 128, 576, 512, 2048, F32) == 0
     assert ws(1, 8, 16, 576, 512, 2048, BF16) == 0
     assert ws(1, 8, 96, 576, 512, 2048, BF16) == 0
@@ -160,12 +160,13 @@ def test_forward_workspace(L):
                                                                             T, sel)
     # score tiles: one tile of scores plus the selected sets of every row (the
     # attention runs once over all rows after the last tile)
-    assert ws(1, 32768, 32768, 2048, 1024) == 1024 * 32768 * 4 + 32768 * 2048 * 4
-    assert ws(1, 131072, 131072, 2048, 4096) == 4096 * 131072 * 4 + 131072 * 2048 * 4
+    # (plus 256 bytes: the attention's row counter)
+    assert ws(1, 32768, 32768, 2048, 1024) == 1024 * 32768 * 4 + 32768 * 2048 * 4 + 256
+    assert ws(1, 131072, 131072, 2048, 4096) == 4096 * 131072 * 4 + 131072 * 2048 * 4 + 256
     # auto tile: the largest score tile within AUTO_TILE_BYTES
     for Lk in (4096, 32768, 131072):
         T = min(Lk, AUTO_TILE_BYTES // (Lk * 4))
-        tiles = T * Lk * 4 + Lk * 2048 * 4
+        tiles = T * Lk * 4 + Lk * 2048 * 4 + 256
         assert ws(1, Lk, Lk, 2048, 0) == tiles
         # candidates on top of the fallback tiles
         assert ws(1, Lk, Lk, 2048, 0, SEL_CAND) == tiles + _cand_extra(1, Lk, Lk, 2048)

@@ -451,6 +451,38 @@ def test_attention_split_matches_unsplit_and_oracle(dsa):
         check_attention(out_s[b].float().cpu().numpy(), o_ref, lse_s[b].cpu().numpy(), l_ref, True)
 
 
+@pytest.mark.parametrize("H", [32, 64, 128])
+def test_attention_row_counter_matches_fixed_rows(dsa, H):
+    """Many query rows: with its workspace the 576/512 kernel hands rows to
+    workgroups from a counter (more workgroups than rows, the late ones leave
+    without work); without it one workgroup per row.  The two are identical
+    bit for bit, twice in a row (the counter is cleared on every call), and
+    sampled rows of both sequences meet the oracle."""
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(17 + H)
+    B, Lq, Lk, k = 2, 301, 4000, 333
+    assert dsa.dsa_sparse_attn_workspace_size(B, Lq, H, 576, 512, k) == 256
+    q = torch.randn(B, Lq, H, 576, device=dev, generator=g).to(torch.bfloat16)
+    kv = torch.randn(B, Lk, 576, device=dev, generator=g).to(torch.bfloat16)
+    idx = torch.randint(0, Lk, (B, Lq, k), device=dev, generator=g, dtype=torch.int32)
+    idx[0, 5, 40:] = -1                        # short set
+    idx[1, 7, :] = -1                          # empty set
+    ws = torch.empty(256, dtype=torch.uint8, device=dev)
+    out_c, lse_c = dsa.dsa_sparse_attn(q, kv, idx, 512, 192 ** -0.5, q_pos0=Lk - Lq, workspace=ws)
+    out_c2, lse_c2 = dsa.dsa_sparse_attn(q, kv, idx, 512, 192 ** -0.5, q_pos0=Lk - Lq, workspace=ws)
+    out_f, lse_f = dsa.dsa_sparse_attn(q, kv, idx, 512, 192 ** -0.5, q_pos0=Lk - Lq, split=False)
+    torch.cuda.synchronize()
+    for o, l in ((out_c, lse_c), (out_c2, lse_c2)):
+        assert torch.equal(o.view(torch.int16), out_f.view(torch.int16)), "row counter changes the output"
+        assert torch.equal(l, lse_f), "row counter changes lse"
+    assert torch.all(out_c[1, 7] == 0) and torch.all(torch.isneginf(lse_c[1, 7]))
+    rows = [0, 5, 7, 150, Lq - 1]
+    for b in range(B):
+        o_ref, l_ref = oracle.sparse_attn(q[b, rows].cpu(), kv[b].cpu(), idx[b, rows].cpu().numpy(), 512,
+                                          192 ** -0.5, BF16)
+        check_attention(out_c[b, rows].float().cpu().numpy(), o_ref, lse_c[b, rows].cpu().numpy(), l_ref, True)
+
+
 def test_attention_fp32_crafted(dsa):
     dev = torch.device("cuda:0")
     g = torch.Generator(device=dev).manual_seed(5)
