@@ -283,8 +283,9 @@ typedef enum dsa_select {
  * is non-zero, and for the
  * candidate route per row: the sample scores ((Lk - 1) / R + 1 fp32, padded
  * to a multiple of 4), tau, the list (2k pairs of 4-byte words), its length and
- * a flag.  q_tile_rows = 0 picks T automatically (the largest T whose score
- * tile fits the automatic tile budget, at most Lq).  Returns 0 for an empty
+ * a flag, then 256 bytes for the list pass's block counter.  q_tile_rows = 0
+ * picks T automatically (the largest T whose score tile fits the automatic
+ * tile budget, at most Lq).  Returns 0 for an empty
  * problem, for q_tile_rows < 0, and for DSA_SELECT_CANDIDATES on a problem the
  * candidate route does not take (with any idx_dtype).
  */

@@ -189,7 +189,7 @@ int forward_route(int select, const CandPlan& c)
 // route, per row the sample scores, tau, the list length, the flag and the
 // list.
 struct ForwardLayout {
-    size_t scores, idx, part, sample, tau, cnt, flag, cand, total;
+    size_t scores, idx, part, sample, tau, cnt, flag, cand, ctr, total;
 };
 
 ForwardLayout forward_layout(int B, int Lq, int Lk, int k, int n_heads, int d_qk, int d_v, dsa_dtype io_dtype,
@@ -210,8 +210,9 @@ ForwardLayout forward_layout(int B, int Lq, int Lk, int k, int n_heads, int d_qk
         L.cnt = round256(rows * sizeof(int32_t));
         L.flag = round256(rows * sizeof(int32_t));
         L.cand = round256(rows * (size_t)cand->cap * 2 * sizeof(uint32_t));
+        L.ctr = 256;                                         // the list pass's block counter
     }
-    L.total = L.scores + L.idx + L.part + L.sample + L.tau + L.cnt + L.flag + L.cand;
+    L.total = L.scores + L.idx + L.part + L.sample + L.tau + L.cnt + L.flag + L.cand + L.ctr;
     return L;
 }
 
@@ -264,6 +265,8 @@ dsa_status forward_run(const char* fn, const void* q_idx, const float* q_scale, 
     int32_t* ws_flag = (int32_t*)p;
     p += L.flag;
     uint32_t* ws_cand = (uint32_t*)p;
+    p += L.cand;
+    int* ws_ctr = (int*)p;
     const int64_t idx_bstride = (int64_t)Lq * k;
 
     dsa::IndexerLaunch base{};
@@ -290,6 +293,7 @@ dsa_status forward_run(const char* fn, const void* q_idx, const float* q_scale, 
         dsa::IndexerLaunch fa = base;
         fa.t_begin = 0; fa.t_count = Lq;
         fa.tau = ws_tau; fa.cand = ws_cand; fa.cand_cnt = ws_cnt; fa.cap = cand->cap;
+        fa.blk_ctr = ws_ctr;
         if ((e = dsa::launch_indexer(fa, s)) != hipSuccess) return hip_status(fn, e);
         if ((e = dsa::launch_select_candidates(sl, s)) != hipSuccess) return hip_status(fn, e);
     }

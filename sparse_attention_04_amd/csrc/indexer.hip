@@ -71,6 +71,7 @@ struct IdxExt {
     uint32_t* cand;
     int32_t* cand_cnt;
     int cap;
+    int* blk_ctr;
 };
 
 template <bool CAND>
@@ -91,8 +92,22 @@ void indexer_fp8_kernel(const uint8_t* __restrict__ q8, const float* __restrict_
     __shared__ __attribute__((aligned(16))) uint32_t cpart[3][kQB][kD / 2]; // bf16 pairs: hi, mid, lo
 
     const int nqb = (t_count + kQB - 1) / kQB;
-    const int qb = nqb - 1 - (int)blockIdx.x;          // longest rows first
-    const int b = blockIdx.y;
+    // Longest rows first.  With a block counter (keys not split), each
+    // workgroup takes the next (sequence, row block) from it, so the GPU's
+    // dies share the blocks by speed; the grid has about 1/8 more workgroups
+    // than blocks and the late ones leave.  Which workgroup scores a block
+    // does not change a score.
+    int qb = nqb - 1 - (int)blockIdx.x, b = blockIdx.y;
+    if (x.blk_ctr != nullptr) {
+        __shared__ int s_blk;
+        if (threadIdx.x == 0) s_blk = atomicAdd(x.blk_ctr, 1);
+        __syncthreads();
+        const int item = s_blk;
+        if (item >= (int)gridDim.y * nqb) return;           // uniform over the workgroup
+        const int b_ = item % (int)gridDim.y;               // the sequences' blocks interleaved
+        b = __builtin_amdgcn_readfirstlane(b_);
+        qb = __builtin_amdgcn_readfirstlane(nqb - 1 - item / (int)gridDim.y);
+    }
     const int t0 = t_begin + qb * kQB;
     const int rows_here = min(kQB, t_begin + t_count - t0);
     const int tpos_last = q_pos0 + t0 + rows_here - 1;
@@ -539,6 +554,11 @@ void indexer_f32_kernel(const float* __restrict__ q, const float* __restrict__ k
 
 }  // namespace
 
+__global__ void zero_block_counter_kernel(int* __restrict__ p)
+{
+    if (threadIdx.x == 0) *p = 0;
+}
+
 constexpr int64_t kMinBlocks = 1024;    // below this many row blocks the keys are split too
 
 hipError_t launch_indexer(const IndexerLaunch& a, hipStream_t s)
@@ -576,8 +596,16 @@ hipError_t launch_indexer(const IndexerLaunch& a, hipStream_t s)
                  : (int)std::min<int64_t>((kMinBlocks + blocks - 1) / blocks, gmax);
         const int gps = (gmax + nz - 1) / nz;
         nz = (gmax + gps - 1) / gps;
-        const IdxExt x{a.kshift, a.flag, a.tau, a.cand, a.cand_cnt, a.cap};
-        hipLaunchKernelGGL(cand ? indexer_fp8_kernel<true> : indexer_fp8_kernel<false>, dim3(nqb, a.B, nz),
+        const IdxExt x{a.kshift, a.flag, a.tau, a.cand, a.cand_cnt, a.cap, nz == 1 ? a.blk_ctr : nullptr};
+        unsigned gx = (unsigned)nqb;
+        if (x.blk_ctr != nullptr) {
+            // the counter is cleared by a kernel (not a memset): the pair can be captured in a graph
+            hipLaunchKernelGGL(zero_block_counter_kernel, dim3(1), dim3(64), 0, s, x.blk_ctr);
+            const int64_t items = (int64_t)nqb * a.B;
+            const int64_t g = (items + items / 8 + 64 + a.B - 1) / a.B;   // workgroups per sequence row of the grid
+            gx = (unsigned)g;
+        }
+        hipLaunchKernelGGL(cand ? indexer_fp8_kernel<true> : indexer_fp8_kernel<false>, dim3(gx, a.B, nz),
                            dim3(kThreads), 0, s,
                            (const uint8_t*)a.q, a.q_scale, (const uint8_t*)a.k, a.k_scale, a.w,
                            a.scores, a.Lq, a.Lk, a.q_pos0, a.t_begin, a.t_count,

@@ -32,6 +32,10 @@ struct IndexerLaunch {
     uint32_t* cand = nullptr;
     int32_t* cand_cnt = nullptr;
     int cap = 0;
+    // FP8 block kernel, keys not split over workgroups: a device counter
+    // (cleared by the launch) from which workgroups take their row blocks,
+    // longest first; null: one workgroup per row block, fixed
+    int* blk_ctr = nullptr;
 };
 
 struct TopkLaunch {

@@ -146,13 +146,14 @@ def _r256(x):
 def _cand_extra(B, Lq, Lk, k):
     """Candidate-route workspace beyond the score-tile route's: per row the
     sample scores (every 2^r-th key, r = max(0, floor(log2(k / 128))), padded
-    to 4), tau, the list length, the flag and the list of 2k (score, s) pairs."""
+    to 4), tau, the list length, the flag and the list of 2k (score, s) pairs,
+    and the list pass's 256-byte block counter."""
     r = 0
     while (128 << (r + 1)) <= k:
         r += 1
     ls_pad = ((((Lk - 1) >> r) + 1) + 3) // 4 * 4
     rows = B * Lq
-    return _r256(rows * ls_pad * 4) + 3 * _r256(rows * 4) + _r256(rows * 2 * k * 8)
+    return _r256(rows * ls_pad * 4) + 3 * _r256(rows * 4) + _r256(rows * 2 * k * 8) + 256
 
 
 def test_forward_workspace(L):
