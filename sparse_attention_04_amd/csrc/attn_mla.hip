@@ -321,7 +321,6 @@ void sparse_attn_mla_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
             auto soft = [&](int v) {
                 const float pv = __builtin_amdgcn_exp2f(fmaf(z[v], scale_log2, negm));
                 psum += pv;
-                cmax = fmaxf(cmax, z[v]);
                 if (v & 1) pw[v >> 1] = pack_bf16x2(peven, pv);
                 else peven = pv;
             };
@@ -339,6 +338,12 @@ void sparse_attn_mla_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
                                                   : u32x4{pw[4], pw[5], pw[6], pw[7]});
                 o[dt] = mfma_bf16_32x32x16(as_bf8(vf[s % (kPvPre + 1)]), pfrag, o[dt]);
                 if (s < 8) soft(8 + s);
+                if (s == 10) {
+                    // the chunk's largest logit (overflow check, second-pass
+                    // reference), taken between MFMAs, off the path into P.V
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) cmax = fmaxf(cmax, z[v]);
+                }
                 __builtin_amdgcn_sched_barrier(0);
             }
             l += psum;
