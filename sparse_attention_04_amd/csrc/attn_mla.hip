@@ -209,8 +209,7 @@ void sparse_attn_mla_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
             const uint8_t* cur = ring[c % NBUF];
             const bool copies = it + AHEAD < nchunks;        // chunk it+AHEAD goes into chunk it-1's slot
             CopySrc cs;
-            if (copies) cs = copy_src(c + AHEAD);
-            const uint32_t vmask = valid_mask(c);            // read ahead of Q.K, off the softmax's path
+            uint32_t vmask;
 
             // S^T (32 rows x 32 heads).  Step c2 < 32 reads value-part piece
             // 2*c2 + hi of row slot_row(col); later steps read the tail.  Copy
@@ -229,6 +228,11 @@ void sparse_attn_mla_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
                 u32x4 kf[kPre + 1];
 #pragma unroll
                 for (int i = 0; i < kPre; ++i) kf[i] = kfrag(i);
+                // the copy sources and the valid-row mask after the first key
+                // fragments (the first MFMA waits on those), ahead of the
+                // copies and of the softmax that use them
+                if (copies) cs = copy_src(c + AHEAD);
+                vmask = valid_mask(c);
                 // fully unrolled for every wave count: with one wave (36 copies
                 // per chunk) the default heuristic kept the loop, and the query
                 // fragments, indexed at run time, went to scratch memory
