@@ -321,12 +321,13 @@ void sparse_attn_mla_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
             // p = exp2(z - m) (masked entries are -inf: exp2 gives 0), packed
             // into bf16 pairs in place: P^T's lane layout is the B operand's
             uint32_t pw[8];
+            float pz[16];
             float psum = 0.f, cmax = -INFINITY, peven = 0.f;
             auto soft = [&](int v) {
                 const float pv = __builtin_amdgcn_exp2f(fmaf(z[v], scale_log2, negm));
-                psum += pv;
                 if (v & 1) pw[v >> 1] = pack_bf16x2(peven, pv);
                 else peven = pv;
+                pz[v] = pv;
             };
 #pragma unroll
             for (int v = 0; v < 8; ++v) soft(v);
@@ -342,6 +343,8 @@ void sparse_attn_mla_kernel(const uint16_t* __restrict__ q, const uint16_t* __re
                                                   : u32x4{pw[4], pw[5], pw[6], pw[7]});
                 o[dt] = mfma_bf16_32x32x16(as_bf8(vf[s % (kPvPre + 1)]), pfrag, o[dt]);
                 if (s < 8) soft(8 + s);
+                // the sum of p, in the same order, off the path into P.V
+                if (s >= 8 && s < 16) { psum += pz[2 * (s - 8)]; psum += pz[2 * (s - 8) + 1]; }
                 if (s == 10) {
                     // the chunk's largest logit (overflow check, second-pass
                     // reference), taken between MFMAs, off the path into P.V
