@@ -39,7 +39,7 @@ ORACLE_SAMPLE = {"tiny_fp32_L256": 256, "prefill_L4096": 128, HEADLINE: 384, "de
 # FETCH_SIZE / WRITE_SIZE runs scaled by a 1 GiB plain copy measured in the same
 # runs (fetch factor 2.0, write factor 1.0).  Valid only for the attention
 # source it was measured on; any other source reports null.
-ATTN_TRAFFIC = {"source_sha256_16": "65ddbdbf7f024166", "fetch_bytes": 32709136199.9,
+ATTN_TRAFFIC = {"source_sha256_16": "e34f4f0fad0bac23", "fetch_bytes": 33821857868.4,
                 "write_bytes": 4312926208.0}
 
 
